@@ -1,0 +1,135 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that a pin catches each.
+
+Every mutation below is a slip that could be made when writing the method down from
+the pages: a dropped term, a transposed operand, a reversed order, a wrong index.
+"""
+import numpy as np
+import pytest
+
+from oracle import indexmem as im
+from oracle import momentkv as mk
+from tests import test_oracle_golden as gold
+from tests import test_oracle_pins as pins
+
+_orig = {name: getattr(im, name) for name in dir(im) if callable(getattr(im, name))}
+_orig_mk = {name: getattr(mk, name) for name in dir(mk) if callable(getattr(mk, name))}
+
+
+def _phi_no_plus_one(x):
+    x = np.asarray(x, np.float64)
+    return np.where(x > 0, x, np.exp(np.minimum(x, 0.0)))
+
+
+def _memory_transposed(K_ev, V_ev, lam, M0=None, b0=None):
+    M, b = _orig["memory_build"](K_ev, V_ev, lam, M0, b0)
+    return M.T, b
+
+
+def _memory_reversed_decay(K_ev, V_ev, lam, M0=None, b0=None):
+    return _orig["memory_build"](np.asarray(K_ev)[::-1], np.asarray(V_ev)[::-1], lam, M0, b0)
+
+
+def _score_mask_flipped(q_hat, gate, k_hat, q_pos, act="relu"):
+    A = _orig["score_matrix"](q_hat, gate, k_hat, np.full(len(q_pos), k_hat.shape[0]), act)
+    L = k_hat.shape[0]
+    mask = np.arange(L)[None, :] < np.asarray(q_pos)[:, None] - 1
+    return np.where(mask, -np.inf, A)
+
+
+def _score_relu_after_sum(q_hat, gate, k_hat, q_pos, act="relu"):
+    A = _orig["score_matrix"](q_hat, gate, k_hat, q_pos, "none")
+    return np.where(np.isneginf(A), A, np.maximum(A, 0.0)) if act == "relu" else A
+
+
+def _score_no_scale(q_hat, gate, k_hat, q_pos, act="relu"):
+    return _orig["score_matrix"](q_hat, gate, k_hat, q_pos, act) * np.sqrt(k_hat.shape[1])
+
+
+def _topk_tie_high(I, B, R=0, recent_inclusive=True):
+    L = len(I)
+    rev = np.asarray(I)[::-1]
+    # select on the reversed array (ties then prefer the original higher position)
+    idx, _ = _orig["topk_select"](rev, B, 0, recent_inclusive) if R == 0 else (None, None)
+    if idx is None:
+        return _orig["topk_select"](I, B, R, recent_inclusive)
+    kept = sorted(L - 1 - idx)
+    sm = np.zeros(L, np.int64)
+    s = e = 0
+    for t in range(L):
+        if t in kept:
+            sm[t] = s
+            s += 1
+        else:
+            e += 1
+            sm[t] = -e
+    return np.array(kept), sm
+
+
+def _merge_unweighted(states):
+    lses = np.array([l for _, l in states])
+    a = sum(ai for ai, _ in states) / len(states)
+    return a, np.log(np.sum(np.exp(lses)))
+
+
+def _gqa_modulo(q, Kc, Vc, n, scale):
+    q = np.asarray(q, np.float64)
+    H_kv = Kc.shape[0]
+    o = np.zeros_like(q)
+    lse = np.zeros(q.shape[0])
+    for h in range(q.shape[0]):
+        o[h], lse[h] = _orig["attention_state"](q[h], Kc[h % H_kv, :n], Vc[h % H_kv, :n], scale)
+    return o, lse
+
+
+def _readout_transposed(q, M, b, w_g, eps=1e-6):
+    return _orig["memory_readout"](q, np.swapaxes(M, 1, 2), b, w_g, eps)
+
+
+def _stats_unscaled(mom):
+    kbar, vbar, St = _orig_mk["stats"](mom)
+    return kbar, vbar, mom["S"] - np.outer(mom["sv"], mom["sk"])
+
+
+def _estimate_no_sqrt(q, mom, d):
+    _, vbar, St = mk.stats(mom)
+    return vbar + St @ np.asarray(q, np.float64) / mom["n"]
+
+
+def _logz_no_count(q, mom, d):
+    return _orig_mk["log_Z_hat"](q, mom, d) - np.log(mom["n"])
+
+
+def _residual_plus(k, v, mom, d):
+    if mom["n"] == 0:
+        return np.asarray(v, np.float64).copy()
+    _, vbar, St = mk.stats(mom)
+    return np.asarray(v) - vbar + (np.asarray(k) @ St.T) / (mom["n"] * np.sqrt(d))
+
+
+MUTATIONS = [
+    ("phi drops +1", im, "phi", _phi_no_plus_one, [pins.test_phi_is_elu_plus_one, gold.test_memory_tiny]),
+    ("M transposed", im, "memory_build", _memory_transposed, [pins.test_memory_special_cases, gold.test_memory_tiny]),
+    ("decay order reversed", im, "memory_build", _memory_reversed_decay,
+     [lambda: pins.test_memory_closed_form_equals_recurrence(0.5), gold.test_memory_tiny]),
+    ("causal mask flipped", im, "score_matrix", _score_mask_flipped,
+     [lambda: pins.test_importance_brute_force_and_streaming("relu"), gold.test_indexer_tiny]),
+    ("ReLU after head sum", im, "score_matrix", _score_relu_after_sum, [pins.test_relu_is_per_head_before_the_gated_sum]),
+    ("logit scale dropped", im, "score_matrix", _score_no_scale, [pins.test_indexer_logit_is_scaled_cosine, gold.test_indexer_tiny]),
+    ("ties keep higher position", im, "topk_select", _topk_tie_high, [gold.test_indexer_tiny]),
+    ("merge ignores Z", im, "merge_states", _merge_unweighted, [lambda: pins.test_split_merge_equals_unsplit(0)]),
+    ("GQA head map h % H_kv", im, "decode_attention", _gqa_modulo, [pins.test_decode_attention_gqa_mapping]),
+    ("read-out uses M^T", im, "memory_readout", _readout_transposed, [pins.test_readout_special_cases, gold.test_memory_tiny]),
+    ("S~ missing 1/n_e", mk, "stats", _stats_unscaled, [pins.test_moment_stats_brute_force_and_additivity, gold.test_moments_tiny]),
+    ("estimate missing sqrt d", mk, "evicted_estimate", _estimate_no_sqrt, [pins.test_moment_estimate_is_linearised_softmax]),
+    ("Z^ missing n_e", mk, "log_Z_hat", _logz_no_count, [gold.test_moments_tiny]),
+    ("residual sign flipped", mk, "residual", _residual_plus,
+     [gold.test_moments_tiny, pins.test_residual_is_value_minus_estimate_at_its_key]),
+]
+
+
+@pytest.mark.parametrize("name,mod,attr,fn,tests", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, name, mod, attr, fn, tests):
+    monkeypatch.setattr(mod, attr, fn)
+    for t in tests:
+        with pytest.raises(Exception):
+            t()
