@@ -1,0 +1,232 @@
+/*
+ * libkvmem -- C ABI of the IndexMem / MomentKV hot path on AMD Instinct MI355X (gfx950).
+ *
+ * IndexMem: a learned MQA-style indexer scores every prefill token from an observation
+ * window of queries; the highest-scoring tokens are kept in a compact KV cache before the
+ * full prefill ("pre-eviction"); evicted tokens are folded into a fixed-size latent memory
+ * (M, b) by decayed outer products; decode attends over the kept tokens and adds a gated
+ * memory read-out.  MomentKV: evicted tokens are summarised by moment sums instead; they
+ * drive a residual-based eviction score and a normalisation-corrected output.
+ *
+ * Sources, cited by page title and section:
+ *   [IM]  "IndexMem - learned KV-cache eviction with latent memory", technical summary
+ *         (gist.science, arXiv 2605.25475), section 2 "Method", parts A and B.
+ *   [MKV] "MOMENTKV" technical summary (gist.science, arXiv 2606.01563), Method parts 1-4.
+ *   [ASM] "Context Memorization for Efficient Long Context Generation" technical summary
+ *         (gist.science, arXiv 2605.18226), Method: attention state (a, Z), online-softmax merge.
+ *
+ * Conventions (every entry point):
+ *   - Pointers named in the argument lists are DEVICE pointers owned by the caller unless
+ *     the comment says "host".  The library never allocates or frees memory.
+ *   - Every call only enqueues work on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream) and returns without synchronising.  Results are visible in stream order.
+ *   - Arguments are validated before any HIP call; a failed check returns a status and
+ *     enqueues nothing.  kvm_last_error() then gives a thread-local message.
+ *   - Layouts are dense row-major (C order) with the shapes given; element types are fixed
+ *     per argument (KVM_F32 / KVM_BF16 arguments follow desc->dtype).  Device pointers must
+ *     be 16-byte aligned.
+ *   - Workspaces: `ws` must hold kvm_*_workspace_size() bytes and be ZERO-FILLED before its
+ *     first use; every call leaves the counters it uses at zero again, so one zero-fill at
+ *     allocation suffices.  Two calls that share a workspace must not overlap in time.
+ *   - No floating-point atomics are used; repeated calls give bitwise identical results.
+ */
+#ifndef KVM_H
+#define KVM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVM_ABI_VERSION 1
+
+typedef enum {
+  KVM_OK = 0,
+  KVM_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  KVM_ERR_SHAPE = 2,       /* a size is non-positive or unsupported               */
+  KVM_ERR_DTYPE = 3,       /* dtype not KVM_F32 / KVM_BF16 or unsupported here     */
+  KVM_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned             */
+  KVM_ERR_RANGE = 5,       /* inconsistent sizes, e.g. budget below recent window */
+  KVM_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required          */
+  KVM_ERR_ARCH = 7,        /* the current device is not gfx950                    */
+  KVM_ERR_HIP = 8          /* a HIP runtime call failed                           */
+} kvm_status;
+
+typedef enum { KVM_F32 = 0, KVM_BF16 = 1 } kvm_dtype;
+
+int kvm_abi_version(void);
+const char* kvm_status_string(kvm_status s);
+/* Message of the last failed call on this thread ("" if none). */
+const char* kvm_last_error(void);
+/* Checks that the current HIP device is gfx950 (KVM_ERR_ARCH otherwise). */
+kvm_status kvm_check_device(void);
+
+/* ------------------------------------------------------------------------------------ *
+ * A1-A3  Indexer scores and per-key importance                        [IM 2.A]
+ *
+ * For one layer and b sequences of length L, with the last W positions as the
+ * observation window (query s at position L-W+s):
+ *   k_hat[t]   = RMSNorm_{gamma_k}(W_kI x_t)                      (shared key, d_I)
+ *   q_hat[s,h] = RMSNorm_{gamma_q}(W_qI[h] q_{s, c(h)}),  c(h) = floor(h*H_q/H_I)
+ *   g[s,h]     = sigmoid(W_g[h] . x_s)                            (learned head gate)
+ *   A[s,t]     = sum_h g[s,h] * relu(q_hat[s,h] . k_hat[t] / sqrt(d_I))   for t <= pos(s)
+ *   I[t]       = max_s A[s,t]                                     (running max-pool)
+ * The head gate, per-head ReLU, RMSNorm and 1/sqrt(d_I) are readings of the section's
+ * "MQA-style indexer with QK norm and a learnable gate on head contributions".
+ * Arithmetic: projections with fp32 accumulation; the score contraction uses fp16
+ * hi+lo split operands on the matrix cores (relative error ~1e-7 of each logit), so I
+ * carries near-fp32 accuracy.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t b, L, D;         /* batch, prefill length, hidden size                        */
+  int32_t H_q, d;          /* model query heads, head dim                                */
+  int32_t H_I, d_I, W;     /* indexer heads, indexer dim, window (1 <= W <= L)            */
+  int32_t dtype;           /* kvm_dtype of X, Qwin and the three weight matrices         */
+  float eps_rms;           /* RMSNorm epsilon (1e-6)                                     */
+} kvm_index_desc;
+
+size_t kvm_index_workspace_size(const kvm_index_desc* desc);
+/*
+ * X      [b, L, D]            hidden states (dtype)
+ * Qwin   [b, W, H_q, d]       model queries of positions L-W .. L-1 (dtype)
+ * W_kI   [d_I, D], W_qI [H_I, d_I, d], W_g [H_I, D]   (dtype);  gamma_k, gamma_q [d_I] f32
+ * I      [b, L] f32           output importance
+ * khat   [b, L, d_I] f32      optional output (NULL to skip): the normalised keys
+ * Supported: d_I in {32, 64}, d in {64, 128}; D % 8 == 0.
+ */
+kvm_status kvm_index_score(const kvm_index_desc* desc, const void* X, const void* Qwin,
+                           const void* W_kI, const float* gamma_k, const void* W_qI,
+                           const float* gamma_q, const void* W_g, float* I, float* khat,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * A4  Pre-eviction top-k                                              [IM 2.A]
+ *
+ * Per row of I [rows, L]: keep the last R positions (recent window) plus the n_top
+ * highest-scoring positions before them, n_top = B - R if recent_inclusive else B,
+ * ordered by (score descending, position ascending) -- ties keep the lower position.
+ * NaN scores order as -inf, -0 as +0.  If n_top >= L - R every position is kept.
+ * Outputs: idx [rows, keep] i32 = kept positions ascending (keep = min(L, n_top + R));
+ *          slot_map [rows, L] i32: slot (>= 0) of a kept position, or -i for the i-th
+ *          evicted position in ascending order (i = 1..L-keep).
+ * Errors: KVM_ERR_RANGE if recent_inclusive and B < R, or B < 0, R < 0.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t rows, L, B, R;
+  int32_t recent_inclusive;  /* 1: R counts inside B; 0: B plus R                       */
+} kvm_topk_desc;
+
+int32_t kvm_topk_keep(const kvm_topk_desc* desc);  /* keep = number of kept positions   */
+kvm_status kvm_topk_select(const kvm_topk_desc* desc, const float* I, int32_t* idx,
+                           int32_t* slot_map, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * A5 + A6 / V2  Compaction with a fused latent-memory or moment build  [IM 2.A, 2.B; MKV 1]
+ *
+ * One pass over K, V: kept rows go to the head-major cache Kc, Vc [b, H_kv, cap, d] at
+ * their slot; evicted rows are folded in:
+ *   KVM_FUSE_MEM:     n = number evicted; with eviction ranks i = 1..n (ascending position)
+ *                     M <- lam^n M + sum_i lam^(n-i) v_i phi(k_i)^T,
+ *                     bvec <- lam^n bvec + sum_i lam^(n-i) phi(k_i),   phi = elu + 1.
+ *   KVM_FUSE_MOMENTS: n_e += n; s_k += sum k; s_v += sum v; S += sum v k^T.
+ * K, V:  token-major [b, L, H_kv, d] (kv_head_major = 0) or head-major [b, H_kv, L, d].
+ * slot_map: [b, L] (shared by all KV heads) or [b, H_kv, L] (per_head = 1), as produced
+ *           by kvm_topk_select; n is taken as the count of negative entries (= L - keep).
+ * keep:  number of kept positions per row (the caller's budget arithmetic; host value).
+ * Kc/Vc may be NULL (memory/moment update only).  M [b,H_kv,d,d] f32 (rows index v,
+ * columns index phi(k)), bvec [b,H_kv,d] f32; moments n_e [b,H_kv] i32, s_k, s_v
+ * [b,H_kv,d] f32, S [b,H_kv,d,d] f32.  All state arrays are read-modify-write.
+ * Supported: d in {64, 128}; cap >= keep.
+ * Arithmetic: bf16 inputs use the matrix cores with exact bf16 V (or K) operands and
+ * hi+lo bf16 split of lam^(n-i) phi(k) (relative error ~1e-5); fp32 inputs use fp32 FMA.
+ * ------------------------------------------------------------------------------------ */
+#define KVM_FUSE_MEM 1
+#define KVM_FUSE_MOMENTS 2
+
+typedef struct {
+  int32_t b, L, H_kv, d, cap, keep;
+  int32_t dtype;           /* kvm_dtype of K, V, Kc, Vc                                  */
+  int32_t per_head;        /* slot_map per (b, KV head)                                  */
+  int32_t kv_head_major;   /* layout of K, V                                             */
+  int32_t flags;           /* KVM_FUSE_MEM or KVM_FUSE_MOMENTS (or 0: copy only)          */
+  float lam;               /* memory decay, 0 <= lam <= 1                                */
+} kvm_compact_desc;
+
+size_t kvm_compact_workspace_size(const kvm_compact_desc* desc);
+kvm_status kvm_compact_kv(const kvm_compact_desc* desc, const void* K, const void* V,
+                          const int32_t* slot_map, void* Kc, void* Vc, float* M, float* bvec,
+                          int32_t* n_e, float* s_k, float* s_v, float* S,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Row gather that follows a slot map: dst[r, slot_map[r,t], :] = src[r, t, :] for kept t.
+ * src [rows, L, elem_bytes], dst [rows, cap, elem_bytes]; elem_bytes % 4 == 0.  Used to
+ * carry per-token side data (indexer keys, importance, positions) into the compact pool. */
+kvm_status kvm_gather_rows(int32_t rows, int32_t L, int32_t cap, int32_t elem_bytes,
+                           const void* src, const int32_t* slot_map, void* dst, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * A6/A7  Rank-r decayed memory update                                  [IM 2.B]
+ *
+ * For rows i = 1..r in the given order (per sequence and KV head):
+ *   M <- lam^r M + sum_i lam^(r-i) v_i phi(k_i)^T,  bvec <- lam^r bvec + sum_i lam^(r-i) phi(k_i).
+ * K_rows, V_rows: [b, r, H_kv, d] (dtype), or, with row_slot != NULL, r = 1 and the row
+ * is taken from the caches Kc, Vc [b, H_kv, cap, d] at slot row_slot[b] (device i32).
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t b, H_kv, d, r, cap;
+  int32_t dtype;
+  float lam;
+} kvm_mem_desc;
+
+kvm_status kvm_mem_update(const kvm_mem_desc* desc, const void* K_rows, const void* V_rows,
+                          const int32_t* row_slot, float* M, float* bvec, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * A8 + A9 / V3  Split-K decode attention with memory read-out          [IM 2.B; ASM; MKV 4]
+ *
+ * Per sequence bb and query head h (KV head g = h / G, G = H_q / H_kv):
+ *   the new token (k_new, v_new) is first written to slot len[bb] (or append_slot[bb]);
+ *   attention over the first n = len[bb] + 1 slots (len[bb] if append_slot is given, or
+ *   if k_new is NULL) is computed as n_split partial states (a_c, lse_c) over disjoint
+ *   slot ranges, merged by lse = log sum_c exp(lse_c), a = sum_c exp(lse_c - lse) a_c;
+ *   mode KVM_READ_NONE:    o = a
+ *   mode KVM_READ_MEMORY:  m = M_g phi(q) / (bvec_g . phi(q) + eps), o = a + sigmoid(w_g[h].q) m
+ *   mode KVM_READ_MOMENTS: f_E = s_v/n_e + (S - s_v s_k^T/n_e) q / (n_e sqrt d),
+ *                          log Z_E = log n_e + (q.s_k/n_e)/sqrt d,
+ *                          w = sigmoid(lse - log Z_E), o = w a + (1 - w) f_E (o = a if n_e = 0)
+ * q [b,H_q,d], k_new/v_new [b,H_kv,d] (dtype, nullable), Kc, Vc [b,H_kv,cap,d] (dtype),
+ * len [b] i32 (not modified), append_slot [b] i32 (nullable), o [b,H_q,d] f32,
+ * lse [b,H_q] f32 (nullable: log-partition of the retained attention, scale applied).
+ * The library never reads or writes a slot >= cap (n is clamped to cap).
+ * Supported: d in {64, 128}, G in {1, 2, 4, 8}; n_split 0 chooses automatically.
+ * ------------------------------------------------------------------------------------ */
+#define KVM_READ_NONE 0
+#define KVM_READ_MEMORY 1
+#define KVM_READ_MOMENTS 2
+
+typedef struct {
+  int32_t b, H_q, H_kv, d, cap;
+  int32_t n_split;         /* 0 = auto                                                  */
+  int32_t dtype;           /* of q, k_new, v_new, Kc, Vc, w_g                           */
+  int32_t mode;            /* KVM_READ_*                                                */
+  float scale;             /* logit scale, normally 1/sqrt(d)                            */
+  float eps;               /* read-out epsilon (1e-6)                                    */
+} kvm_decode_desc;
+
+size_t kvm_decode_workspace_size(const kvm_decode_desc* desc);
+kvm_status kvm_decode_attn_mem(const kvm_decode_desc* desc, const void* q, const void* k_new,
+                               const void* v_new, const int32_t* append_slot, void* Kc, void* Vc,
+                               const int32_t* len, const float* M, const float* bvec,
+                               const void* w_g, const int32_t* n_e, const float* s_k,
+                               const float* s_v, const float* S, float* o, float* lse,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* len[i] += delta for i < b (device i32): advances cache lengths between decode steps. */
+kvm_status kvm_len_add(int32_t* len, int32_t b, int32_t delta, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVM_H */

@@ -1,0 +1,165 @@
+"""Thin torch-facing binding of libkvmem: argument marshalling only.
+
+Each function has the name of the C entry point it calls.  Tensors must be on the
+current HIP device; work is enqueued on torch's current stream unless `stream` is
+given.  Nothing here computes any part of the method -- every step runs in libkvmem.
+"""
+import ctypes as C
+import math
+
+import torch
+
+from . import _lib as K
+from ._lib import check, lib
+
+_DT = {torch.bfloat16: K.KVM_BF16, torch.float32: K.KVM_F32}
+_ws_cache = {}
+
+
+def _p(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dtype(t):
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def workspace(nbytes, device=None, stream=None, tag="default"):
+    """A zero-filled workspace of at least nbytes, cached per (device, stream, tag).
+    libkvmem leaves the counters it uses at zero, so the buffer is reusable in stream order."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    s = torch.cuda.current_stream(dev) if stream is None else stream
+    key = (dev.index, s.cuda_stream, tag)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+# ------------------------------------------------------------------------------- decode
+
+def decode_desc(q, Kc, mode, n_split=0, scale=None, eps=1e-6):
+    b, H_q, d = q.shape
+    _, H_kv, cap, _ = Kc.shape
+    return K.DecodeDesc(b=b, H_q=H_q, H_kv=H_kv, d=d, cap=cap, n_split=n_split, dtype=_dtype(q),
+                        mode=mode, scale=(1.0 / math.sqrt(d)) if scale is None else scale, eps=eps)
+
+
+def kvm_decode_attn_mem(q, Kc, Vc, len_, k_new=None, v_new=None, append_slot=None, M=None, bvec=None,
+                        w_g=None, moments=None, o=None, lse=None, n_split=0, scale=None, eps=1e-6,
+                        stream=None, ws=None):
+    """Decode attention over Kc/Vc [b,H_kv,cap,d] (appending k_new/v_new), merged split-K
+    states, plus the memory read-out (M, bvec, w_g) or the MomentKV mix (moments =
+    dict(n_e, s_k, s_v, S)).  Returns o [b,H_q,d] f32 (and lse [b,H_q] if given)."""
+    _contig(q, Kc, Vc, len_, k_new, v_new, append_slot, M, bvec, w_g)
+    mode = K.KVM_READ_MEMORY if M is not None else (K.KVM_READ_MOMENTS if moments is not None else K.KVM_READ_NONE)
+    desc = decode_desc(q, Kc, mode, n_split, scale, eps)
+    if o is None:
+        o = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    nb = lib().kvm_decode_workspace_size(C.byref(desc))
+    if ws is None:
+        ws = workspace(nb, q.device, stream, "decode")
+    mo = moments or {}
+    check(lib().kvm_decode_attn_mem(C.byref(desc), _p(q), _p(k_new), _p(v_new), _p(append_slot), _p(Kc),
+                                    _p(Vc), _p(len_), _p(M), _p(bvec), _p(w_g), _p(mo.get("n_e")),
+                                    _p(mo.get("s_k")), _p(mo.get("s_v")), _p(mo.get("S")), _p(o), _p(lse),
+                                    _p(ws), ws.numel(), _stream(stream)))
+    return o
+
+
+def kvm_len_add(len_, delta=1, stream=None):
+    check(lib().kvm_len_add(_p(len_), len_.numel(), int(delta), _stream(stream)))
+    return len_
+
+
+# ------------------------------------------------------------------------------- top-k
+
+def kvm_topk_keep(L, B, R=0, recent_inclusive=True, rows=1):
+    d = K.TopkDesc(rows=rows, L=L, B=B, R=R, recent_inclusive=int(bool(recent_inclusive)))
+    return lib().kvm_topk_keep(C.byref(d))
+
+
+def kvm_topk_select(I, B, R=0, recent_inclusive=True, idx=None, slot_map=None, stream=None):
+    """I [rows, L] f32 -> (idx [rows, keep] i32 ascending, slot_map [rows, L] i32)."""
+    _contig(I)
+    if I.dim() == 1:
+        I = I[None]
+    rows, L = I.shape
+    d = K.TopkDesc(rows=rows, L=L, B=B, R=R, recent_inclusive=int(bool(recent_inclusive)))
+    keep = lib().kvm_topk_keep(C.byref(d))
+    if idx is None:
+        idx = torch.empty((rows, max(keep, 0)), dtype=torch.int32, device=I.device)
+    if slot_map is None:
+        slot_map = torch.empty((rows, L), dtype=torch.int32, device=I.device)
+    check(lib().kvm_topk_select(C.byref(d), _p(I), _p(idx), _p(slot_map), _stream(stream)))
+    return idx, slot_map
+
+
+# ------------------------------------------------------------------------------- compaction
+
+def kvm_compact_kv(Kt, Vt, slot_map, keep, cap=None, Kc=None, Vc=None, M=None, bvec=None, moments=None,
+                   lam=1.0, per_head=False, kv_head_major=False, copy=True, stream=None, ws=None):
+    """Compact kept rows of K, V ([b,L,H_kv,d], or [b,H_kv,L,d] if kv_head_major) into
+    Kc, Vc [b,H_kv,cap,d]; fold evicted rows into (M, bvec) or into moments
+    dict(n_e, s_k, s_v, S).  Returns (Kc, Vc)."""
+    _contig(Kt, Vt, slot_map, Kc, Vc, M, bvec)
+    if kv_head_major:
+        b, H_kv, L, d = Kt.shape
+    else:
+        b, L, H_kv, d = Kt.shape
+    cap = keep if cap is None else cap
+    if copy and Kc is None:
+        Kc = torch.zeros((b, H_kv, cap, d), dtype=Kt.dtype, device=Kt.device)
+        Vc = torch.zeros((b, H_kv, cap, d), dtype=Vt.dtype, device=Vt.device)
+    flags = K.KVM_FUSE_MEM if M is not None else (K.KVM_FUSE_MOMENTS if moments is not None else 0)
+    desc = K.CompactDesc(b=b, L=L, H_kv=H_kv, d=d, cap=cap, keep=keep, dtype=_dtype(Kt), per_head=int(per_head),
+                         kv_head_major=int(kv_head_major), flags=flags, lam=lam)
+    nb = lib().kvm_compact_workspace_size(C.byref(desc))
+    if ws is None:
+        ws = workspace(nb, Kt.device, stream, "compact")
+    mo = moments or {}
+    check(lib().kvm_compact_kv(C.byref(desc), _p(Kt), _p(Vt), _p(slot_map), _p(Kc), _p(Vc), _p(M), _p(bvec),
+                               _p(mo.get("n_e")), _p(mo.get("s_k")), _p(mo.get("s_v")), _p(mo.get("S")),
+                               _p(ws), ws.numel(), _stream(stream)))
+    return Kc, Vc
+
+
+def kvm_gather_rows(src, slot_map, cap, dst=None, stream=None):
+    """src [rows, L, ...] -> dst [rows, cap, ...] following slot_map [rows, L]."""
+    _contig(src, slot_map)
+    rows, L = slot_map.shape
+    eb = src[0, 0].numel() * src.element_size()
+    if dst is None:
+        dst = torch.zeros((rows, cap, *src.shape[2:]), dtype=src.dtype, device=src.device)
+    check(lib().kvm_gather_rows(rows, L, cap, eb, _p(src), _p(slot_map), _p(dst), _stream(stream)))
+    return dst
+
+
+def kvm_mem_update(K_rows, V_rows, M, bvec, lam, row_slot=None, stream=None):
+    """Rank-r decayed update of M [b,H_kv,d,d], bvec [b,H_kv,d] with rows K_rows/V_rows
+    [b,r,H_kv,d]; with row_slot [b] i32 the (single) row comes from caches [b,H_kv,cap,d]."""
+    _contig(K_rows, V_rows, M, bvec, row_slot)
+    if row_slot is not None:
+        b, H_kv, cap, d = K_rows.shape
+        r = 1
+    else:
+        b, r, H_kv, d = K_rows.shape
+        cap = 0
+    desc = K.MemDesc(b=b, H_kv=H_kv, d=d, r=r, cap=cap, dtype=_dtype(K_rows), lam=lam)
+    check(lib().kvm_mem_update(C.byref(desc), _p(K_rows), _p(V_rows), _p(row_slot), _p(M), _p(bvec),
+                               _stream(stream)))
+    return M, bvec

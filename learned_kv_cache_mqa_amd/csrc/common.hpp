@@ -1,0 +1,147 @@
+// Shared device helpers and host-side validation for libkvmem (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+#include <string>
+
+#include "kvm.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+namespace kvm {
+
+// ------------------------------------------------------------------------------ host side
+
+kvm_status set_error(kvm_status s, const char* fmt, ...);
+kvm_status check_hip(hipError_t e, const char* what);
+kvm_status require_gfx950();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define KVM_REQUIRE(cond, status, ...)                 \
+  do {                                                 \
+    if (!(cond)) return ::kvm::set_error(status, __VA_ARGS__); \
+  } while (0)
+
+#define KVM_PTR(p) KVM_REQUIRE((p) != nullptr, KVM_ERR_NULL, "%s is NULL", #p)
+#define KVM_ALIGNED(p) KVM_REQUIRE(::kvm::aligned16(p), KVM_ERR_ALIGN, "%s is not 16-byte aligned", #p)
+#define KVM_PTR_ALIGNED(p) do { KVM_PTR(p); KVM_ALIGNED(p); } while (0)
+#define KVM_OPT_ALIGNED(p) do { if (p) KVM_ALIGNED(p); } while (0)
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Every workspace starts with a fixed region of completion counters that calls leave at
+// zero; data sections follow it.  Counters never move, so one zero-filled workspace can
+// serve calls with different descriptors.
+constexpr size_t kCounterBytes = 65536;
+constexpr int kMaxCounters = int(kCounterBytes / sizeof(int));
+
+// ------------------------------------------------------------------------------ device side
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float(uint32_t(u) << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Load EPL consecutive elements (16 bytes) as floats.
+template <typename T> struct Vec16;
+template <> struct Vec16<uint16_t> {  // bf16 storage
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const uint16_t* p, float (&out)[8]) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
+    out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
+    out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
+    out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+  }
+  __device__ __forceinline__ static void unpack(const uint4& v, float (&out)[8]) {
+    out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
+    out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
+    out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
+    out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+  }
+};
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const float* p, float (&out)[4]) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  }
+  __device__ __forceinline__ static void unpack(const uint4& v, float (&out)[4]) {
+    out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+  }
+};
+
+template <typename T> __device__ __forceinline__ float load_scalar(const T* p);
+template <> __device__ __forceinline__ float load_scalar<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+template <> __device__ __forceinline__ float load_scalar<float>(const float* p) { return *p; }
+
+// Cross-lane sums inside groups of N consecutive lanes (N in 1..64); every lane of the group
+// ends with the group total.
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float swz_xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+__device__ __forceinline__ float shfl_xor32(float x) {
+  int lane = __lane_id();
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(x)));
+}
+
+template <int N> __device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group");
+  if (N >= 2) x += dpp<0xB1>(x);        // xor 1
+  if (N >= 4) x += dpp<0x4E>(x);        // xor 2
+  if (N == 8) x += dpp<0x141>(x);       // mirror within 8 lanes
+  if (N >= 16) { x += dpp<0x124>(x); x += dpp<0x128>(x); }   // rotate 4, 8 within 16
+  if (N >= 32) x += swz_xor16(x);
+  if (N >= 64) x += shfl_xor32(x);
+  return x;
+}
+template <int N> __device__ __forceinline__ float group_max(float x) {
+  if (N >= 2) x = fmaxf(x, dpp<0xB1>(x));
+  if (N >= 4) x = fmaxf(x, dpp<0x4E>(x));
+  if (N == 8) x = fmaxf(x, dpp<0x141>(x));
+  if (N >= 16) { x = fmaxf(x, dpp<0x124>(x)); x = fmaxf(x, dpp<0x128>(x)); }
+  if (N >= 32) x = fmaxf(x, swz_xor16(x));
+  if (N >= 64) x = fmaxf(x, shfl_xor32(x));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+
+__device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+__device__ __forceinline__ float sigmoid_f(float x) {
+  float e = __expf(-fabsf(x));
+  return x >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+}
+
+// Last-block ticket: returns true in every thread of the block that arrives last among
+// `n` blocks sharing *counter, and resets the counter for the next call.  Writes made by
+// the other blocks before their ticket are visible to the last block afterwards.
+__device__ __forceinline__ bool last_block_ticket(int* counter, int n, int* smem_flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    int t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    int last = (t == n - 1);
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *smem_flag = last;
+  }
+  __syncthreads();
+  bool last = *smem_flag != 0;
+  if (last) __threadfence();
+  return last;
+}
+
+}  // namespace kvm

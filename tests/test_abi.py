@@ -1,0 +1,65 @@
+"""The C ABI on the CPU: the library loads, exports every entry point include/kvm.h
+declares, and rejects bad arguments before any HIP call (so no GPU is needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kvm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvm_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from learned_kv_cache_mqa_amd import _lib
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 10
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    from learned_kv_cache_mqa_amd import _lib
+    assert set(names) <= set(_lib.SIGNATURES), set(names) - set(_lib.SIGNATURES)
+
+
+def test_version_and_strings(L):
+    assert L.kvm_abi_version() == 1
+    assert L.kvm_status_string(6) == b"workspace too small"
+
+
+FAKE = 0x7f0000000000      # never dereferenced: validation fails before any HIP call
+
+
+def _decode(L, **kw):
+    from learned_kv_cache_mqa_amd import _lib as K
+    d = K.DecodeDesc(b=1, H_q=32, H_kv=8, d=128, cap=64, n_split=0, dtype=K.KVM_BF16,
+                     mode=K.KVM_READ_MEMORY, scale=0.088, eps=1e-6)
+    for k, v in kw.pop("desc", {}).items():
+        setattr(d, k, v)
+    p = dict(q=FAKE, kn=FAKE, vn=FAKE, app=None, Kc=FAKE, Vc=FAKE, len=FAKE, M=FAKE, b=FAKE, wg=FAKE,
+             ne=None, sk=None, sv=None, S=None, o=FAKE, lse=None, ws=FAKE, wsb=1 << 30)
+    p.update(kw)
+    return L.kvm_decode_attn_mem(C.byref(d), *[None if p[k] is None else C.c_void_p(p[k]) if k != "wsb" else p[k]
+                                               for k in ["q", "kn", "vn", "app", "Kc", "Vc", "len", "M", "b", "wg",
+                                                         "ne", "sk", "sv", "S", "o", "lse", "ws", "wsb"]], None)
+
+
+def test_decode_validation(L):
+    assert _decode(L, desc=dict(d=96)) == 2
+    assert _decode(L, desc=dict(H_q=24)) == 2           # G = 3
+    assert _decode(L, desc=dict(dtype=7)) == 3
+    assert _decode(L, q=None) == 1
+    assert _decode(L, M=None) == 1                       # memory mode needs M
+    assert _decode(L, kn=None) == 1                      # k_new without v_new
+    assert _decode(L, Kc=FAKE + 4) == 4
+    assert _decode(L, wsb=16) == 6
+    assert b"workspace" in L.kvm_last_error()
+    assert _decode(L, desc=dict(mode=2)) == 1            # moments mode needs the moments

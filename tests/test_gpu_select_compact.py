@@ -1,0 +1,197 @@
+"""Pre-eviction top-k (bit-exact), compaction (bit-exact) and the fused memory / moment
+build against the oracle."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import indexmem as im
+from oracle import momentkv as mk
+from synth import gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _scores(rows, L, seed, ties=0, specials=False):
+    s = gen.make_scores(7, rows, L, seed, ties)
+    if specials and L >= 8:
+        r = gen.rng(7, 1, 0, seed)
+        for row in range(rows):
+            pos = r.choice(L, size=min(L, 6), replace=False)
+            s[row, pos[0]] = np.nan
+            s[row, pos[1]] = -0.0
+            s[row, pos[2]] = 0.0
+            s[row, pos[3]] = -np.inf
+            s[row, pos[4]] = np.inf
+    return s
+
+
+TOPK = [  # rows, L, B, R, inclusive, ties, specials
+    (1, 1, 1, 0, True, 0, False),
+    (3, 5, 2, 1, True, 2, False),
+    (2, 512, 64, 0, True, 0, True),
+    (1, 4096, 410, 32, True, 0, False),
+    (8, 16384, 1638, 32, True, 0, False),
+    (8, 16384, 1638, 32, True, 3, True),
+    (1, 131072, 1024, 64, False, 0, False),
+    (32, 32768, 128, 0, True, 0, False),
+    (4, 3000, 3000, 0, True, 0, False),   # keep all
+    (4, 3000, 7, 7, True, 0, False),      # recent window only
+    (2, 1025, 1024, 64, False, 50, True),  # more slots than candidates
+]
+
+
+@pytest.mark.parametrize("rows,L,B,R,inc,ties,specials", TOPK)
+def test_topk_bit_exact(rows, L, B, R, inc, ties, specials):
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np
+    I = _scores(rows, L, seed=L + B, ties=ties, specials=specials)
+    idx, sm = api.kvm_topk_select(to_dev(I), B, R, inc)
+    torch.cuda.synchronize()
+    gi, gs = to_np(idx), to_np(sm)
+    for r in range(rows):
+        ri, rs = im.topk_select(I[r].astype(np.float64), B, R, inc)
+        assert gi[r].tolist() == ri.tolist(), f"row {r}"
+        assert gs[r].tolist() == rs.tolist(), f"row {r}"
+
+
+def _kv(dtype, b, L, H, d, seed):
+    r = gen.rng(91, seed, 0, 0)
+    return (gen.to_storage(r.standard_normal((b, L, H, d)), dtype),
+            gen.to_storage(r.standard_normal((b, L, H, d)), dtype))
+
+
+COMPACT = [  # dtype, b, L, H_kv, d, B, R, lam, cap_extra
+    ("bf16", 1, 4096, 8, 128, 410, 32, 0.995, 256),
+    ("bf16", 2, 1000, 2, 128, 100, 7, 0.995, 3),
+    ("bf16", 1, 3001, 3, 64, 200, 0, 0.99, 0),
+    ("bf16", 1, 700, 2, 128, 50, 0, 1.0, 0),
+    ("bf16", 1, 700, 2, 128, 50, 0, 0.0, 0),
+    ("bf16", 1, 40, 1, 128, 40, 0, 0.9, 0),   # nothing evicted
+    ("f32", 1, 512, 1, 64, 64, 0, 0.99, 16),
+    ("f32", 2, 333, 2, 128, 30, 5, 0.9, 0),
+]
+
+
+@pytest.mark.parametrize("dtype,b,L,H,d,B,R,lam,extra", COMPACT)
+def test_compact_and_memory_build(dtype, b, L, H, d, B, R, lam, extra):
+    import torch
+    lam = float(np.float32(lam))      # the library takes lambda as fp32: both sides use that value
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, assert_output, normwise, maxabs
+    Kt, Vt = _kv(dtype, b, L, H, d, seed=L + d)
+    I = _scores(b, L, seed=L)
+    smaps = [im.topk_select(I[i].astype(np.float64), B, R)[1] for i in range(b)]
+    keep = L - int((smaps[0] < 0).sum())
+    cap = keep + extra
+    rM = gen.rng(92, L, 0, 0)
+    M0 = rM.standard_normal((b, H, d, d)).astype(np.float32)
+    b0 = np.abs(rM.standard_normal((b, H, d))).astype(np.float32)
+    M = to_dev(M0.copy())
+    bv = to_dev(b0.copy())
+    Kc, Vc = api.kvm_compact_kv(to_dev(Kt), to_dev(Vt), to_dev(np.stack(smaps).astype(np.int32)), keep, cap,
+                                M=M, bvec=bv, lam=lam)
+    torch.cuda.synchronize()
+    gK, gV, gM, gb = to_np(Kc), to_np(Vc), to_np(M), to_np(bv)
+    Kd, Vd = gen.from_storage(Kt, dtype), gen.from_storage(Vt, dtype)
+    for i in range(b):
+        rK, rV = im.compact(Kt[i], Vt[i], smaps[i], cap)
+        assert gK[i].tobytes() == rK.tobytes()
+        assert gV[i].tobytes() == rV.tobytes()
+        ev = im.evicted_in_order(smaps[i])
+        for g in range(H):
+            refM, refb = im.memory_build(Kd[i, ev, g], Vd[i, ev, g], lam, M0[i, g], b0[i, g])
+            assert_output(gM[i, g], refM, dtype, "M")
+            assert_output(gb[i, g], refb, dtype, "b")
+            if dtype == "bf16":
+                # hi+lo split keeps ~16 bits of lam^(n-i) phi(k): far inside the bar
+                assert normwise(gM[i, g], refM) < 1e-4
+                assert normwise(gb[i, g], refb) < 1e-5
+
+
+@pytest.mark.parametrize("head_major", [False, True])
+def test_moment_update_per_head(head_major):
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, normwise
+    b, L, H, d, keep = 2, 2000, 4, 128, 999
+    Kt, Vt = _kv("bf16", b, L, H, d, seed=5)
+    if head_major:
+        Kt, Vt = np.ascontiguousarray(Kt.transpose(0, 2, 1, 3)), np.ascontiguousarray(Vt.transpose(0, 2, 1, 3))
+    I = _scores(b * H, L, seed=9)
+    smaps = np.stack([im.topk_select(I[r].astype(np.float64), keep, 0)[1] for r in range(b * H)]).astype(np.int32)
+    r0 = gen.rng(93, 0, 0, 0)
+    n0 = np.full((b, H), 17, np.int32)
+    sk0, sv0 = r0.standard_normal((b, H, d)).astype(np.float32), r0.standard_normal((b, H, d)).astype(np.float32)
+    S0 = r0.standard_normal((b, H, d, d)).astype(np.float32)
+    mom = dict(n_e=to_dev(n0.copy()), s_k=to_dev(sk0.copy()), s_v=to_dev(sv0.copy()), S=to_dev(S0.copy()))
+    Kc, Vc = api.kvm_compact_kv(to_dev(Kt), to_dev(Vt), to_dev(smaps), keep, keep + 5, moments=mom, per_head=True,
+                                kv_head_major=head_major)
+    torch.cuda.synchronize()
+    Kd, Vd = gen.from_storage(Kt, "bf16"), gen.from_storage(Vt, "bf16")
+    gK = to_np(Kc)
+    for i in range(b):
+        for g in range(H):
+            sm = smaps[i * H + g]
+            kk = Kd[i, g] if head_major else Kd[i, :, g]
+            vv = Vd[i, g] if head_major else Vd[i, :, g]
+            ev = np.nonzero(sm < 0)[0]
+            m = dict(n=17, sk=sk0[i, g].astype(np.float64), sv=sv0[i, g].astype(np.float64),
+                     S=S0[i, g].astype(np.float64))
+            m = mk.add(m, kk[ev], vv[ev])
+            assert int(to_np(mom["n_e"])[i, g]) == m["n"]
+            assert normwise(to_np(mom["S"])[i, g], m["S"]) < 1e-5
+            assert normwise(to_np(mom["s_k"])[i, g], m["sk"]) < 1e-5
+            assert normwise(to_np(mom["s_v"])[i, g], m["sv"]) < 1e-5
+            kept = np.nonzero(sm >= 0)[0]
+            src = (Kt[i, g] if head_major else Kt[i, :, g])[kept]
+            assert gK[i, g, :keep].tobytes() == src.tobytes()
+
+
+def test_gather_rows_and_rank_r_update():
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, normwise
+    rows, L, E = 3, 777, 64
+    src = gen.rng(94, 0, 0, 0).standard_normal((rows, L, E)).astype(np.float32)
+    I = _scores(rows, L, seed=3)
+    smaps = np.stack([im.topk_select(I[r].astype(np.float64), 70, 6)[1] for r in range(rows)]).astype(np.int32)
+    dst = api.kvm_gather_rows(to_dev(src), to_dev(smaps), 80)
+    torch.cuda.synchronize()
+    got = to_np(dst)
+    for r in range(rows):
+        kept = np.nonzero(smaps[r] >= 0)[0]
+        assert got[r, :len(kept)].tobytes() == src[r, kept].tobytes()
+        assert not got[r, len(kept):].any()
+    # rank-r decayed update == sequential recurrence
+    b, rr, H, d, lam = 2, 37, 3, 128, float(np.float32(0.97))
+    rg = gen.rng(95, 0, 0, 0)
+    Kr = gen.to_storage(rg.standard_normal((b, rr, H, d)), "bf16")
+    Vr = gen.to_storage(rg.standard_normal((b, rr, H, d)), "bf16")
+    M0 = rg.standard_normal((b, H, d, d)).astype(np.float32)
+    b0 = rg.standard_normal((b, H, d)).astype(np.float32)
+    M, bv = to_dev(M0.copy()), to_dev(b0.copy())
+    api.kvm_mem_update(to_dev(Kr), to_dev(Vr), M, bv, lam)
+    torch.cuda.synchronize()
+    Kd, Vd = gen.from_storage(Kr, "bf16"), gen.from_storage(Vr, "bf16")
+    for i in range(b):
+        for g in range(H):
+            rM, rb = im.memory_update_sequential(Kd[i, :, g], Vd[i, :, g], lam, M0[i, g], b0[i, g])
+            assert normwise(to_np(M)[i, g], rM) < 1e-5
+            assert normwise(to_np(bv)[i, g], rb) < 1e-5
+    # single row taken from the cache at a device-given slot
+    cap = 11
+    Kc = gen.to_storage(rg.standard_normal((b, H, cap, d)), "bf16")
+    Vc = gen.to_storage(rg.standard_normal((b, H, cap, d)), "bf16")
+    slots = np.array([3, 10], np.int32)
+    M, bv = to_dev(M0.copy()), to_dev(b0.copy())
+    api.kvm_mem_update(to_dev(Kc), to_dev(Vc), M, bv, lam, row_slot=to_dev(slots))
+    torch.cuda.synchronize()
+    Kd, Vd = gen.from_storage(Kc, "bf16"), gen.from_storage(Vc, "bf16")
+    for i in range(b):
+        for g in range(H):
+            rM, rb = im.memory_update_sequential(Kd[i, g, slots[i]][None], Vd[i, g, slots[i]][None], lam,
+                                                 M0[i, g], b0[i, g])
+            assert normwise(to_np(M)[i, g], rM) < 1e-5
+            assert normwise(to_np(bv)[i, g], rb) < 1e-5
