@@ -163,3 +163,24 @@ def kvm_mem_update(K_rows, V_rows, M, bvec, lam, row_slot=None, stream=None):
     check(lib().kvm_mem_update(C.byref(desc), _p(K_rows), _p(V_rows), _p(row_slot), _p(M), _p(bvec),
                                _stream(stream)))
     return M, bvec
+
+
+# ------------------------------------------------------------------------------- indexer
+
+def kvm_index_score(X, Qwin, W_kI, gamma_k, W_qI, gamma_q, W_g, I=None, khat=None, eps=1e-6, stream=None,
+                    ws=None):
+    """Indexer importance I [b, L] f32 from hidden states X [b,L,D] and the window's model
+    queries Qwin [b,W,H_q,d]; optionally the normalised keys khat [b,L,d_I] f32."""
+    _contig(X, Qwin, W_kI, gamma_k, W_qI, gamma_q, W_g, I, khat)
+    b, L, D = X.shape
+    _, W, H_q, d = Qwin.shape
+    H_I, d_I, _ = W_qI.shape
+    desc = K.IndexDesc(b=b, L=L, D=D, H_q=H_q, d=d, H_I=H_I, d_I=d_I, W=W, dtype=_dtype(X), eps_rms=eps)
+    if I is None:
+        I = torch.empty((b, L), dtype=torch.float32, device=X.device)
+    nb = lib().kvm_index_workspace_size(C.byref(desc))
+    if ws is None:
+        ws = workspace(nb, X.device, stream, "index")
+    check(lib().kvm_index_score(C.byref(desc), _p(X), _p(Qwin), _p(W_kI), _p(gamma_k), _p(W_qI), _p(gamma_q),
+                                _p(W_g), _p(I), _p(khat), _p(ws), ws.numel(), _stream(stream)))
+    return I

@@ -1,0 +1,393 @@
+// A1-A3: the learned MQA-style indexer and its per-key importance [IM 2.A].
+//
+//   k_hat[t]   = RMSNorm(W_kI x_t)                       one shared key per token
+//   q~[s,h]    = sigmoid(W_g[h].x_s) RMSNorm(W_qI[h] q_{s,c(h)}) / sqrt(d_I)
+//   I[t]       = max_{s: pos(s) >= t} sum_h relu(q~[s,h] . k_hat[t])
+// The gate is folded into the query (g > 0, so g relu(x) = relu(g x)).
+//
+// Kernels:
+//  keyproj_mfma  bf16 X, d_I = 64: v_mfma_f32_32x32x16_bf16, one wave per 32 tokens, the
+//                W_kI chunk of each 64-wide k step staged once per block in LDS; X rows
+//                stream from HBM straight into MFMA operand registers (64 contiguous bytes
+//                per lane).  RMSNorm in the epilogue with 32-lane DPP reductions.
+//  query         per (sequence, window query): gate dots and the per-head down-projection
+//                (16 lanes per output row), RMSNorm per head.
+//  score_mfma    H_I = 32, d_I = 64: a 32 x 32 tile is (32 heads of one query) x (32 keys),
+//                so the head sum is an in-lane sum plus one cross-half add.  Operands are
+//                split fp16 hi + lo (lo scaled by 2^11): q.k = hi.hi + 2^-11 (hi.lo' + lo'.hi)
+//                on v_mfma_f32_32x32x16_f16, ~22 bits per operand, so I keeps near-fp32
+//                accuracy.  Each wave keeps its 64 keys' operands in registers and streams
+//                the window queries through LDS; the running max stays in registers.
+//  keyproj_valu / score_valu: fp32 FMA versions for the other shapes.
+#include "common.hpp"
+
+namespace kvm {
+
+struct IndexArgs {
+  const void* X;
+  const void* Qwin;
+  const void* W_kI;
+  const float* gamma_k;
+  const void* W_qI;
+  const float* gamma_q;
+  const void* W_g;
+  float* I;
+  float* khat;   // [b, L, d_I]
+  float* qt;     // [b, W, H_I, d_I]
+  int b, L, D, H_q, d, H_I, d_I, W;
+  float eps;
+};
+
+// ------------------------------------------------------------------ A1: keys, matrix cores
+constexpr int kKpPitch = 36;  // words per LDS row of the W_kI chunk (64 bf16 + 8 pad)
+
+__global__ __launch_bounds__(256) void keyproj_mfma_kernel(IndexArgs a) {
+  // block: 128 tokens (4 waves x 32); d_I = 64 outputs (2 tiles of 32)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bb = blockIdx.y;
+  const int t0 = blockIdx.x * 128 + wave * 32;
+  const int m = lane & 31, kg = lane >> 5;
+  __shared__ uint32_t sW[2][64 * kKpPitch];
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(a.X) + (size_t)bb * a.L * a.D;
+  const uint16_t* Wk = reinterpret_cast<const uint16_t*>(a.W_kI);
+  const int tok = min(t0 + m, a.L - 1);        // clamp: rows past L compute garbage, never stored
+  const uint16_t* xrow = X + (size_t)tok * a.D + kg * 32;
+
+  f32x16_t acc0, acc1;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) { acc0[j] = 0.f; acc1[j] = 0.f; }
+
+  // W chunk loader: 64 rows x 64 bf16 = 512 uint4; 256 threads x 2
+  auto load_w = [&](int k0, uint4 (&w)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + i * 256, row = idx >> 3, q = idx & 7;
+      w[i] = *reinterpret_cast<const uint4*>(Wk + (size_t)row * a.D + k0 + q * 8);
+    }
+  };
+  auto store_w = [&](int buf, const uint4 (&w)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + i * 256, row = idx >> 3, q = idx & 7;
+      *reinterpret_cast<uint4*>(&sW[buf][row * kKpPitch + q * 4]) = w[i];
+    }
+  };
+  uint4 wreg[2];
+  load_w(0, wreg);
+  store_w(0, wreg);
+  uint4 xr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xr[i] = *reinterpret_cast<const uint4*>(xrow + i * 8);
+  __syncthreads();
+  const int nk = a.D / 64;
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    uint4 xn[4];
+    if (ks + 1 < nk) {
+      load_w((ks + 1) * 64, wreg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xn[i] = *reinterpret_cast<const uint4*>(xrow + (ks + 1) * 64 + i * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x8_t A, B0, B1;
+      __builtin_memcpy(&A, &xr[j], 16);
+      const uint4 b0 = *reinterpret_cast<const uint4*>(&sW[buf][m * kKpPitch + kg * 16 + j * 4]);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(&sW[buf][(32 + m) * kKpPitch + kg * 16 + j * 4]);
+      __builtin_memcpy(&B0, &b0, 16);
+      __builtin_memcpy(&B1, &b1, 16);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B1, acc1, 0, 0, 0);
+    }
+    if (ks + 1 < nk) {
+      store_w(buf ^ 1, wreg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[i] = xn[i];
+    }
+    __syncthreads();
+  }
+  // epilogue: lane holds column (output) n = m (tile 0) and 32 + m (tile 1) for 16 rows
+  const float g0 = a.gamma_k[m], g1 = a.gamma_k[32 + m];
+  float* kout = a.khat + (size_t)bb * a.L * 64;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int row = 8 * (j / 4) + 4 * kg + (j % 4);
+    float ss = acc0[j] * acc0[j] + acc1[j] * acc1[j];
+    ss = group_sum<32>(ss);
+    const float r = rsqrtf(ss * (1.f / 64.f) + a.eps);
+    const int t = t0 + row;
+    if (t < a.L) {
+      kout[(size_t)t * 64 + m] = g0 * acc0[j] * r;
+      kout[(size_t)t * 64 + 32 + m] = g1 * acc1[j] * r;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ A1: keys, fp32 FMA
+template <typename T>
+__global__ __launch_bounds__(256) void keyproj_valu_kernel(IndexArgs a) {
+  // block: 16 tokens; thread -> (token, output) pairs
+  const int bb = blockIdx.y, t0 = blockIdx.x * 16;
+  __shared__ float sk[16][64];
+  const T* X = reinterpret_cast<const T*>(a.X) + (size_t)bb * a.L * a.D;
+  const T* Wk = reinterpret_cast<const T*>(a.W_kI);
+  for (int o = threadIdx.x; o < 16 * a.d_I; o += 256) {
+    const int tt = o / a.d_I, n = o % a.d_I, t = t0 + tt;
+    float s = 0.f;
+    if (t < a.L)
+      for (int k = 0; k < a.D; ++k) s = fmaf(load_scalar<T>(X + (size_t)t * a.D + k), load_scalar<T>(Wk + (size_t)n * a.D + k), s);
+    sk[tt][n] = s;
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int tt = wave; tt < 16; tt += 4) {
+    const int t = t0 + tt;
+    const float x = lane < a.d_I ? sk[tt][lane] : 0.f;
+    const float ss = wave_sum(x * x);
+    const float r = rsqrtf(ss / a.d_I + a.eps);
+    if (t < a.L && lane < a.d_I) a.khat[((size_t)bb * a.L + t) * a.d_I + lane] = a.gamma_k[lane] * x * r;
+  }
+}
+
+// ------------------------------------------------------------------ A2: queries and gates
+template <typename T>
+__global__ __launch_bounds__(256) void query_kernel(IndexArgs a) {
+  // block: one (sequence, window query)
+  const int s = blockIdx.x, bb = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  extern __shared__ float smem[];
+  float* sx = smem;                       // [D]
+  float* sq = sx + a.D;                   // [H_q * d]
+  float* sqi = sq + a.H_q * a.d;          // [H_I * d_I]
+  float* sg = sqi + a.H_I * a.d_I;        // [H_I]
+  const int pos = a.L - a.W + s;
+  const T* xs = reinterpret_cast<const T*>(a.X) + ((size_t)bb * a.L + pos) * a.D;
+  const T* qs = reinterpret_cast<const T*>(a.Qwin) + ((size_t)bb * a.W + s) * a.H_q * a.d;
+  for (int i = tid; i < a.D; i += 256) sx[i] = load_scalar<T>(xs + i);
+  for (int i = tid; i < a.H_q * a.d; i += 256) sq[i] = load_scalar<T>(qs + i);
+  __syncthreads();
+  // gates: one wave per head
+  const T* Wg = reinterpret_cast<const T*>(a.W_g);
+  for (int h = wave; h < a.H_I; h += 4) {
+    float acc = 0.f;
+    for (int k = lane; k < a.D; k += 64) acc = fmaf(load_scalar<T>(Wg + (size_t)h * a.D + k), sx[k], acc);
+    acc = wave_sum(acc);
+    if (lane == 0) sg[h] = sigmoid_f(acc);
+  }
+  // down-projection: 16 lanes per output row of W_qI
+  const T* Wq = reinterpret_cast<const T*>(a.W_qI);
+  const int sub = lane & 15, grp = lane >> 4;
+  const int nout = a.H_I * a.d_I;
+  for (int o0 = wave * 4; o0 < nout; o0 += 16) {
+    const int o = o0 + grp;
+    float acc = 0.f;
+    if (o < nout) {
+      const int h = o / a.d_I;
+      const int c = (h * a.H_q) / a.H_I;
+      const T* wr = Wq + (size_t)o * a.d;
+      for (int k = sub; k < a.d; k += 16) acc = fmaf(load_scalar<T>(wr + k), sq[c * a.d + k], acc);
+    }
+    acc = group_sum<16>(acc);
+    if (o < nout && sub == 0) sqi[o] = acc;
+  }
+  __syncthreads();
+  // RMSNorm per head, gate, 1/sqrt(d_I)
+  const float isd = rsqrtf((float)a.d_I);
+  float* out = a.qt + ((size_t)bb * a.W + s) * a.H_I * a.d_I;
+  for (int h = wave; h < a.H_I; h += 4) {
+    const float x = lane < a.d_I ? sqi[h * a.d_I + lane] : 0.f;
+    const float ss = wave_sum(x * x);
+    const float r = rsqrtf(ss / a.d_I + a.eps);
+    if (lane < a.d_I) out[h * a.d_I + lane] = sg[h] * a.gamma_q[lane] * x * r * isd;
+  }
+}
+
+// ------------------------------------------------------------------ A3: scores, matrix cores
+constexpr int kQPitch = 36;   // words per LDS row: 64 fp16 + 8 pad
+
+__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)x;
+  lo = (_Float16)((x - (float)hi) * 2048.f);
+}
+
+__global__ __launch_bounds__(512) void score_mfma_kernel(IndexArgs a) {
+  // block: 512 keys (8 waves x 2 tiles x 32); H_I = 32, d_I = 64
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int bb = blockIdx.y;
+  const int kbase = blockIdx.x * 512 + wave * 64;
+  const int m = lane & 31, kg = lane >> 5;
+  __shared__ uint32_t sQ[2][2][32 * kQPitch];   // [buf][hi/lo][head row]
+
+  // B operands (keys): tile nt, k-step ks: lane holds k_hat[key][ks*16 + kg*8 .. +8]
+  f16x8_t bh[2][4], bl[2][4];
+  const float* kh = a.khat + (size_t)bb * a.L * 64;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int key = min(kbase + nt * 32 + m, a.L - 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const float4 v0 = *reinterpret_cast<const float4*>(kh + (size_t)key * 64 + ks * 16 + kg * 8);
+      const float4 v1 = *reinterpret_cast<const float4*>(kh + (size_t)key * 64 + ks * 16 + kg * 8 + 4);
+      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        _Float16 h, l;
+        split_f16(v[e], h, l);
+        bh[nt][ks][e] = h;
+        bl[nt][ks][e] = l;
+      }
+    }
+  }
+  // query staging: 32 heads x 64 dims fp32 = 2048 floats; 512 threads x 4
+  const float* qbase = a.qt + (size_t)bb * a.W * 2048;
+  auto fetch = [&](int s) { return *reinterpret_cast<const float4*>(qbase + (size_t)s * 2048 + tid * 4); };
+  auto stage = [&](float4 v, int buf) {
+    const int row = (tid * 4) >> 6, col = (tid * 4) & 63;
+    _Float16 h[4], l[4];
+    split_f16(v.x, h[0], l[0]); split_f16(v.y, h[1], l[1]);
+    split_f16(v.z, h[2], l[2]); split_f16(v.w, h[3], l[3]);
+    uint2 hw, lw;
+    __builtin_memcpy(&hw, h, 8);
+    __builtin_memcpy(&lw, l, 8);
+    *reinterpret_cast<uint2*>(&sQ[buf][0][row * kQPitch + col / 2]) = hw;
+    *reinterpret_cast<uint2*>(&sQ[buf][1][row * kQPitch + col / 2]) = lw;
+  };
+  float best0 = -INFINITY, best1 = -INFINITY;
+  stage(fetch(0), 0);
+  __syncthreads();
+  for (int s = 0; s < a.W; ++s) {
+    const int buf = s & 1;
+    float4 nxt = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (s + 1 < a.W) nxt = fetch(s + 1);
+    f32x16_t c0 = {}, c1 = {}, x0 = {}, x1 = {};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 ah = *reinterpret_cast<const uint4*>(&sQ[buf][0][m * kQPitch + ks * 8 + kg * 4]);
+      const uint4 al = *reinterpret_cast<const uint4*>(&sQ[buf][1][m * kQPitch + ks * 8 + kg * 4]);
+      f16x8_t Ah, Al;
+      __builtin_memcpy(&Ah, &ah, 16);
+      __builtin_memcpy(&Al, &al, 16);
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, bh[0][ks], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, bh[1][ks], c1, 0, 0, 0);
+      x0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, bl[0][ks], x0, 0, 0, 0);
+      x1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, bl[1][ks], x1, 0, 0, 0);
+      x0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al, bh[0][ks], x0, 0, 0, 0);
+      x1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al, bh[1][ks], x1, 0, 0, 0);
+    }
+    // rows = heads, column = key; relu, head sum, causal mask, running max
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      s0 += fmaxf(fmaf(x0[j], 1.f / 2048.f, c0[j]), 0.f);
+      s1 += fmaxf(fmaf(x1[j], 1.f / 2048.f, c1[j]), 0.f);
+    }
+    s0 += shfl_xor32(s0);
+    s1 += shfl_xor32(s1);
+    const int pos = a.L - a.W + s;
+    if (kbase + m <= pos) best0 = fmaxf(best0, s0);
+    if (kbase + 32 + m <= pos) best1 = fmaxf(best1, s1);
+    if (s + 1 < a.W) stage(nxt, buf ^ 1);
+    __syncthreads();
+  }
+  float* Ir = a.I + (size_t)bb * a.L;
+  if (kg == 0) {
+    if (kbase + m < a.L) Ir[kbase + m] = best0;
+    if (kbase + 32 + m < a.L) Ir[kbase + 32 + m] = best1;
+  }
+}
+
+// ------------------------------------------------------------------ A3: scores, fp32 FMA
+__global__ __launch_bounds__(256) void score_valu_kernel(IndexArgs a) {
+  // block: 256 keys, one per thread; queries staged per window position in LDS
+  const int bb = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;
+  extern __shared__ float sq[];   // [H_I * d_I]
+  float k[64];
+  const int tt = min(t, a.L - 1);
+#pragma unroll
+  for (int i = 0; i < 64; ++i) k[i] = i < a.d_I ? a.khat[((size_t)bb * a.L + tt) * a.d_I + i] : 0.f;
+  float best = -INFINITY;
+  const int nq = a.H_I * a.d_I;
+  for (int s = 0; s < a.W; ++s) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < nq; i += 256) sq[i] = a.qt[((size_t)bb * a.W + s) * nq + i];
+    __syncthreads();
+    float A = 0.f;
+    for (int h = 0; h < a.H_I; ++h) {
+      float x = 0.f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i)
+        if (i < a.d_I) x = fmaf(sq[h * a.d_I + i], k[i], x);
+      A += fmaxf(x, 0.f);
+    }
+    if (t <= a.L - a.W + s) best = fmaxf(best, A);
+  }
+  if (t < a.L) a.I[(size_t)bb * a.L + t] = best;
+}
+
+struct IndexWs { size_t kh, qt, total; };
+static IndexWs index_ws(const kvm_index_desc* d) {
+  IndexWs w;
+  w.kh = kCounterBytes;
+  w.qt = align_up(w.kh + (size_t)d->b * d->L * d->d_I * sizeof(float), 256);
+  w.total = align_up(w.qt + (size_t)d->b * d->W * d->H_I * d->d_I * sizeof(float), 256);
+  return w;
+}
+
+}  // namespace kvm
+
+using namespace kvm;
+
+extern "C" size_t kvm_index_workspace_size(const kvm_index_desc* d) {
+  if (!d || d->b <= 0 || d->L <= 0 || d->d_I <= 0 || d->W <= 0 || d->H_I <= 0) return 0;
+  return index_ws(d).total;
+}
+
+extern "C" kvm_status kvm_index_score(const kvm_index_desc* d, const void* X, const void* Qwin, const void* W_kI,
+                                      const float* gamma_k, const void* W_qI, const float* gamma_q, const void* W_g,
+                                      float* I, float* khat, void* ws, size_t ws_bytes, void* stream) {
+  KVM_PTR(d);
+  KVM_REQUIRE(d->b > 0 && d->L > 0 && d->D > 0 && d->H_q > 0 && d->H_I > 0, KVM_ERR_SHAPE,
+              "b, L, D, H_q, H_I must be positive");
+  KVM_REQUIRE(d->d_I == 32 || d->d_I == 64, KVM_ERR_SHAPE, "d_I %d not in {32, 64}", d->d_I);
+  KVM_REQUIRE(d->d == 64 || d->d == 128, KVM_ERR_SHAPE, "head dim %d not in {64, 128}", d->d);
+  KVM_REQUIRE(d->D % 8 == 0, KVM_ERR_SHAPE, "D %% 8 != 0");
+  KVM_REQUIRE(d->W >= 1 && d->W <= d->L, KVM_ERR_RANGE, "window %d outside [1, L]", d->W);
+  KVM_REQUIRE(d->dtype == KVM_F32 || d->dtype == KVM_BF16, KVM_ERR_DTYPE, "dtype %d", d->dtype);
+  KVM_PTR_ALIGNED(X); KVM_PTR_ALIGNED(Qwin); KVM_PTR_ALIGNED(W_kI); KVM_PTR_ALIGNED(gamma_k);
+  KVM_PTR_ALIGNED(W_qI); KVM_PTR_ALIGNED(gamma_q); KVM_PTR_ALIGNED(W_g); KVM_PTR_ALIGNED(I);
+  KVM_OPT_ALIGNED(khat);
+  const IndexWs w = index_ws(d);
+  KVM_REQUIRE(ws != nullptr && ws_bytes >= w.total, KVM_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+  KVM_ALIGNED(ws);
+  const size_t qsmem = (size_t)(d->D + d->H_q * d->d + d->H_I * d->d_I + d->H_I) * sizeof(float);
+  KVM_REQUIRE(qsmem <= 64 * 1024, KVM_ERR_SHAPE, "D + H_q*d too large for the query kernel");
+  kvm_status st = require_gfx950();
+  if (st != KVM_OK) return st;
+
+  IndexArgs a{};
+  a.X = X; a.Qwin = Qwin; a.W_kI = W_kI; a.gamma_k = gamma_k; a.W_qI = W_qI; a.gamma_q = gamma_q; a.W_g = W_g;
+  a.I = I;
+  char* base = static_cast<char*>(ws);
+  a.khat = khat ? khat : reinterpret_cast<float*>(base + w.kh);
+  a.qt = reinterpret_cast<float*>(base + w.qt);
+  a.b = d->b; a.L = d->L; a.D = d->D; a.H_q = d->H_q; a.d = d->d; a.H_I = d->H_I; a.d_I = d->d_I; a.W = d->W;
+  a.eps = d->eps_rms;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = d->dtype == KVM_BF16;
+  if (bf && d->d_I == 64 && d->D % 64 == 0)
+    hipLaunchKernelGGL(keyproj_mfma_kernel, dim3((d->L + 127) / 128, d->b), dim3(256), 0, s, a);
+  else if (bf)
+    hipLaunchKernelGGL(keyproj_valu_kernel<uint16_t>, dim3((d->L + 15) / 16, d->b), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(keyproj_valu_kernel<float>, dim3((d->L + 15) / 16, d->b), dim3(256), 0, s, a);
+  if (bf)
+    hipLaunchKernelGGL(query_kernel<uint16_t>, dim3(d->W, d->b), dim3(256), qsmem, s, a);
+  else
+    hipLaunchKernelGGL(query_kernel<float>, dim3(d->W, d->b), dim3(256), qsmem, s, a);
+  if (d->H_I == 32 && d->d_I == 64)
+    hipLaunchKernelGGL(score_mfma_kernel, dim3((d->L + 511) / 512, d->b), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(score_valu_kernel, dim3((d->L + 255) / 256, d->b), dim3(256),
+                       (size_t)d->H_I * d->d_I * sizeof(float), s, a);
+  return check_hip(hipGetLastError(), "index kernels launch");
+}

@@ -54,3 +54,29 @@ def assert_output(got, ref, dtype, what=""):
         e = normwise(got, ref)
         assert e <= 2e-2, f"{what}: normwise error {e:.3e} > 2e-2"
     return e
+
+
+def set_check(gpu_kept, I_ref, B, R, inclusive=True, rel=1e-5):
+    """Index-set rule: the GPU's kept set must equal the oracle's outside the band of
+    scores within `rel` of the oracle's n_top-th selected score, and have the same size.
+    The oracle takes the decision on its scores rounded to fp32 (the kernel's precision).
+    Returns the number of positions inside the band where the two sets differ."""
+    from oracle import indexmem as im
+    I32 = np.asarray(I_ref, np.float64).astype(np.float32).astype(np.float64)
+    L = len(I32)
+    ref_idx, _ = im.topk_select(I32, B, R, inclusive)
+    g = set(int(x) for x in np.asarray(gpu_kept).tolist())
+    r = set(ref_idx.tolist())
+    assert len(g) == len(r), f"kept {len(g)} != {len(r)}"
+    n_cand = L - min(R, L)
+    n_top = B - R if inclusive else B
+    if n_top >= n_cand or n_top <= 0:
+        assert g == r
+        return 0
+    cand_sel = [t for t in ref_idx.tolist() if t < n_cand]
+    tau = min(I32[t] for t in cand_sel)
+    band = np.abs(I32 - tau) <= rel * abs(tau)
+    diff = g ^ r
+    bad = [t for t in diff if not band[t]]
+    assert not bad, f"set mismatch outside the 1e-5 band at {bad[:10]} (tau={tau})"
+    return len(diff)

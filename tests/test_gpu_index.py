@@ -1,0 +1,91 @@
+"""kvm_index_score (indexer keys, queries, gated ReLU scores, max-pool) against the oracle,
+then the selected set and the whole prefill (score -> select -> compact + memory)."""
+import numpy as np
+import pytest
+
+from oracle import indexmem as im
+from synth import CONFIGS, gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_index(cfg, p, i):
+    f = lambda x: gen.from_storage(x, cfg.dtype)
+    X = f(p["X"][i])
+    kh = im.indexer_keys(X, f(p["W_kI"]), p["gamma_k"], cfg.eps_rms)
+    qh, g = im.indexer_queries(f(p["Qwin"][i]), X[cfg.L - cfg.W:], f(p["W_qI"]), p["gamma_q"], f(p["W_g"]), cfg.eps_rms)
+    I = im.importance(im.score_matrix(qh, g, kh, np.arange(cfg.L - cfg.W, cfg.L)))
+    return kh, I
+
+
+def _run(cfg, p):
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np
+    kh = torch.empty((cfg.b, cfg.L, cfg.d_I), dtype=torch.float32, device="cuda")
+    I = api.kvm_index_score(to_dev(p["X"]), to_dev(p["Qwin"]), to_dev(p["W_kI"]), to_dev(p["gamma_k"]),
+                            to_dev(p["W_qI"]), to_dev(p["gamma_q"]), to_dev(p["W_g"]), khat=kh, eps=cfg.eps_rms)
+    torch.cuda.synchronize()
+    return to_np(I), to_np(kh)
+
+
+CASES = [
+    CONFIGS[1],
+    CONFIGS[1].with_(L=300, W=7, B=40),
+    CONFIGS[2],
+    CONFIGS[2].with_(b=2, L=1000, B=100, R=8, needles=4),
+    CONFIGS[2].with_(L=777, W=1, B=77, R=0, needles=0),
+    CONFIGS[2].with_(L=64, W=64, B=16, R=4, needles=0),
+]
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: f"{c.name}-L{c.L}-W{c.W}-b{c.b}")
+def test_index_scores_and_set(cfg):
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import assert_output, set_check, to_dev, to_np
+    p = gen.make_prefill(cfg)
+    gI, gkh = _run(cfg, p)
+    for i in range(cfg.b):
+        kh, I = _oracle_index(cfg, p, i)
+        assert_output(gkh[i], kh, cfg.dtype, "k_hat")
+        assert_output(gI[i], I, cfg.dtype, "I")
+        # near-fp32 scores: far inside the 1e-5 band the index set is judged with
+        assert np.max(np.abs(gI[i] - I) / np.maximum(np.abs(I), 1e-3)) < 2e-6
+        np.testing.assert_allclose(gkh[i], kh, rtol=2e-5, atol=2e-6)
+        idx, _ = api.kvm_topk_select(to_dev(gI[i][None]), cfg.B, cfg.R, cfg.recent_inclusive)
+        n_diff = set_check(to_np(idx)[0], I, cfg.B, cfg.R, cfg.recent_inclusive)
+        assert n_diff == 0 or n_diff <= 2
+
+
+@pytest.mark.parametrize("cfg", [CONFIGS[1], CONFIGS[2], CONFIGS[2].with_(b=2, L=2500, B=250, R=16, needles=4)],
+                         ids=lambda c: f"{c.name}-L{c.L}")
+def test_prefill_end_to_end(cfg):
+    """score -> select -> compact + memory on the GPU vs the oracle's prefill."""
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import assert_output, set_check, to_dev, to_np, normwise
+    lam = float(np.float32(cfg.lam))
+    p = gen.make_prefill(cfg)
+    X, Q, Kt, Vt = (to_dev(p[k]) for k in ("X", "Qwin", "K", "V"))
+    I = api.kvm_index_score(X, Q, to_dev(p["W_kI"]), to_dev(p["gamma_k"]), to_dev(p["W_qI"]), to_dev(p["gamma_q"]),
+                            to_dev(p["W_g"]), eps=cfg.eps_rms)
+    idx, sm = api.kvm_topk_select(I, cfg.B, cfg.R, cfg.recent_inclusive)
+    keep = idx.shape[1]
+    M = torch.zeros((cfg.b, cfg.H_kv, cfg.d, cfg.d), dtype=torch.float32, device="cuda")
+    bv = torch.zeros((cfg.b, cfg.H_kv, cfg.d), dtype=torch.float32, device="cuda")
+    Kc, Vc = api.kvm_compact_kv(Kt, Vt, sm, keep, keep + cfg.T, M=M, bvec=bv, lam=lam)
+    torch.cuda.synchronize()
+    f = lambda x: gen.from_storage(x, cfg.dtype)
+    for i in range(cfg.b):
+        pre = im.prefill(f(p["X"][i]), f(p["Qwin"][i]), f(p["K"][i]), f(p["V"][i]), f(p["W_kI"]), p["gamma_k"],
+                         f(p["W_qI"]), p["gamma_q"], f(p["W_g"]), cfg.B, cfg.R, lam, cfg.recent_inclusive,
+                         eps=cfg.eps_rms, cap=keep + cfg.T)
+        n_diff = set_check(to_np(idx)[i], pre["I"], cfg.B, cfg.R, cfg.recent_inclusive)
+        if n_diff:
+            continue   # a valid different choice inside the band: downstream legitimately differs
+        assert to_np(idx)[i].tolist() == pre["idx"].tolist()
+        rK, rV = im.compact(p["K"][i], p["V"][i], pre["slot_map"], keep + cfg.T)
+        assert to_np(Kc)[i].tobytes() == rK.tobytes()
+        assert to_np(Vc)[i].tobytes() == rV.tobytes()
+        assert_output(to_np(M)[i], pre["M"], cfg.dtype, "M")
+        assert_output(to_np(bv)[i], pre["b"], cfg.dtype, "b")
