@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the IndexMem hot path on one MI355X.
+
+Workload: 32 Llama-3.1-8B-shaped layers (32 query / 8 KV heads, head dim 128, hidden
+4096), batch 8, 16384-token prefill evicted to B = 1638 (recent window 32 inside the
+budget), indexer 32 heads x d_I 64 with a 64-query window, memory decay 0.995, then 512
+decode steps.  One step = prefill index+evict of all 32 layers (indexer scores, top-k,
+compaction + memory build) followed by the 512 decode steps x 32 layers (split-K
+attention + memory read-out).  Inputs are seeded N(0,1) bf16 drawn on the device,
+resident in HBM before timing.
+
+Prints one JSON line: decode tokens/s (value), prefill index+evict ms, the decode
+kernel's roofline against 8 TB/s HBM, and the fp64 oracle timed on a bounded sample on
+the host (cpu_baseline).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode tok/s & %HBM peak (evicted cache+memory); index+evict ms @16K prefill"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--decode-steps", type=int, default=512)
+    ap.add_argument("--graph-chunk", type=int, default=32, help="decode steps per captured HIP graph")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--n-split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-decode-steps", type=int, default=32)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_inputs(cfg, layers, T, torch, dev):
+    """Seeded N(0,1) bf16 tensors of the workload's shapes, drawn on the device."""
+    b, L, D, Hq, Hkv, d, HI, dI, W = cfg.b, cfg.L, cfg.D, cfg.H_q, cfg.H_kv, cfg.d, cfg.H_I, cfg.d_I, cfg.W
+    bf = torch.bfloat16
+    layers_in = []
+    for l in range(layers):
+        g = torch.Generator(device=dev)
+        g.manual_seed(3_000_000 + l)
+        rn = lambda *s, std=1.0: (torch.randn(*s, generator=g, device=dev, dtype=torch.float32) * std).to(bf)
+        X = torch.empty((b, L, D), dtype=bf, device=dev)
+        for i in range(b):
+            X[i] = rn(L, D)
+        li = dict(
+            X=X, Q=rn(b, W, Hq, d), K=rn(b, L, Hkv, d), V=rn(b, L, Hkv, d),
+            W_kI=rn(dI, D, std=D ** -0.5), W_qI=rn(HI, dI, d, std=d ** -0.5), W_g=rn(HI, D, std=D ** -0.5),
+            w_g=rn(Hq, d, std=d ** -0.5),
+            gk=torch.ones(dI, device=dev), gq=torch.ones(dI, device=dev),
+            q=rn(T, b, Hq, d), kn=rn(T, b, Hkv, d), vn=rn(T, b, Hkv, d),
+        )
+        layers_in.append(li)
+        if (l + 1) % 8 == 0:
+            log(f"inputs: {l + 1}/{layers} layers drawn")
+    return layers_in
+
+
+def decode_bytes(cfg, n_attended, elem=2):
+    """Algorithmic HBM bytes of one decode launch (one layer, whole batch): K and V of the
+    attended slots, M and b of every (sequence, KV head), q, the new K/V row and o."""
+    pairs = cfg.b * cfg.H_kv
+    kv = pairs * n_attended * cfg.d * 2 * elem
+    mem = pairs * (cfg.d * cfg.d + cfg.d) * 4
+    qo = cfg.b * cfg.H_q * cfg.d * (elem + 4) + cfg.H_q * cfg.d * elem
+    new = pairs * cfg.d * 2 * elem * 2          # read k_new/v_new, write them into the cache
+    return kv + mem + qo + new
+
+
+def prefill_bytes(cfg, keep, elem=2):
+    """Algorithmic HBM bytes of index+evict for one layer: read X (key projection), read
+    K and V once, write the kept rows, read/write the fp32 normalised keys between the
+    projection and the score pass is implementation traffic and not counted."""
+    tok = cfg.b * cfg.L
+    return tok * cfg.D * elem + tok * cfg.H_kv * cfg.d * 2 * elem + cfg.b * keep * cfg.H_kv * cfg.d * 2 * elem
+
+
+def cpu_baseline(cfg, decode_steps):
+    """The fp64 oracle on one (layer, sequence) of the workload: prefill index+evict and
+    `decode_steps` decode steps, scaled to the workload's units."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import indexmem as im
+    from synth import gen
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    one = cfg.with_(b=1, needles=0)
+    p = gen.make_prefill(one, layer=0)
+    f = lambda x: gen.from_storage(x, one.dtype)
+    X, Q, K, V = f(p["X"][0]), f(p["Qwin"][0]), f(p["K"][0]), f(p["V"][0])
+    Wk, Wq, Wg, wg = f(p["W_kI"]), f(p["W_qI"]), f(p["W_g"]), f(p["w_g"])
+    t0 = time.perf_counter()
+    pre = im.prefill(X, Q, K, V, Wk, p["gamma_k"], Wq, p["gamma_q"], Wg, cfg.B, cfg.R, cfg.lam,
+                     cap=cfg.keep + decode_steps)
+    t_pre = time.perf_counter() - t0
+    dec = gen.make_decode(one, layer=0, steps=decode_steps)
+    t0 = time.perf_counter()
+    im.decode(f(dec["q"][:, 0]), f(dec["k_new"][:, 0]), f(dec["v_new"][:, 0]), pre["Kc"], pre["Vc"], cfg.keep,
+              pre["M"], pre["b"], wg)
+    t_dec = (time.perf_counter() - t0) / decode_steps
+    index_evict_ms = t_pre * cfg.layers * cfg.b * 1e3
+    tok_s = 1.0 / (t_dec * cfg.layers)
+    return dict(value=round(tok_s, 3), unit="tok/s", cores=threads, kind="oracle",
+                sample=f"1 layer x 1 sequence of the workload: prefill index+evict ({t_pre:.2f} s) and "
+                       f"{decode_steps} decode steps ({t_dec * 1e3:.2f} ms each); decode tok/s = "
+                       f"1/(32 layers x step time), sequences run one after another",
+                index_evict_ms=round(index_evict_ms, 1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path shards "
+              "by sequence with no communication; see the design notes)", file=sys.stderr)
+        return 2
+    import torch
+    from synth import CONFIGS
+    from learned_kv_cache_mqa_amd import api
+    from learned_kv_cache_mqa_amd import _lib as KL
+
+    cfg = CONFIGS[3].with_(layers=args.layers, T=args.decode_steps)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    T, layers = cfg.T, cfg.layers
+    keep = api.kvm_topk_keep(cfg.L, cfg.B, cfg.R, True)
+    cap = keep + T
+    lam = float(cfg.lam)
+    log(f"workload: {layers} layers, b={cfg.b}, L={cfg.L}, keep={keep}, cap={cap}, T={T}")
+    L_in = make_inputs(cfg, layers, T, torch, dev)
+
+    bf = torch.bfloat16
+    Kc = [torch.zeros((cfg.b, cfg.H_kv, cap, cfg.d), dtype=bf, device=dev) for _ in range(layers)]
+    Vc = [torch.zeros((cfg.b, cfg.H_kv, cap, cfg.d), dtype=bf, device=dev) for _ in range(layers)]
+    Ms = [torch.zeros((cfg.b, cfg.H_kv, cfg.d, cfg.d), dtype=torch.float32, device=dev) for _ in range(layers)]
+    bs = [torch.zeros((cfg.b, cfg.H_kv, cfg.d), dtype=torch.float32, device=dev) for _ in range(layers)]
+    I = torch.empty((cfg.b, cfg.L), dtype=torch.float32, device=dev)
+    idx = torch.empty((cfg.b, keep), dtype=torch.int32, device=dev)
+    sm = torch.empty((cfg.b, cfg.L), dtype=torch.int32, device=dev)
+    o = torch.empty((layers, cfg.b, cfg.H_q, cfg.d), dtype=torch.float32, device=dev)
+    lens = torch.full((cfg.b,), keep, dtype=torch.int32, device=dev)
+
+    import ctypes as C
+    L0 = L_in[0]
+    idesc = KL.IndexDesc(b=cfg.b, L=cfg.L, D=cfg.D, H_q=cfg.H_q, d=cfg.d, H_I=cfg.H_I, d_I=cfg.d_I, W=cfg.W,
+                         dtype=KL.KVM_BF16, eps_rms=cfg.eps_rms)
+    cdesc = KL.CompactDesc(b=cfg.b, L=cfg.L, H_kv=cfg.H_kv, d=cfg.d, cap=cap, keep=keep, dtype=KL.KVM_BF16,
+                           per_head=0, kv_head_major=0, flags=KL.KVM_FUSE_MEM, lam=lam)
+    ddesc = api.decode_desc(L0["q"][0], Kc[0], KL.KVM_READ_MEMORY, args.n_split)
+    ws_i = torch.zeros(KL.lib().kvm_index_workspace_size(C.byref(idesc)), dtype=torch.uint8, device=dev)
+    ws_c = torch.zeros(KL.lib().kvm_compact_workspace_size(C.byref(cdesc)), dtype=torch.uint8, device=dev)
+    ws_d = torch.zeros(KL.lib().kvm_decode_workspace_size(C.byref(ddesc)), dtype=torch.uint8, device=dev)
+
+    def prefill():
+        for l in range(layers):
+            li = L_in[l]
+            api.kvm_index_score(li["X"], li["Q"], li["W_kI"], li["gk"], li["W_qI"], li["gq"], li["W_g"], I=I,
+                                eps=cfg.eps_rms, ws=ws_i)
+            api.kvm_topk_select(I, cfg.B, cfg.R, True, idx=idx, slot_map=sm)
+            api.kvm_compact_kv(li["K"], li["V"], sm, keep, cap, Kc=Kc[l], Vc=Vc[l], M=Ms[l], bvec=bs[l], lam=lam,
+                               ws=ws_c)
+
+    def decode_steps(t0, t1):
+        for t in range(t0, t1):
+            for l in range(layers):
+                li = L_in[l]
+                api.kvm_decode_attn_mem(li["q"][t], Kc[l], Vc[l], lens, k_new=li["kn"][t], v_new=li["vn"][t],
+                                        M=Ms[l], bvec=bs[l], w_g=li["w_g"], o=o[l], n_split=args.n_split, ws=ws_d)
+            api.kvm_len_add(lens, 1)
+
+    graphs = []
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    if not args.no_graph:
+        # capture the decode loop in chunks; the kernels never allocate or memset
+        with torch.cuda.stream(stream):
+            prefill()      # fill caches once so capture-time launches see valid data
+            for c0 in range(0, T, args.graph_chunk):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    decode_steps(c0, min(T, c0 + args.graph_chunk))
+                graphs.append(g)
+        torch.cuda.synchronize()
+        lens.fill_(keep)
+        torch.cuda.synchronize()
+        log(f"captured {len(graphs)} decode graphs of {args.graph_chunk} steps x {layers} layers")
+
+    def step(ev):
+        with torch.cuda.stream(stream):
+            ev[0].record(stream)
+            prefill()
+            ev[1].record(stream)
+            if graphs:
+                for g in graphs:
+                    g.replay()
+            else:
+                decode_steps(0, T)
+            api.kvm_len_add(lens, -T)
+            ev[2].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for w in range(args.warmup):
+        step(mk())
+        torch.cuda.synchronize()
+        log(f"warmup step {w + 1}/{args.warmup} done")
+    evs = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    log(f"timed {args.steps} steps: prefill {sum(pre_ms) / len(pre_ms):.3f} ms, decode {sum(dec_ms) / len(dec_ms):.3f} ms")
+
+    dec_mean = sum(dec_ms) / len(dec_ms)
+    pre_mean = sum(pre_ms) / len(pre_ms)
+    tok_s = cfg.b * T / (dec_mean / 1e3)
+    launch_us = dec_mean * 1e3 / (T * layers)
+    avg_bytes = sum(decode_bytes(cfg, keep + t + 1) for t in range(T)) / T
+    achieved = avg_bytes / (launch_us * 1e-6) / 1e9
+    pbytes = prefill_bytes(cfg, keep) * layers
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode_kernel<bf16,128,4,4> (one layer-step: split-K attention + memory read-out)",
+                "bytes_per_launch": round(avg_bytes), "launch_us": round(launch_us, 3)}
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"Llama-3.1-8B-shaped {layers}-layer stack, batch {cfg.b}, {cfg.L}-token prefill "
+                               f"evicted to {cfg.B} (recent {cfg.R} inside), {T} decode steps",
+                   "layers": layers, "batch": cfg.b, "prefill_len": cfg.L, "budget": cfg.B, "recent": cfg.R,
+                   "decode_steps": T, "indexer": f"{cfg.H_I}x{cfg.d_I}, window {cfg.W}", "lam": cfg.lam,
+                   "hip_graphs": not args.no_graph},
+        "index_evict_ms": round(pre_mean, 3),
+        "index_evict_hbm_frac": round(pbytes / (pre_mean / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_ms_per_step": round(dec_mean / T, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on one layer x one sequence ...")
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_decode_steps)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
