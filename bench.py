@@ -134,14 +134,14 @@ def main():
     torch.cuda.set_device(dev)
     T, layers = cfg.T, cfg.layers
     keep = api.kvm_topk_keep(cfg.L, cfg.B, cfg.R, True)
-    cap = keep + T
+    cap = api.cache_cap(keep + T)
     lam = float(cfg.lam)
     log(f"workload: {layers} layers, b={cfg.b}, L={cfg.L}, keep={keep}, cap={cap}, T={T}")
     L_in = make_inputs(cfg, layers, T, torch, dev)
 
     bf = torch.bfloat16
     Kc = [torch.zeros((cfg.b, cfg.H_kv, cap, cfg.d), dtype=bf, device=dev) for _ in range(layers)]
-    Vc = [torch.zeros((cfg.b, cfg.H_kv, cap, cfg.d), dtype=bf, device=dev) for _ in range(layers)]
+    Vc = [torch.zeros((cfg.b, cfg.H_kv, cfg.d, cap), dtype=bf, device=dev) for _ in range(layers)]
     Ms = [torch.zeros((cfg.b, cfg.H_kv, cfg.d, cfg.d), dtype=torch.float32, device=dev) for _ in range(layers)]
     bs = [torch.zeros((cfg.b, cfg.H_kv, cfg.d), dtype=torch.float32, device=dev) for _ in range(layers)]
     I = torch.empty((cfg.b, cfg.L), dtype=torch.float32, device=dev)

@@ -125,8 +125,9 @@ kvm_status kvm_topk_select(const kvm_topk_desc* desc, const float* I, int32_t* i
 /* ------------------------------------------------------------------------------------ *
  * A5 + A6 / V2  Compaction with a fused latent-memory or moment build  [IM 2.A, 2.B; MKV 1]
  *
- * One pass over K, V: kept rows go to the head-major cache Kc, Vc [b, H_kv, cap, d] at
- * their slot; evicted rows are folded in:
+ * One pass over K, V: kept rows go to the caches at their slot -- Kc [b, H_kv, cap, d]
+ * (slot-major) and Vc [b, H_kv, d, cap] (dim-major: element (slot, i) at Vc[.., i, slot]);
+ * evicted rows are folded in:
  *   KVM_FUSE_MEM:     n = number evicted; with eviction ranks i = 1..n (ascending position)
  *                     M <- lam^n M + sum_i lam^(n-i) v_i phi(k_i)^T,
  *                     bvec <- lam^n bvec + sum_i lam^(n-i) phi(k_i),   phi = elu + 1.
@@ -172,7 +173,8 @@ kvm_status kvm_gather_rows(int32_t rows, int32_t L, int32_t cap, int32_t elem_by
  * For rows i = 1..r in the given order (per sequence and KV head):
  *   M <- lam^r M + sum_i lam^(r-i) v_i phi(k_i)^T,  bvec <- lam^r bvec + sum_i lam^(r-i) phi(k_i).
  * K_rows, V_rows: [b, r, H_kv, d] (dtype), or, with row_slot != NULL, r = 1 and the row
- * is taken from the caches Kc, Vc [b, H_kv, cap, d] at slot row_slot[b] (device i32).
+ * is taken from the caches Kc [b, H_kv, cap, d] and Vc [b, H_kv, d, cap] at slot
+ * row_slot[b] (device i32).
  * ------------------------------------------------------------------------------------ */
 typedef struct {
   int32_t b, H_kv, d, r, cap;
@@ -196,7 +198,8 @@ kvm_status kvm_mem_update(const kvm_mem_desc* desc, const void* K_rows, const vo
  *   mode KVM_READ_MOMENTS: f_E = s_v/n_e + (S - s_v s_k^T/n_e) q / (n_e sqrt d),
  *                          log Z_E = log n_e + (q.s_k/n_e)/sqrt d,
  *                          w = sigmoid(lse - log Z_E), o = w a + (1 - w) f_E (o = a if n_e = 0)
- * q [b,H_q,d], k_new/v_new [b,H_kv,d] (dtype, nullable), Kc, Vc [b,H_kv,cap,d] (dtype),
+ * q [b,H_q,d], k_new/v_new [b,H_kv,d] (dtype, nullable), Kc [b,H_kv,cap,d] slot-major and
+ * Vc [b,H_kv,d,cap] dim-major (dtype; as written by kvm_compact_kv), cap % 8 == 0,
  * len [b] i32 (not modified), append_slot [b] i32 (nullable), o [b,H_q,d] f32,
  * lse [b,H_q] f32 (nullable: log-partition of the retained attention, scale applied).
  * The library never reads or writes a slot >= cap (n is clamped to cap).

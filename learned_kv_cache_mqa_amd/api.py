@@ -62,7 +62,7 @@ def decode_desc(q, Kc, mode, n_split=0, scale=None, eps=1e-6):
 def kvm_decode_attn_mem(q, Kc, Vc, len_, k_new=None, v_new=None, append_slot=None, M=None, bvec=None,
                         w_g=None, moments=None, o=None, lse=None, n_split=0, scale=None, eps=1e-6,
                         stream=None, ws=None):
-    """Decode attention over Kc/Vc [b,H_kv,cap,d] (appending k_new/v_new), merged split-K
+    """Decode attention over Kc [b,H_kv,cap,d] / Vc [b,H_kv,d,cap] (appending k_new/v_new), merged split-K
     states, plus the memory read-out (M, bvec, w_g) or the MomentKV mix (moments =
     dict(n_e, s_k, s_v, S)).  Returns o [b,H_q,d] f32 (and lse [b,H_q] if given)."""
     _contig(q, Kc, Vc, len_, k_new, v_new, append_slot, M, bvec, w_g)
@@ -111,11 +111,16 @@ def kvm_topk_select(I, B, R=0, recent_inclusive=True, idx=None, slot_map=None, s
 
 # ------------------------------------------------------------------------------- compaction
 
+def cache_cap(n):
+    """Smallest cache capacity >= n accepted by the decode kernel (a multiple of 8)."""
+    return (int(n) + 7) // 8 * 8
+
+
 def kvm_compact_kv(Kt, Vt, slot_map, keep, cap=None, Kc=None, Vc=None, M=None, bvec=None, moments=None,
                    lam=1.0, per_head=False, kv_head_major=False, copy=True, stream=None, ws=None):
     """Compact kept rows of K, V ([b,L,H_kv,d], or [b,H_kv,L,d] if kv_head_major) into
-    Kc, Vc [b,H_kv,cap,d]; fold evicted rows into (M, bvec) or into moments
-    dict(n_e, s_k, s_v, S).  Returns (Kc, Vc)."""
+    Kc [b,H_kv,cap,d] (slot-major) and Vc [b,H_kv,d,cap] (dim-major); fold evicted rows into
+    (M, bvec) or into moments dict(n_e, s_k, s_v, S).  Returns (Kc, Vc)."""
     _contig(Kt, Vt, slot_map, Kc, Vc, M, bvec)
     if kv_head_major:
         b, H_kv, L, d = Kt.shape
@@ -124,7 +129,7 @@ def kvm_compact_kv(Kt, Vt, slot_map, keep, cap=None, Kc=None, Vc=None, M=None, b
     cap = keep if cap is None else cap
     if copy and Kc is None:
         Kc = torch.zeros((b, H_kv, cap, d), dtype=Kt.dtype, device=Kt.device)
-        Vc = torch.zeros((b, H_kv, cap, d), dtype=Vt.dtype, device=Vt.device)
+        Vc = torch.zeros((b, H_kv, d, cap), dtype=Vt.dtype, device=Vt.device)
     flags = K.KVM_FUSE_MEM if M is not None else (K.KVM_FUSE_MOMENTS if moments is not None else 0)
     desc = K.CompactDesc(b=b, L=L, H_kv=H_kv, d=d, cap=cap, keep=keep, dtype=_dtype(Kt), per_head=int(per_head),
                          kv_head_major=int(kv_head_major), flags=flags, lam=lam)
@@ -151,7 +156,8 @@ def kvm_gather_rows(src, slot_map, cap, dst=None, stream=None):
 
 def kvm_mem_update(K_rows, V_rows, M, bvec, lam, row_slot=None, stream=None):
     """Rank-r decayed update of M [b,H_kv,d,d], bvec [b,H_kv,d] with rows K_rows/V_rows
-    [b,r,H_kv,d]; with row_slot [b] i32 the (single) row comes from caches [b,H_kv,cap,d]."""
+    [b,r,H_kv,d]; with row_slot [b] i32 the (single) row comes from the caches
+    (K_rows = Kc [b,H_kv,cap,d], V_rows = Vc [b,H_kv,d,cap])."""
     _contig(K_rows, V_rows, M, bvec, row_slot)
     if row_slot is not None:
         b, H_kv, cap, d = K_rows.shape

@@ -1,6 +1,8 @@
 // A5 + A6 / V2: one pass over K, V that compacts the kept rows into the head-major cache
 // and folds the evicted rows into the latent memory [IM 2.B: decayed outer-product
 // accumulation into M and b] or into MomentKV's moment sums [MKV 1].
+// Cache layout written: Kc [b, H_kv, cap, d] (slot-major), Vc [b, H_kv, d, cap] (dim-major,
+// so that decode's P V product reads 8 consecutive slots of a dim as one 16-byte operand).
 //
 // The memory build is a contraction over evicted tokens:
 //   M_g = sum_i w_i v_i u_i^T,  u_i = phi(k_i) (memory) or k_i (moments), w_i = lam^(n-i) or 1.
@@ -137,7 +139,12 @@ __global__ __launch_bounds__(256) void compact_mfma_kernel(CompactArgs a) {
           const uint4 vr = *reinterpret_cast<const uint4*>(Vb + t * a.tok_stride + db * 8);
           if (s >= 0) {
             if (Kcb) *reinterpret_cast<uint4*>(Kcb + (size_t)s * D + db * 8) = kr;
-            if (Vcb) *reinterpret_cast<uint4*>(Vcb + (size_t)s * D + db * 8) = vr;
+            if (Vcb) {   // dim-major V cache
+              const uint32_t vv[4] = {vr.x, vr.y, vr.z, vr.w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                Vcb[(size_t)(db * 8 + e) * a.cap + s] = (uint16_t)((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xffffu));
+            }
           } else if (fuse) {
             const float w = evict_weight(a, -s);
             float kf[8], vf[8];
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(256) void compact_f32_kernel(CompactArgs a) {
         const int s = smr[t];
         if (s >= 0) {
           if (Kcb) Kcb[(size_t)s * D + dd] = kv;
-          if (Vcb) Vcb[(size_t)s * D + dd] = vf;
+          if (Vcb) Vcb[(size_t)dd * a.cap + s] = vf;
         } else if (fuse) {
           vv = vf;
           if (a.mode == KVM_FUSE_MEM) {
@@ -355,13 +362,15 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
         if (a.row_slot) {
           const int s = slot;
           kp = reinterpret_cast<const T*>(a.K) + (pair * a.cap + s) * D;
-          vp = reinterpret_cast<const T*>(a.V) + (pair * a.cap + s) * D;
+          vp = reinterpret_cast<const T*>(a.V) + pair * a.cap * D + s;   // dim-major V cache
+          k = load_scalar<T>(kp + dd);
+          v = load_scalar<T>(vp + (size_t)dd * a.cap);
         } else {
           kp = reinterpret_cast<const T*>(a.K) + (((size_t)bb * a.r + ri) * a.H_kv + g) * D;
           vp = reinterpret_cast<const T*>(a.V) + (((size_t)bb * a.r + ri) * a.H_kv + g) * D;
+          k = load_scalar<T>(kp + dd);
+          v = load_scalar<T>(vp + dd);
         }
-        k = load_scalar<T>(kp + dd);
-        v = load_scalar<T>(vp + dd);
         const int e = a.r - 1 - ri;  // lam^(r-i) with i = ri + 1
         w = a.lam == 0.f ? (e == 0 ? 1.f : 0.f) : __powf(a.lam, (float)e);
       }

@@ -57,37 +57,34 @@ __global__ __launch_bounds__(256) void keyproj_mfma_kernel(IndexArgs a) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) { acc0[j] = 0.f; acc1[j] = 0.f; }
 
-  // W chunk loader: 64 rows x 64 bf16 = 512 uint4; 256 threads x 2
-  auto load_w = [&](int k0, uint4 (&w)[2]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + i * 256, row = idx >> 3, q = idx & 7;
-      w[i] = *reinterpret_cast<const uint4*>(Wk + (size_t)row * a.D + k0 + q * 8);
-    }
-  };
-  auto store_w = [&](int buf, const uint4 (&w)[2]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + i * 256, row = idx >> 3, q = idx & 7;
-      *reinterpret_cast<uint4*>(&sW[buf][row * kKpPitch + q * 4]) = w[i];
-    }
-  };
-  uint4 wreg[2];
-  load_w(0, wreg);
-  store_w(0, wreg);
-  uint4 xr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) xr[i] = *reinterpret_cast<const uint4*>(xrow + i * 8);
+  // W chunk: 64 rows x 64 bf16 = 512 uint4; 256 threads x 2
+  const int wrow0 = tid >> 3, wrow1 = (tid + 256) >> 3, wq = tid & 7;
+  const uint16_t* w0p = Wk + (size_t)wrow0 * a.D + wq * 8;
+  const uint16_t* w1p = Wk + (size_t)wrow1 * a.D + wq * 8;
+  uint4 w0 = *reinterpret_cast<const uint4*>(w0p);
+  uint4 w1 = *reinterpret_cast<const uint4*>(w1p);
+  *reinterpret_cast<uint4*>(&sW[0][wrow0 * kKpPitch + wq * 4]) = w0;
+  *reinterpret_cast<uint4*>(&sW[0][wrow1 * kKpPitch + wq * 4]) = w1;
+  uint4 x0 = *reinterpret_cast<const uint4*>(xrow + 0);
+  uint4 x1 = *reinterpret_cast<const uint4*>(xrow + 8);
+  uint4 x2 = *reinterpret_cast<const uint4*>(xrow + 16);
+  uint4 x3 = *reinterpret_cast<const uint4*>(xrow + 24);
   __syncthreads();
   const int nk = a.D / 64;
   for (int ks = 0; ks < nk; ++ks) {
     const int buf = ks & 1;
-    uint4 xn[4];
-    if (ks + 1 < nk) {
-      load_w((ks + 1) * 64, wreg);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xn[i] = *reinterpret_cast<const uint4*>(xrow + (ks + 1) * 64 + i * 8);
+    uint4 n0, n1, n2, n3;
+    const bool more = ks + 1 < nk;
+    if (more) {
+      const int k1 = (ks + 1) * 64;
+      w0 = *reinterpret_cast<const uint4*>(w0p + k1);
+      w1 = *reinterpret_cast<const uint4*>(w1p + k1);
+      n0 = *reinterpret_cast<const uint4*>(xrow + k1 + 0);
+      n1 = *reinterpret_cast<const uint4*>(xrow + k1 + 8);
+      n2 = *reinterpret_cast<const uint4*>(xrow + k1 + 16);
+      n3 = *reinterpret_cast<const uint4*>(xrow + k1 + 24);
     }
+    const uint4 xr[4] = {x0, x1, x2, x3};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       bf16x8_t A, B0, B1;
@@ -99,10 +96,10 @@ __global__ __launch_bounds__(256) void keyproj_mfma_kernel(IndexArgs a) {
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B0, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B1, acc1, 0, 0, 0);
     }
-    if (ks + 1 < nk) {
-      store_w(buf ^ 1, wreg);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xr[i] = xn[i];
+    if (more) {
+      *reinterpret_cast<uint4*>(&sW[buf ^ 1][wrow0 * kKpPitch + wq * 4]) = w0;
+      *reinterpret_cast<uint4*>(&sW[buf ^ 1][wrow1 * kKpPitch + wq * 4]) = w1;
+      x0 = n0; x1 = n1; x2 = n2; x3 = n3;
     }
     __syncthreads();
   }

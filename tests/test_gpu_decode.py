@@ -52,12 +52,14 @@ def _oracle(c, dtype, append, memory):
 
 CASES = [
     # dtype, b, H_q, H_kv, d, cap, lens, n_split
-    ("bf16", 2, 32, 8, 128, 700, [410, 666], 0),
-    ("bf16", 1, 32, 8, 128, 700, [333], 3),
-    ("bf16", 3, 32, 8, 128, 300, [0, 17, 298], 5),
+    ("bf16", 2, 32, 8, 128, 704, [410, 666], 0),
+    ("bf16", 1, 32, 8, 128, 704, [333], 3),
+    ("bf16", 3, 32, 8, 128, 304, [0, 17, 303], 5),
     ("bf16", 1, 16, 8, 128, 200, [150], 1),
     ("bf16", 1, 8, 8, 64, 200, [199], 0),
-    ("bf16", 2, 64, 8, 128, 500, [257, 300], 7),
+    ("bf16", 2, 64, 8, 128, 504, [257, 300], 7),
+    ("bf16", 1, 8, 8, 128, 2152, [2151], 0),
+    ("bf16", 1, 32, 8, 128, 64, [0], 2),
     ("f32", 1, 1, 1, 64, 80, [64], 0),
     ("f32", 1, 1, 1, 64, 80, [79], 4),
     ("f32", 2, 8, 2, 128, 96, [33, 60], 2),
@@ -73,7 +75,7 @@ def test_decode_matches_oracle(dtype, b, H_q, H_kv, d, cap, lens, n_split, appen
 
     c = _case(dtype, b, H_q, H_kv, d, cap, lens, seed=cap + b + H_q)
     ref_o, ref_lse, ref_K, ref_V = _oracle(c, dtype, append, memory)
-    Kc, Vc = to_dev(c["Kc"]), to_dev(c["Vc"])
+    Kc, Vc = to_dev(c["Kc"]), to_dev(np.ascontiguousarray(c["Vc"].transpose(0, 1, 3, 2)))   # V dim-major
     lse = torch.empty((b, H_q), dtype=torch.float32, device=Kc.device)
     o = api.kvm_decode_attn_mem(to_dev(c["q"]), Kc, Vc, to_dev(c["lens"]),
                                 k_new=to_dev(c["kn"]) if append else None,
@@ -97,7 +99,7 @@ def test_decode_matches_oracle(dtype, b, H_q, H_kv, d, cap, lens, n_split, appen
         for bi in range(b):
             n = lens[bi]
             assert gK[bi, :, n].tobytes() == c["kn"][bi].tobytes()
-            assert gV[bi, :, n].tobytes() == c["vn"][bi].tobytes()
+            assert np.ascontiguousarray(gV[bi, :, :, n]).tobytes() == c["vn"][bi].tobytes()
 
 
 def test_decode_deterministic_and_split_invariant():
@@ -105,10 +107,10 @@ def test_decode_deterministic_and_split_invariant():
     from learned_kv_cache_mqa_amd import api
     from tests.gpu_util import to_dev, to_np
 
-    c = _case("bf16", 2, 32, 8, 128, 900, [800, 899], seed=7)
+    c = _case("bf16", 2, 32, 8, 128, 904, [800, 899], seed=7)
     outs = []
     for ns in (0, 0, 1, 2, 9, 31):
-        Kc, Vc = to_dev(c["Kc"]), to_dev(c["Vc"])
+        Kc, Vc = to_dev(c["Kc"]), to_dev(np.ascontiguousarray(c["Vc"].transpose(0, 1, 3, 2)))
         o = api.kvm_decode_attn_mem(to_dev(c["q"]), Kc, Vc, to_dev(c["lens"]), M=to_dev(c["M"]),
                                     bvec=to_dev(c["bv"]), w_g=to_dev(c["w_g"]), n_split=ns)
         torch.cuda.synchronize()

@@ -71,21 +71,22 @@ def test_prefill_end_to_end(cfg):
                             to_dev(p["W_g"]), eps=cfg.eps_rms)
     idx, sm = api.kvm_topk_select(I, cfg.B, cfg.R, cfg.recent_inclusive)
     keep = idx.shape[1]
+    cap = api.cache_cap(keep + cfg.T)
     M = torch.zeros((cfg.b, cfg.H_kv, cfg.d, cfg.d), dtype=torch.float32, device="cuda")
     bv = torch.zeros((cfg.b, cfg.H_kv, cfg.d), dtype=torch.float32, device="cuda")
-    Kc, Vc = api.kvm_compact_kv(Kt, Vt, sm, keep, keep + cfg.T, M=M, bvec=bv, lam=lam)
+    Kc, Vc = api.kvm_compact_kv(Kt, Vt, sm, keep, cap, M=M, bvec=bv, lam=lam)
     torch.cuda.synchronize()
     f = lambda x: gen.from_storage(x, cfg.dtype)
     for i in range(cfg.b):
         pre = im.prefill(f(p["X"][i]), f(p["Qwin"][i]), f(p["K"][i]), f(p["V"][i]), f(p["W_kI"]), p["gamma_k"],
                          f(p["W_qI"]), p["gamma_q"], f(p["W_g"]), cfg.B, cfg.R, lam, cfg.recent_inclusive,
-                         eps=cfg.eps_rms, cap=keep + cfg.T)
+                         eps=cfg.eps_rms, cap=cap)
         n_diff = set_check(to_np(idx)[i], pre["I"], cfg.B, cfg.R, cfg.recent_inclusive)
         if n_diff:
             continue   # a valid different choice inside the band: downstream legitimately differs
         assert to_np(idx)[i].tolist() == pre["idx"].tolist()
-        rK, rV = im.compact(p["K"][i], p["V"][i], pre["slot_map"], keep + cfg.T)
+        rK, rV = im.compact(p["K"][i], p["V"][i], pre["slot_map"], cap)
         assert to_np(Kc)[i].tobytes() == rK.tobytes()
-        assert to_np(Vc)[i].tobytes() == rV.tobytes()
+        assert to_np(Vc)[i].tobytes() == np.ascontiguousarray(rV.transpose(0, 2, 1)).tobytes()
         assert_output(to_np(M)[i], pre["M"], cfg.dtype, "M")
         assert_output(to_np(bv)[i], pre["b"], cfg.dtype, "b")

@@ -98,7 +98,7 @@ def test_compact_and_memory_build(dtype, b, L, H, d, B, R, lam, extra):
     for i in range(b):
         rK, rV = im.compact(Kt[i], Vt[i], smaps[i], cap)
         assert gK[i].tobytes() == rK.tobytes()
-        assert gV[i].tobytes() == rV.tobytes()
+        assert gV[i].tobytes() == np.ascontiguousarray(rV.transpose(0, 2, 1)).tobytes()   # V dim-major
         ev = im.evicted_in_order(smaps[i])
         for g in range(H):
             refM, refb = im.memory_build(Kd[i, ev, g], Vd[i, ev, g], lam, M0[i, g], b0[i, g])
@@ -181,12 +181,13 @@ def test_gather_rows_and_rank_r_update():
             assert normwise(to_np(M)[i, g], rM) < 1e-5
             assert normwise(to_np(bv)[i, g], rb) < 1e-5
     # single row taken from the cache at a device-given slot
-    cap = 11
+    cap = 16
     Kc = gen.to_storage(rg.standard_normal((b, H, cap, d)), "bf16")
     Vc = gen.to_storage(rg.standard_normal((b, H, cap, d)), "bf16")
     slots = np.array([3, 10], np.int32)
     M, bv = to_dev(M0.copy()), to_dev(b0.copy())
-    api.kvm_mem_update(to_dev(Kc), to_dev(Vc), M, bv, lam, row_slot=to_dev(slots))
+    api.kvm_mem_update(to_dev(Kc), to_dev(np.ascontiguousarray(Vc.transpose(0, 1, 3, 2))), M, bv, lam,
+                       row_slot=to_dev(slots))
     torch.cuda.synchronize()
     Kd, Vd = gen.from_storage(Kc, "bf16"), gen.from_storage(Vc, "bf16")
     for i in range(b):
