@@ -167,7 +167,7 @@ def main():
             api.kvm_index_score(li["X"], li["Q"], li["W_kI"], li["gk"], li["W_qI"], li["gq"], li["W_g"], I=I,
                                 eps=cfg.eps_rms, ws=ws_i)
             api.kvm_topk_select(I, cfg.B, cfg.R, True, idx=idx, slot_map=sm)
-            api.kvm_compact_kv(li["K"], li["V"], sm, keep, cap, Kc=Kc[l], Vc=Vc[l], M=Ms[l], bvec=bs[l], lam=lam,
+            api.kvm_compact_kv(li["K"], li["V"], sm, idx, keep, cap, Kc=Kc[l], Vc=Vc[l], M=Ms[l], bvec=bs[l], lam=lam,
                                ws=ws_c)
 
     def decode_steps(t0, t1):

@@ -25,9 +25,9 @@
  *   - Layouts are dense row-major (C order) with the shapes given; element types are fixed
  *     per argument (KVM_F32 / KVM_BF16 arguments follow desc->dtype).  Device pointers must
  *     be 16-byte aligned.
- *   - Workspaces: `ws` must hold kvm_*_workspace_size() bytes and be ZERO-FILLED before its
- *     first use; every call leaves the counters it uses at zero again, so one zero-fill at
- *     allocation suffices.  Two calls that share a workspace must not overlap in time.
+ *   - Workspaces: `ws` must hold kvm_*_workspace_size() bytes (device memory, any
+ *     contents); it holds only intermediates of one call.  Two calls that share a
+ *     workspace must not overlap in time.
  *   - No floating-point atomics are used; repeated calls give bitwise identical results.
  */
 #ifndef KVM_H
@@ -125,18 +125,22 @@ kvm_status kvm_topk_select(const kvm_topk_desc* desc, const float* I, int32_t* i
 /* ------------------------------------------------------------------------------------ *
  * A5 + A6 / V2  Compaction with a fused latent-memory or moment build  [IM 2.A, 2.B; MKV 1]
  *
- * One pass over K, V: kept rows go to the caches at their slot -- Kc [b, H_kv, cap, d]
- * (slot-major) and Vc [b, H_kv, d, cap] (dim-major: element (slot, i) at Vc[.., i, slot]);
- * evicted rows are folded in:
+ * Kept rows go to the caches at their slot -- Kc [b, H_kv, cap, d] (slot-major) and
+ * Vc [b, H_kv, d, cap] (dim-major: element (slot, i) at Vc[.., i, slot]); one pass over all
+ * of K, V folds the evicted rows in:
  *   KVM_FUSE_MEM:     n = number evicted; with eviction ranks i = 1..n (ascending position)
  *                     M <- lam^n M + sum_i lam^(n-i) v_i phi(k_i)^T,
  *                     bvec <- lam^n bvec + sum_i lam^(n-i) phi(k_i),   phi = elu + 1.
  *   KVM_FUSE_MOMENTS: n_e += n; s_k += sum k; s_v += sum v; S += sum v k^T.
  * K, V:  token-major [b, L, H_kv, d] (kv_head_major = 0) or head-major [b, H_kv, L, d].
  * slot_map: [b, L] (shared by all KV heads) or [b, H_kv, L] (per_head = 1), as produced
- *           by kvm_topk_select; n is taken as the count of negative entries (= L - keep).
+ *           by kvm_topk_select: selects the evicted rows and their ranks; read only when
+ *           flags != 0.  n = L - keep.
+ * idx:   [b, keep] (or [b, H_kv, keep]) kept positions in slot order, as produced by the same
+ *        kvm_topk_select call; required when Kc/Vc are given (slot s <- position idx[s];
+ *        an index outside [0, L) leaves a zero row).
  * keep:  number of kept positions per row (the caller's budget arithmetic; host value).
- * Kc/Vc may be NULL (memory/moment update only).  M [b,H_kv,d,d] f32 (rows index v,
+ * Kc/Vc may be NULL (memory/moment update only); slots >= keep are not written.  M [b,H_kv,d,d] f32 (rows index v,
  * columns index phi(k)), bvec [b,H_kv,d] f32; moments n_e [b,H_kv] i32, s_k, s_v
  * [b,H_kv,d] f32, S [b,H_kv,d,d] f32.  All state arrays are read-modify-write.
  * Supported: d in {64, 128}; cap >= keep.
@@ -157,7 +161,8 @@ typedef struct {
 
 size_t kvm_compact_workspace_size(const kvm_compact_desc* desc);
 kvm_status kvm_compact_kv(const kvm_compact_desc* desc, const void* K, const void* V,
-                          const int32_t* slot_map, void* Kc, void* Vc, float* M, float* bvec,
+                          const int32_t* slot_map, const int32_t* idx, void* Kc, void* Vc,
+                          float* M, float* bvec,
                           int32_t* n_e, float* s_k, float* s_v, float* S,
                           void* ws, size_t ws_bytes, void* stream);
 

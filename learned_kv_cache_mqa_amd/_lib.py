@@ -66,7 +66,7 @@ SIGNATURES = {
     "kvm_topk_keep": (i32, [C.POINTER(TopkDesc)]),
     "kvm_topk_select": (C.c_int, [C.POINTER(TopkDesc), vp, vp, vp, vp]),
     "kvm_compact_workspace_size": (sz, [C.POINTER(CompactDesc)]),
-    "kvm_compact_kv": (C.c_int, [C.POINTER(CompactDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+    "kvm_compact_kv": (C.c_int, [C.POINTER(CompactDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  vp, sz, vp]),
     "kvm_gather_rows": (C.c_int, [i32, i32, i32, i32, vp, vp, vp, vp]),
     "kvm_mem_update": (C.c_int, [C.POINTER(MemDesc), vp, vp, vp, vp, vp, vp]),

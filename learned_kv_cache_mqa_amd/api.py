@@ -32,14 +32,14 @@ def _dtype(t):
 
 
 def workspace(nbytes, device=None, stream=None, tag="default"):
-    """A zero-filled workspace of at least nbytes, cached per (device, stream, tag).
-    libkvmem leaves the counters it uses at zero, so the buffer is reusable in stream order."""
+    """A device workspace of at least nbytes, cached per (device, stream, tag); calls on one
+    stream use it in stream order."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     s = torch.cuda.current_stream(dev) if stream is None else stream
     key = (dev.index, s.cuda_stream, tag)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf
     return buf
 
@@ -116,12 +116,13 @@ def cache_cap(n):
     return (int(n) + 7) // 8 * 8
 
 
-def kvm_compact_kv(Kt, Vt, slot_map, keep, cap=None, Kc=None, Vc=None, M=None, bvec=None, moments=None,
+def kvm_compact_kv(Kt, Vt, slot_map, idx, keep, cap=None, Kc=None, Vc=None, M=None, bvec=None, moments=None,
                    lam=1.0, per_head=False, kv_head_major=False, copy=True, stream=None, ws=None):
     """Compact kept rows of K, V ([b,L,H_kv,d], or [b,H_kv,L,d] if kv_head_major) into
     Kc [b,H_kv,cap,d] (slot-major) and Vc [b,H_kv,d,cap] (dim-major); fold evicted rows into
-    (M, bvec) or into moments dict(n_e, s_k, s_v, S).  Returns (Kc, Vc)."""
-    _contig(Kt, Vt, slot_map, Kc, Vc, M, bvec)
+    (M, bvec) or into moments dict(n_e, s_k, s_v, S).  slot_map and idx are the two outputs
+    of one kvm_topk_select call (idx may be None when no cache is filled).  Returns (Kc, Vc)."""
+    _contig(Kt, Vt, slot_map, idx, Kc, Vc, M, bvec)
     if kv_head_major:
         b, H_kv, L, d = Kt.shape
     else:
@@ -137,7 +138,7 @@ def kvm_compact_kv(Kt, Vt, slot_map, keep, cap=None, Kc=None, Vc=None, M=None, b
     if ws is None:
         ws = workspace(nb, Kt.device, stream, "compact")
     mo = moments or {}
-    check(lib().kvm_compact_kv(C.byref(desc), _p(Kt), _p(Vt), _p(slot_map), _p(Kc), _p(Vc), _p(M), _p(bvec),
+    check(lib().kvm_compact_kv(C.byref(desc), _p(Kt), _p(Vt), _p(slot_map), _p(idx), _p(Kc), _p(Vc), _p(M), _p(bvec),
                                _p(mo.get("n_e")), _p(mo.get("s_k")), _p(mo.get("s_v")), _p(mo.get("S")),
                                _p(ws), ws.numel(), _stream(stream)))
     return Kc, Vc

@@ -11,6 +11,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 namespace kvm {
 
@@ -33,12 +35,6 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 #define KVM_OPT_ALIGNED(p) do { if (p) KVM_ALIGNED(p); } while (0)
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-// Every workspace starts with a fixed region of completion counters that calls leave at
-// zero; data sections follow it.  Counters never move, so one zero-filled workspace can
-// serve calls with different descriptors.
-constexpr size_t kCounterBytes = 65536;
-constexpr int kMaxCounters = int(kCounterBytes / sizeof(int));
 
 // ------------------------------------------------------------------------------ device side
 
@@ -124,24 +120,6 @@ __device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __e
 __device__ __forceinline__ float sigmoid_f(float x) {
   float e = __expf(-fabsf(x));
   return x >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
-}
-
-// Last-block ticket: returns true in every thread of the block that arrives last among
-// `n` blocks sharing *counter, and resets the counter for the next call.  Writes made by
-// the other blocks before their ticket are visible to the last block afterwards.
-__device__ __forceinline__ bool last_block_ticket(int* counter, int n, int* smem_flag) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    int t = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    int last = (t == n - 1);
-    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *smem_flag = last;
-  }
-  __syncthreads();
-  bool last = *smem_flag != 0;
-  if (last) __threadfence();
-  return last;
 }
 
 }  // namespace kvm

@@ -10,9 +10,9 @@
 // 32 tokens; V^T and U^T tiles are staged in LDS (token pairs packed per dim row) and the
 // d x d partial product runs on the matrix cores (v_mfma_f32_32x32x16_bf16).  V is exact
 // in bf16; u = w phi(k) is split into bf16 hi + lo so the product keeps ~16 bits of u.
-// fp32 inputs use fp32 FMA.  Partial states per chunk go to the workspace; the last block
-// of a (sequence, KV head) sums them in chunk order (deterministic, no float atomics) and
-// applies the decay of the previous state: M <- lam^n M + sum_c M_c.
+// fp32 inputs use fp32 FMA.  Partial states per chunk go to the workspace; a second kernel
+// sums them in chunk order (deterministic, no float atomics) and applies the decay of the
+// previous state: M <- lam^n M + sum_c M_c.
 #include "common.hpp"
 
 namespace kvm {
@@ -21,8 +21,6 @@ struct CompactArgs {
   const void* K;
   const void* V;
   const int32_t* slot_map;
-  void* Kc;
-  void* Vc;
   float* M;     // memory: M; moments: S
   float* vec0;  // memory: bvec; moments: s_k
   float* vec1;  // moments: s_v
@@ -30,8 +28,7 @@ struct CompactArgs {
   float* partM;    // [pairs, chunks, D, D]
   float* partv;    // [pairs, chunks, 2, D]
   int* partn;      // [pairs, chunks]
-  int* counters;   // [pairs]
-  int L, H_kv, cap, n_ev, chunk, n_chunks, per_head;
+  int L, H_kv, n_ev, chunk, n_chunks, per_head;
   long long tok_stride, head_stride, batch_stride;  // elements
   int mode;        // 0 copy, KVM_FUSE_MEM, KVM_FUSE_MOMENTS
   float log2lam;   // log2(lam) (lam > 0)
@@ -40,39 +37,46 @@ struct CompactArgs {
   float lam_n;     // lam^n_ev
 };
 
-__device__ __forceinline__ float evict_weight(const CompactArgs& a, int rank) {
-  if (a.mode != KVM_FUSE_MEM) return 1.f;
-  const int e = a.n_ev - rank;
-  if (a.lam_zero) return e == 0 ? 1.f : 0.f;
-  return exp2f((float)e * a.log2lam);
-}
-
-// ------------------------------------------------------------------ final fixed-order reduce
+// ------------------------------------------------------------------ fixed-order reduce
+// grid (ceil(E / 1024), pairs) with E = D*D + 2*D + 1 elements per (sequence, KV head):
+// sums the chunk partials in chunk order (deterministic) and applies the decay of the
+// previous state: state <- lam^n state + sum_c part_c (lam^n = 1 for the moment sums).
 template <int D>
-__device__ void compact_finish(const CompactArgs& a, size_t pair) {
-  const int tid = threadIdx.x;
-  const float* pm = a.partM + pair * a.n_chunks * (size_t)(D * D);
-  const float* pv = a.partv + pair * a.n_chunks * (size_t)(2 * D);
+__global__ __launch_bounds__(256) void compact_reduce_kernel(CompactArgs a) {
+  const size_t pair = blockIdx.y;
+  const int e0 = (blockIdx.x * 256 + threadIdx.x) * 4;
   const bool mem = a.mode == KVM_FUSE_MEM;
   const float dec = mem ? a.lam_n : 1.f;
-  float* Mo = a.M + pair * (size_t)(D * D);
-  for (int i = tid; i < D * D; i += blockDim.x) {
-    float s = 0.f;
-    for (int c = 0; c < a.n_chunks; ++c) s += pm[(size_t)c * D * D + i];
-    Mo[i] = fmaf(dec, Mo[i], s);
-  }
-  for (int i = tid; i < 2 * D; i += blockDim.x) {
-    if (mem && i >= D) break;
-    float s = 0.f;
-    for (int c = 0; c < a.n_chunks; ++c) s += pv[(size_t)c * 2 * D + i];
-    float* out = (i < D ? a.vec0 : a.vec1) + pair * D;
-    const int j = i % D;
-    out[j] = fmaf(dec, out[j], s);
-  }
-  if (!mem && tid == 0) {
-    int s = 0;
-    for (int c = 0; c < a.n_chunks; ++c) s += a.partn[pair * a.n_chunks + c];
-    a.n_e[pair] += s;
+  if (e0 < D * D) {
+    const float* pm = a.partM + pair * a.n_chunks * (size_t)(D * D) + e0;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < a.n_chunks; ++c) {
+      const float4 v = *reinterpret_cast<const float4*>(pm + (size_t)c * D * D);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    float4* mo = reinterpret_cast<float4*>(a.M + pair * (size_t)(D * D) + e0);
+    float4 o = *mo;
+    o.x = fmaf(dec, o.x, acc.x); o.y = fmaf(dec, o.y, acc.y);
+    o.z = fmaf(dec, o.z, acc.z); o.w = fmaf(dec, o.w, acc.w);
+    *mo = o;
+  } else if (e0 < D * D + 2 * D) {
+    const int i = e0 - D * D;
+    if (mem && i >= D) return;
+    const float* pv = a.partv + pair * a.n_chunks * (size_t)(2 * D) + i;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < a.n_chunks; ++c) {
+      const float4 v = *reinterpret_cast<const float4*>(pv + (size_t)c * 2 * D);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    float4* vo = reinterpret_cast<float4*>((i < D ? a.vec0 : a.vec1) + pair * D + (i % D));
+    float4 o = *vo;
+    o.x = fmaf(dec, o.x, acc.x); o.y = fmaf(dec, o.y, acc.y);
+    o.z = fmaf(dec, o.z, acc.z); o.w = fmaf(dec, o.w, acc.w);
+    *vo = o;
+  } else if (e0 == D * D + 2 * D && !mem) {
+    int n = 0;
+    for (int c = 0; c < a.n_chunks; ++c) n += a.partn[pair * a.n_chunks + c];
+    a.n_e[pair] += n;
   }
 }
 
@@ -82,160 +86,249 @@ __device__ void compact_finish(const CompactArgs& a, size_t pair) {
 constexpr int kTok = 32;
 constexpr int kPitch = 18;
 
-template <int D>
-__global__ __launch_bounds__(256) void compact_mfma_kernel(CompactArgs a) {
+// Buffer resource over `bytes` bytes from `base`: loads at offsets past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Stages one tile of 32 tokens for the contraction: this thread holds tokens (2 pr, 2 pr + 1)
+// x dims db*8 .. db*8+8 of K and V.  Writes V^T (exact bf16) to sV and u = w phi(k) (memory)
+// or k (moments) to sH (+ the bf16 remainder of u to sL in memory mode), one word per token
+// pair per dim row; rows of kept tokens and positions past the chunk are staged as zeros.
+//   memory: w = lam^(n - rank) = 2^lw,  w phi(x) = w (x + 1) for x > 0, 2^(x log2 e + lw) else.
+template <int D, bool MEM>
+__device__ __forceinline__ void stage_tile(const CompactArgs& a, int pr, int db, bool loader,
+                                           int t0, int p1, uint4 k0v, uint4 k1v, uint4 v0v, uint4 v1v,
+                                           int s0, int s1, uint32_t* sV, uint32_t* sH, uint32_t* sL,
+                                           float (&vacc0)[8], float (&vacc1)[8], int& nloc) {
+  const bool ev0 = loader && t0 < p1 && s0 < 0;
+  const bool ev1 = loader && t0 + 1 < p1 && s1 < 0;
+  if (db == 0) nloc += (int)ev0 + (int)ev1;
+  if (!loader) return;   // D = 64: the spare threads alias a loader's LDS words
+  float w0 = 0.f, w1 = 0.f, lw0 = -INFINITY, lw1 = -INFINITY;
+  if (MEM) {
+    const int e0 = a.n_ev + s0, e1 = a.n_ev + s1;
+    if (ev0) lw0 = a.lam_zero ? (e0 == 0 ? 0.f : -INFINITY) : (float)e0 * a.log2lam;
+    if (ev1) lw1 = a.lam_zero ? (e1 == 0 ? 0.f : -INFINITY) : (float)e1 * a.log2lam;
+    w0 = __builtin_amdgcn_exp2f(lw0);
+    w1 = __builtin_amdgcn_exp2f(lw1);
+  }
+  // byte selectors: a token's bf16 half of a K word moved to the top half (or zero when the
+  // token is not evicted), and the two tokens' halves of a V word packed into one word
+  const uint32_t se0 = ev0 ? 0x01000c0cu : 0x0c0c0c0cu, so0 = ev0 ? 0x03020c0cu : 0x0c0c0c0cu;
+  const uint32_t se1 = ev1 ? 0x01000c0cu : 0x0c0c0c0cu, so1 = ev1 ? 0x03020c0cu : 0x0c0c0c0cu;
+  const uint32_t vmask = (ev0 ? 0x0000ffffu : 0u) | (ev1 ? 0xffff0000u : 0u);
+  const uint32_t k0[4] = {k0v.x, k0v.y, k0v.z, k0v.w}, k1[4] = {k1v.x, k1v.y, k1v.z, k1v.w};
+  const uint32_t v0[4] = {v0v.x, v0v.y, v0v.z, v0v.w}, v1[4] = {v1v.x, v1v.y, v1v.z, v1v.w};
+  constexpr float kLog2e = 1.4426950408889634f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int at = (db * 8 + e) * kPitch + pr;
+    const bool odd = e & 1;
+    const uint32_t vw = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], odd ? 0x07060302u : 0x05040100u) & vmask;
+    sV[at] = vw;
+    const float x0 = __uint_as_float(__builtin_amdgcn_perm(0u, k0[e >> 1], odd ? so0 : se0));
+    const float x1 = __uint_as_float(__builtin_amdgcn_perm(0u, k1[e >> 1], odd ? so1 : se1));
+    f32x2_t u;
+    if (MEM) {
+      const float n0 = __builtin_amdgcn_exp2f(fmaf(x0, kLog2e, lw0));
+      const float n1 = __builtin_amdgcn_exp2f(fmaf(x1, kLog2e, lw1));
+      u.x = x0 > 0.f ? fmaf(w0, x0, w0) : n0;
+      u.y = x1 > 0.f ? fmaf(w1, x1, w1) : n1;
+    } else {
+      u.x = x0;
+      u.y = x1;
+      vacc1[e] += __uint_as_float(vw << 16) + __uint_as_float(vw & 0xffff0000u);
+    }
+    vacc0[e] += u.x + u.y;
+    const bf16x2_t hi = __builtin_convertvector(u, bf16x2_t);   // round to nearest even
+    uint32_t hw;
+    __builtin_memcpy(&hw, &hi, 4);
+    sH[at] = hw;
+    if (MEM) {
+      f32x2_t r;
+      r.x = u.x - __uint_as_float(hw << 16);
+      r.y = u.y - __uint_as_float(hw & 0xffff0000u);
+      const bf16x2_t lo = __builtin_convertvector(r, bf16x2_t);
+      uint32_t lw;
+      __builtin_memcpy(&lw, &lo, 4);
+      sL[at] = lw;
+    }
+  }
+}
+
+#ifndef KVM_COMPACT_NB
+#define KVM_COMPACT_NB 2
+#endif
+#ifndef KVM_COMPACT_WPE
+#define KVM_COMPACT_WPE 2
+#endif
+// Contraction of the evicted rows of one chunk of positions of one (sequence, KV head):
+// grid (chunks, H_kv, b), 256 threads.  Raw K/V rows stream through a register ring NB tiles
+// deep; staged tiles alternate between two LDS buffers so that the staging of tile t + 1 (VALU)
+// overlaps the matrix-core work on tile t, with one barrier per tile.  Each wave owns a
+// 2 x 2 block of 32 x 32 output tiles (D = 128) or one tile (D = 64).
+template <int D, bool MEM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVM_COMPACT_WPE, KVM_COMPACT_WPE)))
+void compact_mfma_kernel(CompactArgs a) {
   static_assert(D == 64 || D == 128, "D");
   constexpr int NT = D / 32;               // 32x32 tiles per side
-  constexpr int TPW = NT * NT / 4;         // output tiles per wave (4 waves)
+  constexpr int NTI = NT / 2, NTJ = NT / 2; // tiles per wave along v rows / u columns
   constexpr int DB = D / 8;                // 8-dim blocks per row
-  constexpr int PAIRS_PER_PASS = (256 / DB) < (kTok / 2) ? (256 / DB) : (kTok / 2);
-  constexpr int PASSES = (kTok / 2) / PAIRS_PER_PASS;
-  static_assert(PASSES * PAIRS_PER_PASS == kTok / 2, "tile");
+  constexpr int PAIRS = (256 / DB) < (kTok / 2) ? (256 / DB) : (kTok / 2);
+  static_assert(PAIRS == kTok / 2, "one pass of token pairs per tile");
+  constexpr int NB = KVM_COMPACT_NB;       // raw tiles in flight per thread
   const int c = blockIdx.x, g = blockIdx.y, bb = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t pair = (size_t)bb * a.H_kv + g;
 
-  __shared__ uint32_t sV[D * kPitch];
-  __shared__ uint32_t sH[D * kPitch];
-  __shared__ uint32_t sL[D * kPitch];
-  __shared__ int s_flag, s_n;
+  __shared__ uint32_t sV[2][D * kPitch];
+  __shared__ uint32_t sH[2][D * kPitch];
+  __shared__ uint32_t sL[2][MEM ? D * kPitch : 1];
+  __shared__ int s_n;
 
-  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + bb * a.batch_stride + g * a.head_stride;
-  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.V) + bb * a.batch_stride + g * a.head_stride;
-  const int32_t* smr = a.slot_map + (a.per_head ? pair : (size_t)bb) * a.L;
-  uint16_t* Kcb = a.Kc ? reinterpret_cast<uint16_t*>(a.Kc) + pair * a.cap * D : nullptr;
-  uint16_t* Vcb = a.Vc ? reinterpret_cast<uint16_t*>(a.Vc) + pair * a.cap * D : nullptr;
-  const bool fuse = a.mode != 0;
+  const int p0 = c * a.chunk, p1 = min(a.L, p0 + a.chunk);
+  const int ntiles = (p1 - p0 + kTok - 1) / kTok;
+  // this chunk's rows through buffer resources: positions past p1 read as zeros (slot 0,
+  // i.e. kept, so they stage nothing)
+  const long long cbase = bb * a.batch_stride + g * a.head_stride + (long long)p0 * a.tok_stride;
+  const int rowb = (int)(a.tok_stride * 2);
+  const int nbytes = (p1 - p0 - 1) * rowb + D * 2;
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(reinterpret_cast<const uint16_t*>(a.K) + cbase, nbytes);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(reinterpret_cast<const uint16_t*>(a.V) + cbase, nbytes);
+  const __amdgpu_buffer_rsrc_t rS =
+      make_rsrc(a.slot_map + (a.per_head ? pair : (size_t)bb) * a.L + p0, (p1 - p0) * 4);
 
-  // thread -> (token pair within pass, 8-dim block)
-  const int tp = tid % PAIRS_PER_PASS;
-  const int db = tid / PAIRS_PER_PASS;
-  const bool loader = db < DB;   // D = 64 leaves half the threads without a load slot
+  // thread -> (token pair, 8-dim block); D = 64 leaves half the threads without a slot of
+  // their own (they load a duplicate and stage nothing)
+  const int pr = tid % PAIRS;
+  const int db = (tid / PAIRS) % DB;
+  const bool loader = DB * PAIRS >= 256 || tid / PAIRS < DB;
   float vacc0[8], vacc1[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { vacc0[e] = 0.f; vacc1[e] = 0.f; }
   int nloc = 0;
 
-  f32x16_t acc[TPW];
+  const int wi = wave / 2, wj = wave % 2;
+  f32x16_t acc[NTI * NTJ];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
+  for (int t = 0; t < NTI * NTJ; ++t)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[t][j] = 0.f;
 
-  const int p0 = c * a.chunk, p1 = min(a.L, p0 + a.chunk);
-  for (int base = p0; base < p1; base += kTok) {
+  uint4 rk[NB][2] = {}, rv[NB][2] = {};
+  int rs[NB][2] = {};
+  // Loads are unconditional and the tile loop runs a multiple of NB tiles without an early
+  // exit, so the number of loads in flight is static and the waits cover only the oldest tile.
+  const int voff0 = 2 * pr * rowb + db * 16;
+  auto fetch = [&](int st, int tile) {
+    const int tb = tile * kTok * rowb;
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const int pr = ps * PAIRS_PER_PASS + tp;  // pair index in tile
-      uint32_t vw[8], hw[8], lw[8];
+    for (int h = 0; h < 2; ++h) {
+      const int off = voff0 + h * rowb + tb;
+      rs[st][h] = __builtin_amdgcn_raw_buffer_load_b32(rS, (tile * kTok + 2 * pr + h) * 4, 0, 0);
+      const auto kv = __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, 0);
+      const auto vv = __builtin_amdgcn_raw_buffer_load_b128(rV, off, 0, 0);
+      rk[st][h] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
+      rv[st][h] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+    }
+  };
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { vw[e] = 0; hw[e] = 0; lw[e] = 0; }
+  for (int st = 0; st < NB; ++st) fetch(st, st);
+  stage_tile<D, MEM>(a, pr, db, loader, p0 + 2 * pr, p1, rk[0][0], rk[0][1], rv[0][0], rv[0][1], rs[0][0], rs[0][1],
+                     sV[0], sH[0], sL[0], vacc0, vacc1, nloc);
+  fetch(0, NB);
+  __syncthreads();
+
+  static_assert(NB % 2 == 0, "LDS buffer parity follows the ring slot");
+  for (int t0 = 0; t0 < ntiles; t0 += NB) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int t = base + 2 * pr + half;
-        if (loader && t < p1) {
-          const int s = smr[t];
-          const uint4 kr = *reinterpret_cast<const uint4*>(Kb + t * a.tok_stride + db * 8);
-          const uint4 vr = *reinterpret_cast<const uint4*>(Vb + t * a.tok_stride + db * 8);
-          if (s >= 0) {
-            if (Kcb) *reinterpret_cast<uint4*>(Kcb + (size_t)s * D + db * 8) = kr;
-            if (Vcb) {   // dim-major V cache
-              const uint32_t vv[4] = {vr.x, vr.y, vr.z, vr.w};
+    for (int st = 0; st < NB; ++st) {
+      const int t = t0 + st;   // tiles past the chunk stage zeros and add nothing
+      const int cur = st & 1, nxt = cur ^ 1;
+      // matrix cores on tile t: 2 k-steps of 16 tokens; lane (m, kg) reads 8 tokens = 4 words.
+      // All hi products are issued before the lo ones so that no MFMA waits on the previous.
 #pragma unroll
-              for (int e = 0; e < 8; ++e)
-                Vcb[(size_t)(db * 8 + e) * a.cap + s] = (uint16_t)((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xffffu));
-            }
-          } else if (fuse) {
-            const float w = evict_weight(a, -s);
-            float kf[8], vf[8];
-            Vec16<uint16_t>::unpack(kr, kf);
-            Vec16<uint16_t>::unpack(vr, vf);
-            const uint32_t vv[4] = {vr.x, vr.y, vr.z, vr.w};
+      for (int ks = 0; ks < 2; ++ks) {
+        const int woff = ks * 8 + (lane >> 5) * 4;
+        const int m = lane & 31;
+        bf16x8_t A[NTI], Bh[NTJ], Bl[NTJ];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float u = a.mode == KVM_FUSE_MEM ? w * phi_f(kf[e]) : kf[e];
-              const uint32_t hb = f32_to_bf16_bits(u);
-              const uint32_t lb = f32_to_bf16_bits(u - __uint_as_float(hb << 16));
-              const uint32_t vb = (e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xffffu);
-              vw[e] |= vb << (16 * half);
-              hw[e] |= hb << (16 * half);
-              lw[e] |= lb << (16 * half);
-              vacc0[e] += u;
-              vacc1[e] += vf[e];
-            }
-            if (db == 0) ++nloc;
+        for (int x = 0; x < NTI; ++x) {
+          const uint32_t* pa = sV[cur] + ((wi * NTI + x) * 32 + m) * kPitch + woff;
+          const uint2 a0 = *reinterpret_cast<const uint2*>(pa), a1 = *reinterpret_cast<const uint2*>(pa + 2);
+          const uint4 av = {a0.x, a0.y, a1.x, a1.y};
+          __builtin_memcpy(&A[x], &av, 16);
+        }
+#pragma unroll
+        for (int y = 0; y < NTJ; ++y) {
+          const int r = ((wj * NTJ + y) * 32 + m) * kPitch + woff;
+          const uint2 h0 = *reinterpret_cast<const uint2*>(sH[cur] + r), h1 = *reinterpret_cast<const uint2*>(sH[cur] + r + 2);
+          const uint4 hv = {h0.x, h0.y, h1.x, h1.y};
+          __builtin_memcpy(&Bh[y], &hv, 16);
+          if (MEM) {
+            const uint2 l0 = *reinterpret_cast<const uint2*>(sL[cur] + r), l1 = *reinterpret_cast<const uint2*>(sL[cur] + r + 2);
+            const uint4 lv = {l0.x, l0.y, l1.x, l1.y};
+            __builtin_memcpy(&Bl[y], &lv, 16);
           }
         }
-      }
-      if (fuse && loader) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int row = db * 8 + e;
-          sV[row * kPitch + pr] = vw[e];
-          sH[row * kPitch + pr] = hw[e];
-          sL[row * kPitch + pr] = lw[e];
-        }
+        for (int x = 0; x < NTI; ++x)
+#pragma unroll
+          for (int y = 0; y < NTJ; ++y)
+            acc[x * NTJ + y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[x], Bh[y], acc[x * NTJ + y], 0, 0, 0);
+        if (MEM)
+#pragma unroll
+          for (int x = 0; x < NTI; ++x)
+#pragma unroll
+            for (int y = 0; y < NTJ; ++y)
+              acc[x * NTJ + y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[x], Bl[y], acc[x * NTJ + y], 0, 0, 0);
       }
+      // stage tile t + 1 (ring slot (st + 1) % NB) into the other buffer, refill its slot
+      const int sn = (st + 1) % NB;
+      stage_tile<D, MEM>(a, pr, db, loader, p0 + (t + 1) * kTok + 2 * pr, p1, rk[sn][0], rk[sn][1], rv[sn][0],
+                         rv[sn][1], rs[sn][0], rs[sn][1], sV[nxt], sH[nxt], sL[nxt], vacc0, vacc1, nloc);
+      fetch(sn, t + 1 + NB);
+#ifdef KVM_COMPACT_INTERLEAVE
+      // spread the matrix-core instructions over the staging arithmetic
+#pragma unroll
+      for (int i = 0; i < NTI * NTJ * 2 * (MEM ? 2 : 1); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, KVM_COMPACT_INTERLEAVE, 0);
+      }
+#endif
+      __syncthreads();
     }
-    if (!fuse) continue;
-    __syncthreads();
-    // 2 k-steps of 16 tokens; lane (m = lane % 32, kg = lane / 32) reads 8 tokens = 4 words
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int woff = ks * 8 + (lane >> 5) * 4;
-      const int m = lane & 31;
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const int tile = wave * TPW + t;
-        const int ti = tile / NT, tj = tile % NT;   // dv tile, dk tile
-        const uint32_t* pa = sV + (ti * 32 + m) * kPitch + woff;
-        const uint32_t* ph = sH + (tj * 32 + m) * kPitch + woff;
-        const uint32_t* pl = sL + (tj * 32 + m) * kPitch + woff;
-        const uint2 a0 = *reinterpret_cast<const uint2*>(pa), a1 = *reinterpret_cast<const uint2*>(pa + 2);
-        const uint2 h0 = *reinterpret_cast<const uint2*>(ph), h1 = *reinterpret_cast<const uint2*>(ph + 2);
-        const uint2 l0 = *reinterpret_cast<const uint2*>(pl), l1 = *reinterpret_cast<const uint2*>(pl + 2);
-        const uint4 av = {a0.x, a0.y, a1.x, a1.y}, hv = {h0.x, h0.y, h1.x, h1.y}, lv = {l0.x, l0.y, l1.x, l1.y};
-        bf16x8_t A, Bh, Bl;
-        __builtin_memcpy(&A, &av, 16);
-        __builtin_memcpy(&Bh, &hv, 16);
-        __builtin_memcpy(&Bl, &lv, 16);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bh, acc[t], 0, 0, 0);
-        if (a.mode == KVM_FUSE_MEM) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bl, acc[t], 0, 0, 0);
-      }
-    }
-    __syncthreads();
   }
-  if (!fuse) return;
 
   // partial state of this chunk -> workspace
   float* pm = a.partM + (pair * a.n_chunks + c) * (size_t)(D * D);
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int tile = wave * TPW + t;
-    const int ti = tile / NT, tj = tile % NT;
+  for (int x = 0; x < NTI; ++x)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = ti * 32 + 8 * (j / 4) + 4 * (lane / 32) + (j % 4);
-      const int col = tj * 32 + (lane & 31);
-      pm[r * D + col] = acc[t][j];
+    for (int y = 0; y < NTJ; ++y) {
+      const int ti = wi * NTI + x, tj = wj * NTJ + y;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = ti * 32 + 8 * (j / 4) + 4 * (lane / 32) + (j % 4);
+        const int col = tj * 32 + (lane & 31);
+        pm[r * D + col] = acc[x * NTJ + y][j];
+      }
     }
-  }
   // vector sums: threads sharing db reduce over their token pairs
   float* pv = a.partv + (pair * a.n_chunks + c) * (size_t)(2 * D);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float x0 = vacc0[e], x1 = vacc1[e];
-    x0 = group_sum<PAIRS_PER_PASS>(x0);
-    x1 = group_sum<PAIRS_PER_PASS>(x1);
-    if (tp == 0 && loader) { pv[db * 8 + e] = x0; pv[D + db * 8 + e] = x1; }
+    x0 = group_sum<PAIRS>(x0);
+    x1 = group_sum<PAIRS>(x1);
+    if (pr == 0 && loader) { pv[db * 8 + e] = x0; pv[D + db * 8 + e] = x1; }
   }
   if (tid == 0) s_n = 0;
   __syncthreads();
   if (db == 0 && nloc) atomicAdd(&s_n, nloc);
   __syncthreads();
   if (tid == 0) a.partn[pair * a.n_chunks + c] = s_n;
-  if (!last_block_ticket(a.counters + pair, a.n_chunks, &s_flag)) return;
-  compact_finish<D>(a, pair);
 }
 
 // ------------------------------------------------------------------ fp32: FMA
@@ -249,13 +342,10 @@ __global__ __launch_bounds__(256) void compact_f32_kernel(CompactArgs a) {
   const size_t pair = (size_t)bb * a.H_kv + g;
   __shared__ double sv[kTok][D];
   __shared__ double su[kTok][D];
-  __shared__ int s_flag, s_cnt;
+  __shared__ int s_cnt;
   const float* Kb = reinterpret_cast<const float*>(a.K) + bb * a.batch_stride + g * a.head_stride;
   const float* Vb = reinterpret_cast<const float*>(a.V) + bb * a.batch_stride + g * a.head_stride;
   const int32_t* smr = a.slot_map + (a.per_head ? pair : (size_t)bb) * a.L;
-  float* Kcb = a.Kc ? reinterpret_cast<float*>(a.Kc) + pair * a.cap * D : nullptr;
-  float* Vcb = a.Vc ? reinterpret_cast<float*>(a.Vc) + pair * a.cap * D : nullptr;
-  const bool fuse = a.mode != 0;
   double acc[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; ++i) acc[i] = 0.0;
@@ -270,10 +360,7 @@ __global__ __launch_bounds__(256) void compact_f32_kernel(CompactArgs a) {
         const float kv = Kb[t * a.tok_stride + dd];
         const float vf = Vb[t * a.tok_stride + dd];
         const int s = smr[t];
-        if (s >= 0) {
-          if (Kcb) Kcb[(size_t)s * D + dd] = kv;
-          if (Vcb) Vcb[(size_t)dd * a.cap + s] = vf;
-        } else if (fuse) {
+        if (s < 0) {
           vv = vf;
           if (a.mode == KVM_FUSE_MEM) {
             const int e = a.n_ev + s;  // n - rank
@@ -288,7 +375,6 @@ __global__ __launch_bounds__(256) void compact_f32_kernel(CompactArgs a) {
       sv[tt][dd] = vv;
       su[tt][dd] = u;
     }
-    if (!fuse) continue;
     __syncthreads();
     if (tid < D) {
       for (int tt = 0; tt < kTok; ++tt) { v0 += su[tt][tid]; v1 += sv[tt][tid]; }
@@ -302,7 +388,6 @@ __global__ __launch_bounds__(256) void compact_f32_kernel(CompactArgs a) {
     }
     __syncthreads();
   }
-  if (!fuse) return;
   float* pm = a.partM + (pair * a.n_chunks + c) * (size_t)(D * D);
 #pragma unroll
   for (int i = 0; i < EPT; ++i) pm[tid + i * 256] = (float)acc[i];
@@ -313,8 +398,63 @@ __global__ __launch_bounds__(256) void compact_f32_kernel(CompactArgs a) {
   if (cnt) atomicAdd(&s_cnt, cnt);
   __syncthreads();
   if (tid == 0) a.partn[pair * a.n_chunks + c] = s_cnt;
-  if (!last_block_ticket(a.counters + pair, a.n_chunks, &s_flag)) return;
-  compact_finish<D>(a, pair);
+}
+
+// ------------------------------------------------------------------ kept-row gather (A5)
+// Kept rows into the caches: slot s of row r holds position idx[r, s].  grid
+// (ceil(keep / 64), H_kv, b), 256 threads; a block moves 64 slots.  K rows are copied in
+// 16-byte pieces; V rows are transposed through LDS so that each dim row of the dim-major
+// V cache is written as one contiguous run of 64 slots.
+struct GatherArgs {
+  const void* K;
+  const void* V;
+  const int32_t* idx;
+  void* Kc;
+  void* Vc;
+  int L, H_kv, cap, keep, per_head;
+  long long tok_stride, head_stride, batch_stride;  // elements
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gather_kv_kernel(GatherArgs a) {
+  constexpr int E16 = 16 / (int)sizeof(T);   // elements per 16-byte piece
+  constexpr int C16 = D / E16;               // pieces per row
+  constexpr int SP = 64 + 4 / (int)sizeof(T); // LDS pitch (elements): odd word stride
+  const int g = blockIdx.y, bb = blockIdx.z, tid = threadIdx.x;
+  const size_t pair = (size_t)bb * a.H_kv + g;
+  const int s0 = blockIdx.x * 64;
+  const int ns = min(64, a.keep - s0);
+  __shared__ T sVt[D * SP];
+  __shared__ int sPos[64];
+  const int32_t* ix = a.idx + (a.per_head ? pair : (size_t)bb) * a.keep + s0;
+  if (tid < ns) {
+    const int t = ix[tid];
+    sPos[tid] = (t >= 0 && t < a.L) ? t : -1;   // an out-of-range index copies nothing
+  }
+  __syncthreads();
+  const T* Kb = reinterpret_cast<const T*>(a.K) + bb * a.batch_stride + g * a.head_stride;
+  const T* Vb = reinterpret_cast<const T*>(a.V) + bb * a.batch_stride + g * a.head_stride;
+  T* Kcb = reinterpret_cast<T*>(a.Kc) + (pair * a.cap + s0) * D;
+  T* Vcb = reinterpret_cast<T*>(a.Vc) + pair * a.cap * D + s0;
+  for (int i = tid; i < ns * C16; i += 256) {
+    const int sl = i / C16, cc = i % C16;
+    const int t = sPos[sl];
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (t >= 0) {
+      kv = *reinterpret_cast<const uint4*>(Kb + t * a.tok_stride + cc * E16);
+      vv = *reinterpret_cast<const uint4*>(Vb + t * a.tok_stride + cc * E16);
+    }
+    *reinterpret_cast<uint4*>(Kcb + (size_t)sl * D + cc * E16) = kv;
+    T ve[E16];
+    __builtin_memcpy(ve, &vv, 16);
+#pragma unroll
+    for (int e = 0; e < E16; ++e) sVt[(cc * E16 + e) * SP + sl] = ve[e];
+  }
+  __syncthreads();
+  for (int i = tid; i < D * 64; i += 256) {
+    const int dim = i / 64, sl = i % 64;
+    if (sl < ns) Vcb[(size_t)dim * a.cap + sl] = sVt[dim * SP + sl];
+  }
 }
 
 // ------------------------------------------------------------------ side-data gather
@@ -399,21 +539,20 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
   }
 }
 
-struct CompactWs { size_t cnt, M, v, n, total; };
+struct CompactWs { size_t M, v, n, total; };
 static int compact_chunk(const kvm_compact_desc* d) {
-  // ~4 chunks per (sequence, KV head) for long rows, whole row for short ones
-  int ch = (d->L + 3) / 4;
-  ch = std::max(ch, 1024);
-  ch = (ch + kTok - 1) / kTok * kTok;
-  return ch;
+  // 2048-token chunks: enough blocks to fill the chip at 16K tokens x 64 (sequence, KV head)
+  // pairs while keeping the fp32 partial states (d*d floats per chunk) near a tenth of the
+  // K/V bytes read
+  (void)d;
+  return 2048;
 }
 static CompactWs compact_ws(const kvm_compact_desc* d) {
   const size_t pairs = (size_t)d->b * d->H_kv;
   const int ch = compact_chunk(d);
   const size_t nc = (d->L + ch - 1) / ch;
   CompactWs w;
-  w.cnt = 0;
-  w.M = kCounterBytes;
+  w.M = 0;
   w.v = align_up(w.M + pairs * nc * d->d * d->d * sizeof(float), 256);
   w.n = align_up(w.v + pairs * nc * 2 * d->d * sizeof(float), 256);
   w.total = align_up(w.n + pairs * nc * sizeof(int), 256);
@@ -430,7 +569,8 @@ extern "C" size_t kvm_compact_workspace_size(const kvm_compact_desc* d) {
 }
 
 extern "C" kvm_status kvm_compact_kv(const kvm_compact_desc* d, const void* K, const void* V,
-                                     const int32_t* slot_map, void* Kc, void* Vc, float* M, float* bvec,
+                                     const int32_t* slot_map, const int32_t* idx, void* Kc, void* Vc,
+                                     float* M, float* bvec,
                                      int32_t* n_e, float* s_k, float* s_v, float* S, void* ws,
                                      size_t ws_bytes, void* stream) {
   KVM_PTR(d);
@@ -443,13 +583,15 @@ extern "C" kvm_status kvm_compact_kv(const kvm_compact_desc* d, const void* K, c
   KVM_REQUIRE(d->lam >= 0.f && d->lam <= 1.f, KVM_ERR_RANGE, "lam %g outside [0, 1]", d->lam);
   KVM_REQUIRE((Kc == nullptr) == (Vc == nullptr), KVM_ERR_NULL, "Kc and Vc must both be given or both NULL");
   KVM_REQUIRE(Kc == nullptr || d->cap >= d->keep, KVM_ERR_RANGE, "cap %d below keep %d", d->cap, d->keep);
-  KVM_PTR_ALIGNED(K); KVM_PTR_ALIGNED(V); KVM_PTR_ALIGNED(slot_map);
+  KVM_REQUIRE(Kc == nullptr || idx != nullptr, KVM_ERR_NULL, "idx is required to fill the caches");
+  KVM_PTR_ALIGNED(K); KVM_PTR_ALIGNED(V);
+  if (d->flags) KVM_PTR_ALIGNED(slot_map);
   KVM_OPT_ALIGNED(Kc); KVM_OPT_ALIGNED(Vc);
+  if (Kc) KVM_PTR_ALIGNED(idx);
   if (d->flags == KVM_FUSE_MEM) { KVM_PTR_ALIGNED(M); KVM_PTR_ALIGNED(bvec); }
   if (d->flags == KVM_FUSE_MOMENTS) {
     KVM_PTR_ALIGNED(n_e); KVM_PTR_ALIGNED(s_k); KVM_PTR_ALIGNED(s_v); KVM_PTR_ALIGNED(S);
   }
-  KVM_REQUIRE((size_t)d->b * d->H_kv <= (size_t)kMaxCounters, KVM_ERR_SHAPE, "b * H_kv exceeds %d", kMaxCounters);
   const CompactWs w = compact_ws(d);
   if (d->flags) {
     KVM_REQUIRE(ws != nullptr && ws_bytes >= w.total, KVM_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
@@ -458,39 +600,62 @@ extern "C" kvm_status kvm_compact_kv(const kvm_compact_desc* d, const void* K, c
   kvm_status st = require_gfx950();
   if (st != KVM_OK) return st;
 
-  CompactArgs a{};
-  a.K = K; a.V = V; a.slot_map = slot_map; a.Kc = Kc; a.Vc = Vc;
-  if (d->flags == KVM_FUSE_MEM) { a.M = M; a.vec0 = bvec; }
-  if (d->flags == KVM_FUSE_MOMENTS) { a.M = S; a.vec0 = s_k; a.vec1 = s_v; a.n_e = n_e; }
-  char* base = static_cast<char*>(ws);
+  long long tok_stride, head_stride, batch_stride;
+  if (d->kv_head_major) {
+    tok_stride = d->d; head_stride = (long long)d->L * d->d; batch_stride = (long long)d->H_kv * d->L * d->d;
+  } else {
+    tok_stride = (long long)d->H_kv * d->d; head_stride = d->d; batch_stride = (long long)d->L * d->H_kv * d->d;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = d->dtype == KVM_BF16;
   if (d->flags) {
-    a.counters = reinterpret_cast<int*>(base + w.cnt);
+    CompactArgs a{};
+    a.K = K; a.V = V; a.slot_map = slot_map;
+    if (d->flags == KVM_FUSE_MEM) { a.M = M; a.vec0 = bvec; }
+    if (d->flags == KVM_FUSE_MOMENTS) { a.M = S; a.vec0 = s_k; a.vec1 = s_v; a.n_e = n_e; }
+    char* base = static_cast<char*>(ws);
     a.partM = reinterpret_cast<float*>(base + w.M);
     a.partv = reinterpret_cast<float*>(base + w.v);
     a.partn = reinterpret_cast<int*>(base + w.n);
+    a.L = d->L; a.H_kv = d->H_kv; a.per_head = d->per_head;
+    a.n_ev = d->L - d->keep;
+    a.chunk = compact_chunk(d);
+    a.n_chunks = (d->L + a.chunk - 1) / a.chunk;
+    a.tok_stride = tok_stride; a.head_stride = head_stride; a.batch_stride = batch_stride;
+    a.mode = d->flags;
+    a.lam_zero = d->lam == 0.f;
+    a.log2lam = d->lam > 0.f ? (float)log2((double)d->lam) : 0.f;
+    a.log2lam_d = d->lam > 0.f ? log2((double)d->lam) : 0.0;
+    a.lam_n = (float)pow((double)d->lam, (double)a.n_ev);
+    const dim3 grid(a.n_chunks, d->H_kv, d->b);
+    const bool mem = d->flags == KVM_FUSE_MEM;
+    if (bf) {
+      if (d->d == 128) {
+        if (mem) hipLaunchKernelGGL((compact_mfma_kernel<128, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((compact_mfma_kernel<128, false>), grid, dim3(256), 0, s, a);
+      } else {
+        if (mem) hipLaunchKernelGGL((compact_mfma_kernel<64, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((compact_mfma_kernel<64, false>), grid, dim3(256), 0, s, a);
+      }
+    } else {
+      if (d->d == 128) hipLaunchKernelGGL(compact_f32_kernel<128>, grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL(compact_f32_kernel<64>, grid, dim3(256), 0, s, a);
+    }
+    const int E = d->d * d->d + 2 * d->d + 1;
+    const dim3 rgrid((E + 1023) / 1024, d->b * d->H_kv);
+    if (d->d == 128) hipLaunchKernelGGL(compact_reduce_kernel<128>, rgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(compact_reduce_kernel<64>, rgrid, dim3(256), 0, s, a);
   }
-  a.L = d->L; a.H_kv = d->H_kv; a.cap = d->cap; a.per_head = d->per_head;
-  a.n_ev = d->L - d->keep;
-  a.chunk = compact_chunk(d);
-  a.n_chunks = (d->L + a.chunk - 1) / a.chunk;
-  if (d->kv_head_major) {
-    a.tok_stride = d->d; a.head_stride = (long long)d->L * d->d; a.batch_stride = (long long)d->H_kv * d->L * d->d;
-  } else {
-    a.tok_stride = (long long)d->H_kv * d->d; a.head_stride = d->d; a.batch_stride = (long long)d->L * d->H_kv * d->d;
-  }
-  a.mode = d->flags;
-  a.lam_zero = d->lam == 0.f;
-  a.log2lam = d->lam > 0.f ? (float)log2((double)d->lam) : 0.f;
-  a.log2lam_d = d->lam > 0.f ? log2((double)d->lam) : 0.0;
-  a.lam_n = (float)pow((double)d->lam, (double)a.n_ev);
-  dim3 grid(a.n_chunks, d->H_kv, d->b);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d->dtype == KVM_BF16) {
-    if (d->d == 128) hipLaunchKernelGGL(compact_mfma_kernel<128>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(compact_mfma_kernel<64>, grid, dim3(256), 0, s, a);
-  } else {
-    if (d->d == 128) hipLaunchKernelGGL(compact_f32_kernel<128>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(compact_f32_kernel<64>, grid, dim3(256), 0, s, a);
+  if (Kc && d->keep > 0) {
+    GatherArgs ga{K, V, idx, Kc, Vc, d->L, d->H_kv, d->cap, d->keep, d->per_head, tok_stride, head_stride, batch_stride};
+    const dim3 grid((d->keep + 63) / 64, d->H_kv, d->b);
+    if (bf) {
+      if (d->d == 128) hipLaunchKernelGGL((gather_kv_kernel<uint16_t, 128>), grid, dim3(256), 0, s, ga);
+      else hipLaunchKernelGGL((gather_kv_kernel<uint16_t, 64>), grid, dim3(256), 0, s, ga);
+    } else {
+      if (d->d == 128) hipLaunchKernelGGL((gather_kv_kernel<float, 128>), grid, dim3(256), 0, s, ga);
+      else hipLaunchKernelGGL((gather_kv_kernel<float, 64>), grid, dim3(256), 0, s, ga);
+    }
   }
   return check_hip(hipGetLastError(), "compact kernel launch");
 }

@@ -596,7 +596,7 @@ static DecodeWs decode_ws(const kvm_decode_desc* d, int ns) {
   const int G = d->H_q / d->H_kv;
   const size_t pairs = (size_t)d->b * d->H_kv;
   DecodeWs w;
-  w.a = kCounterBytes;
+  w.a = 0;
   w.lse = align_up(w.a + pairs * ns * G * d->d * sizeof(float), 256);
   w.num = align_up(w.lse + pairs * ns * G * sizeof(float), 256);
   w.red = align_up(w.num + pairs * G * d->d * sizeof(float), 256);
@@ -660,7 +660,6 @@ extern "C" kvm_status kvm_decode_attn_mem(const kvm_decode_desc* d, const void* 
   if (d->mode == KVM_READ_MOMENTS) {
     KVM_PTR_ALIGNED(n_e); KVM_PTR_ALIGNED(s_k); KVM_PTR_ALIGNED(s_v); KVM_PTR_ALIGNED(S);
   }
-  KVM_REQUIRE((size_t)d->b * d->H_kv <= (size_t)kMaxCounters, KVM_ERR_SHAPE, "b * H_kv exceeds %d", kMaxCounters);
   const int ns = auto_split(d);
   const DecodeWs w = decode_ws(d, ns);
   KVM_REQUIRE(ws != nullptr && ws_bytes >= w.total, KVM_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);

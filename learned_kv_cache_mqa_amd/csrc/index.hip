@@ -34,74 +34,107 @@ struct IndexArgs {
   float* I;
   float* khat;   // [b, L, d_I]
   float* qt;     // [b, W, H_I, d_I]
+  float* gate;   // [b, W, H_I] head gates from the key kernel (matrix-core path), or null
   int b, L, D, H_q, d, H_I, d_I, W;
   float eps;
 };
 
 // ------------------------------------------------------------------ A1: keys, matrix cores
-constexpr int kKpPitch = 36;  // words per LDS row of the W_kI chunk (64 bf16 + 8 pad)
+constexpr int kKpPitch = 36;  // words per LDS row of a weight chunk (64 bf16 + 8 pad)
 
+// Block: 128 tokens (4 waves x 32); outputs = d_I = 64 key dims (2 tiles of 32) plus, in
+// blocks that hold window positions, a third tile with the H_I (<= 32) gate logits
+// W_g[h] . x, so X is read once for both.  X streams through a ring of XS k-steps in
+// registers; the weight chunk of each k-step is staged in LDS (double-buffered).
 __global__ __launch_bounds__(256) void keyproj_mfma_kernel(IndexArgs a) {
-  // block: 128 tokens (4 waves x 32); d_I = 64 outputs (2 tiles of 32)
+  constexpr int XS = 4;   // k-steps of X in flight per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bb = blockIdx.y;
-  const int t0 = blockIdx.x * 128 + wave * 32;
+  const int tb0 = blockIdx.x * 128, t0 = tb0 + wave * 32;
   const int m = lane & 31, kg = lane >> 5;
-  __shared__ uint32_t sW[2][64 * kKpPitch];
+  const bool gate = tb0 + 127 >= a.L - a.W && a.gate != nullptr;   // block-uniform
+  __shared__ uint32_t sW[2][96 * kKpPitch];
   const uint16_t* X = reinterpret_cast<const uint16_t*>(a.X) + (size_t)bb * a.L * a.D;
   const uint16_t* Wk = reinterpret_cast<const uint16_t*>(a.W_kI);
+  const uint16_t* Wg = reinterpret_cast<const uint16_t*>(a.W_g);
   const int tok = min(t0 + m, a.L - 1);        // clamp: rows past L compute garbage, never stored
-  const uint16_t* xrow = X + (size_t)tok * a.D + kg * 32;
+  const uint16_t* xrow = X + (size_t)tok * a.D + kg * 8;   // MFMA j of a k-step: dims j*16 + kg*8 .. +8
 
-  f32x16_t acc0, acc1;
+  f32x16_t acc0, acc1, acc2;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) { acc0[j] = 0.f; acc1[j] = 0.f; }
+  for (int j = 0; j < 16; ++j) { acc0[j] = 0.f; acc1[j] = 0.f; acc2[j] = 0.f; }
 
-  // W chunk: 64 rows x 64 bf16 = 512 uint4; 256 threads x 2
-  const int wrow0 = tid >> 3, wrow1 = (tid + 256) >> 3, wq = tid & 7;
-  const uint16_t* w0p = Wk + (size_t)wrow0 * a.D + wq * 8;
-  const uint16_t* w1p = Wk + (size_t)wrow1 * a.D + wq * 8;
-  uint4 w0 = *reinterpret_cast<const uint4*>(w0p);
-  uint4 w1 = *reinterpret_cast<const uint4*>(w1p);
-  *reinterpret_cast<uint4*>(&sW[0][wrow0 * kKpPitch + wq * 4]) = w0;
-  *reinterpret_cast<uint4*>(&sW[0][wrow1 * kKpPitch + wq * 4]) = w1;
-  uint4 x0 = *reinterpret_cast<const uint4*>(xrow + 0);
-  uint4 x1 = *reinterpret_cast<const uint4*>(xrow + 8);
-  uint4 x2 = *reinterpret_cast<const uint4*>(xrow + 16);
-  uint4 x3 = *reinterpret_cast<const uint4*>(xrow + 24);
-  __syncthreads();
+  // weight chunk rows: 0..63 W_kI, 64..95 W_g (zero beyond H_I); 768 uint4 over 256 threads
+  const int wq = tid & 7;
+  auto wsrc = [&](int i, int k0) -> uint4 {
+    const int row = (tid + i * 256) >> 3;
+    if (row < 64) return *reinterpret_cast<const uint4*>(Wk + (size_t)row * a.D + k0 + wq * 8);
+    if (row - 64 < a.H_I) return *reinterpret_cast<const uint4*>(Wg + (size_t)(row - 64) * a.D + k0 + wq * 8);
+    return make_uint4(0, 0, 0, 0);
+  };
+  const int nwl = gate ? 3 : 2;   // rows in use: 64 or 96
   const int nk = a.D / 64;
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    uint4 n0, n1, n2, n3;
-    const bool more = ks + 1 < nk;
-    if (more) {
-      const int k1 = (ks + 1) * 64;
-      w0 = *reinterpret_cast<const uint4*>(w0p + k1);
-      w1 = *reinterpret_cast<const uint4*>(w1p + k1);
-      n0 = *reinterpret_cast<const uint4*>(xrow + k1 + 0);
-      n1 = *reinterpret_cast<const uint4*>(xrow + k1 + 8);
-      n2 = *reinterpret_cast<const uint4*>(xrow + k1 + 16);
-      n3 = *reinterpret_cast<const uint4*>(xrow + k1 + 24);
-    }
-    const uint4 xr[4] = {x0, x1, x2, x3};
+  // Each block starts its k loop at a different k-step so that the blocks' concurrent X
+  // reads (rows 2*D bytes apart) spread over the HBM channels instead of all hitting the
+  // same column offset at once.
+  const int rot = (int)((blockIdx.x * 7u + blockIdx.y * 13u) % (unsigned)nk);
+  auto kofs = [&](int ks) { int k = ks + rot; return (k >= nk ? k - nk : k) * 64; };
+  // Weight chunks run two k-steps ahead: the chunk of step ks + 2 is loaded at step ks into
+  // one register set while the other set (step ks + 1) is written to the idle LDS buffer.
+  uint4 w[2][3];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8_t A, B0, B1;
-      __builtin_memcpy(&A, &xr[j], 16);
-      const uint4 b0 = *reinterpret_cast<const uint4*>(&sW[buf][m * kKpPitch + kg * 16 + j * 4]);
-      const uint4 b1 = *reinterpret_cast<const uint4*>(&sW[buf][(32 + m) * kKpPitch + kg * 16 + j * 4]);
-      __builtin_memcpy(&B0, &b0, 16);
-      __builtin_memcpy(&B1, &b1, 16);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B1, acc1, 0, 0, 0);
+  for (int h = 0; h < 2; ++h) w[h][0] = w[h][1] = w[h][2] = make_uint4(0, 0, 0, 0);
+  auto wload = [&](int h, int ks) {
+    const int k = kofs(ks);
+    w[h][0] = wsrc(0, k); w[h][1] = wsrc(1, k); if (nwl == 3) w[h][2] = wsrc(2, k);
+  };
+  auto wstore = [&](int h, int buf) {
+    *reinterpret_cast<uint4*>(&sW[buf][((tid) >> 3) * kKpPitch + wq * 4]) = w[h][0];
+    *reinterpret_cast<uint4*>(&sW[buf][((tid + 256) >> 3) * kKpPitch + wq * 4]) = w[h][1];
+    if (nwl == 3) *reinterpret_cast<uint4*>(&sW[buf][((tid + 512) >> 3) * kKpPitch + wq * 4]) = w[h][2];
+  };
+  wload(0, 0);
+  if (nk > 1) wload(1, 1);
+  wstore(0, 0);
+
+  uint4 xr[XS][4];
+#pragma unroll
+  for (int st = 0; st < XS; ++st)
+    if (st < nk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[st][i] = *reinterpret_cast<const uint4*>(xrow + kofs(st) + i * 16);
+  __syncthreads();
+  static_assert(XS % 2 == 0, "register set of a step follows from st");
+  for (int k0 = 0; k0 < nk; k0 += XS) {
+#pragma unroll
+    for (int st = 0; st < XS; ++st) {
+      const int ks = k0 + st;
+      if (ks >= nk) break;
+      const int buf = st & 1;   // == ks & 1
+      if (ks + 2 < nk) wload(st & 1, ks + 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8_t A, B0, B1, B2;
+        __builtin_memcpy(&A, &xr[st][j], 16);
+        const uint4 b0 = *reinterpret_cast<const uint4*>(&sW[buf][m * kKpPitch + j * 8 + kg * 4]);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(&sW[buf][(32 + m) * kKpPitch + j * 8 + kg * 4]);
+        __builtin_memcpy(&B0, &b0, 16);
+        __builtin_memcpy(&B1, &b1, 16);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B1, acc1, 0, 0, 0);
+        if (gate) {
+          const uint4 b2 = *reinterpret_cast<const uint4*>(&sW[buf][(64 + m) * kKpPitch + j * 8 + kg * 4]);
+          __builtin_memcpy(&B2, &b2, 16);
+          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B2, acc2, 0, 0, 0);
+        }
+      }
+      if (ks + XS < nk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xr[st][i] = *reinterpret_cast<const uint4*>(xrow + kofs(ks + XS) + i * 16);
+      }
+      if (ks + 1 < nk) wstore((st + 1) & 1, buf ^ 1);
+      __syncthreads();
     }
-    if (more) {
-      *reinterpret_cast<uint4*>(&sW[buf ^ 1][wrow0 * kKpPitch + wq * 4]) = w0;
-      *reinterpret_cast<uint4*>(&sW[buf ^ 1][wrow1 * kKpPitch + wq * 4]) = w1;
-      x0 = n0; x1 = n1; x2 = n2; x3 = n3;
-    }
-    __syncthreads();
   }
   // epilogue: lane holds column (output) n = m (tile 0) and 32 + m (tile 1) for 16 rows
   const float g0 = a.gamma_k[m], g1 = a.gamma_k[32 + m];
@@ -116,6 +149,8 @@ __global__ __launch_bounds__(256) void keyproj_mfma_kernel(IndexArgs a) {
     if (t < a.L) {
       kout[(size_t)t * 64 + m] = g0 * acc0[j] * r;
       kout[(size_t)t * 64 + 32 + m] = g1 * acc1[j] * r;
+      if (gate && t >= a.L - a.W && m < a.H_I)
+        a.gate[((size_t)bb * a.W + (t - (a.L - a.W))) * a.H_I + m] = sigmoid_f(acc2[j]);
     }
   }
 }
@@ -147,55 +182,141 @@ __global__ __launch_bounds__(256) void keyproj_valu_kernel(IndexArgs a) {
 }
 
 // ------------------------------------------------------------------ A2: queries and gates
+// Block: QB window queries of one sequence, so every W_g / W_qI element read from L2 serves
+// QB queries.  x and q of the QB queries sit in LDS in their storage type; weights stream
+// in 16-byte vectors (8 bf16 or 4 fp32 per lane).
+constexpr int kQB = 2;
+
 template <typename T>
 __global__ __launch_bounds__(256) void query_kernel(IndexArgs a) {
-  // block: one (sequence, window query)
-  const int s = blockIdx.x, bb = blockIdx.y;
+  constexpr int EPL = Vec16<T>::N;
+  const int s0 = blockIdx.x * kQB, bb = blockIdx.y;
+  const int nq = min(kQB, a.W - s0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   extern __shared__ float smem[];
-  float* sx = smem;                       // [D]
-  float* sq = sx + a.D;                   // [H_q * d]
-  float* sqi = sq + a.H_q * a.d;          // [H_I * d_I]
-  float* sg = sqi + a.H_I * a.d_I;        // [H_I]
-  const int pos = a.L - a.W + s;
-  const T* xs = reinterpret_cast<const T*>(a.X) + ((size_t)bb * a.L + pos) * a.D;
-  const T* qs = reinterpret_cast<const T*>(a.Qwin) + ((size_t)bb * a.W + s) * a.H_q * a.d;
-  for (int i = tid; i < a.D; i += 256) sx[i] = load_scalar<T>(xs + i);
-  for (int i = tid; i < a.H_q * a.d; i += 256) sq[i] = load_scalar<T>(qs + i);
+  float* sqi = smem;                         // [QB][H_I * d_I]
+  float* sg = sqi + kQB * a.H_I * a.d_I;     // [QB][H_I]
+  T* sx = reinterpret_cast<T*>(smem + ((kQB * (a.H_I * a.d_I + a.H_I) + 3) & ~3));   // [QB][D], 16-byte aligned
+  T* sq = sx + kQB * a.D;                    // [QB][H_q * d]
+  const int qd = a.H_q * a.d;
+  for (int j = 0; j < kQB; ++j) {
+    const int s = min(s0 + j, a.W - 1);
+    const T* xs = reinterpret_cast<const T*>(a.X) + ((size_t)bb * a.L + a.L - a.W + s) * a.D;
+    const T* qs = reinterpret_cast<const T*>(a.Qwin) + ((size_t)bb * a.W + s) * qd;
+    for (int i = tid * EPL; i < a.D; i += 256 * EPL)
+      *reinterpret_cast<uint4*>(sx + j * a.D + i) = *reinterpret_cast<const uint4*>(xs + i);
+    for (int i = tid * EPL; i < qd; i += 256 * EPL)
+      *reinterpret_cast<uint4*>(sq + j * qd + i) = *reinterpret_cast<const uint4*>(qs + i);
+  }
   __syncthreads();
-  // gates: one wave per head
+  // gates: one wave per head, lanes over D in 16-byte vectors
   const T* Wg = reinterpret_cast<const T*>(a.W_g);
   for (int h = wave; h < a.H_I; h += 4) {
-    float acc = 0.f;
-    for (int k = lane; k < a.D; k += 64) acc = fmaf(load_scalar<T>(Wg + (size_t)h * a.D + k), sx[k], acc);
-    acc = wave_sum(acc);
-    if (lane == 0) sg[h] = sigmoid_f(acc);
+    float acc[kQB] = {};
+    for (int k = lane * EPL; k < a.D; k += 64 * EPL) {
+      float w[EPL];
+      Vec16<T>::load(Wg + (size_t)h * a.D + k, w);
+#pragma unroll
+      for (int j = 0; j < kQB; ++j) {
+        float xv[EPL];
+        Vec16<T>::load(sx + j * a.D + k, xv);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j] = fmaf(w[e], xv[e], acc[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kQB; ++j) {
+      const float t = wave_sum(acc[j]);
+      if (lane == 0) sg[j * a.H_I + h] = sigmoid_f(t);
+    }
   }
-  // down-projection: 16 lanes per output row of W_qI
+  // down-projection: LPR lanes per W_qI row (16 bytes each), 64 / LPR rows per instruction
   const T* Wq = reinterpret_cast<const T*>(a.W_qI);
-  const int sub = lane & 15, grp = lane >> 4;
+  const int LPR = a.d / EPL;                 // 16 (bf16, d = 128) .. 8 (bf16 d = 64 / f32 d = 128)
+  const int rpi = 64 / LPR;
+  const int sub = lane % LPR, grp = lane / LPR;
   const int nout = a.H_I * a.d_I;
-  for (int o0 = wave * 4; o0 < nout; o0 += 16) {
+  for (int o0 = wave * rpi; o0 < nout; o0 += 4 * rpi) {
     const int o = o0 + grp;
-    float acc = 0.f;
+    float acc[kQB] = {};
     if (o < nout) {
       const int h = o / a.d_I;
       const int c = (h * a.H_q) / a.H_I;
-      const T* wr = Wq + (size_t)o * a.d;
-      for (int k = sub; k < a.d; k += 16) acc = fmaf(load_scalar<T>(wr + k), sq[c * a.d + k], acc);
+      float w[EPL];
+      Vec16<T>::load(Wq + (size_t)o * a.d + sub * EPL, w);
+#pragma unroll
+      for (int j = 0; j < kQB; ++j) {
+        float qv[EPL];
+        Vec16<T>::load(sq + j * qd + c * a.d + sub * EPL, qv);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j] = fmaf(w[e], qv[e], acc[j]);
+      }
     }
-    acc = group_sum<16>(acc);
-    if (o < nout && sub == 0) sqi[o] = acc;
+#pragma unroll
+    for (int j = 0; j < kQB; ++j) {
+      float t = acc[j];
+      for (int msk = 1; msk < LPR; msk <<= 1) t += __shfl_xor(t, msk);
+      if (o < nout && sub == 0) sqi[j * nout + o] = t;
+    }
   }
   __syncthreads();
-  // RMSNorm per head, gate, 1/sqrt(d_I)
+  // RMSNorm per (query, head), gate, 1/sqrt(d_I)
   const float isd = rsqrtf((float)a.d_I);
-  float* out = a.qt + ((size_t)bb * a.W + s) * a.H_I * a.d_I;
-  for (int h = wave; h < a.H_I; h += 4) {
-    const float x = lane < a.d_I ? sqi[h * a.d_I + lane] : 0.f;
+  for (int jh = wave; jh < nq * a.H_I; jh += 4) {
+    const int j = jh / a.H_I, h = jh % a.H_I;
+    const float x = lane < a.d_I ? sqi[j * nout + h * a.d_I + lane] : 0.f;
     const float ss = wave_sum(x * x);
     const float r = rsqrtf(ss / a.d_I + a.eps);
-    if (lane < a.d_I) out[h * a.d_I + lane] = sg[h] * a.gamma_q[lane] * x * r * isd;
+    float* out = a.qt + ((size_t)bb * a.W + s0 + j) * nout;
+    if (lane < a.d_I) out[h * a.d_I + lane] = sg[j * a.H_I + h] * a.gamma_q[lane] * x * r * isd;
+  }
+}
+
+// ------------------------------------------------------------------ A2: queries, matrix cores
+// bf16, d = 128, d_I = 64, W % 32 == 0.  One wave per (sequence, indexer head h): the window
+// queries of model head c(h), Q [W x 128], times W_qI[h]^T [128 x 64] on
+// v_mfma_f32_32x32x16_bf16; then RMSNorm over d_I per query, the gate from the key kernel
+// and 1/sqrt(d_I).
+__global__ __launch_bounds__(256) void query_mfma_kernel(IndexArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.x * 4 + wave, bb = blockIdx.y;
+  if (h >= a.H_I) return;
+  const int m = lane & 31, kg = lane >> 5;
+  const int c = (h * a.H_q) / a.H_I;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Qwin) + (size_t)bb * a.W * a.H_q * 128 + (size_t)c * 128;
+  const uint16_t* Wq = reinterpret_cast<const uint16_t*>(a.W_qI) + (size_t)h * 64 * 128;
+  const float isd = 0.125f;   // 1/sqrt(64)
+  const float gk0 = a.gamma_q[m], gk1 = a.gamma_q[32 + m];
+  for (int mt = 0; mt < a.W / 32; ++mt) {
+    f32x16_t acc0 = {}, acc1 = {};
+    uint4 qa[8], wb0[8], wb1[8];
+    const int s = mt * 32 + m;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qa[j] = *reinterpret_cast<const uint4*>(Q + (size_t)s * a.H_q * 128 + j * 16 + kg * 8);
+      wb0[j] = *reinterpret_cast<const uint4*>(Wq + (size_t)m * 128 + j * 16 + kg * 8);
+      wb1[j] = *reinterpret_cast<const uint4*>(Wq + (size_t)(32 + m) * 128 + j * 16 + kg * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      bf16x8_t A, B0, B1;
+      __builtin_memcpy(&A, &qa[j], 16);
+      __builtin_memcpy(&B0, &wb0[j], 16);
+      __builtin_memcpy(&B1, &wb1[j], 16);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B1, acc1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int sq = mt * 32 + 8 * (j / 4) + 4 * kg + (j % 4);
+      float ss = acc0[j] * acc0[j] + acc1[j] * acc1[j];
+      ss = group_sum<32>(ss);
+      const float r = rsqrtf(ss * (1.f / 64.f) + a.eps);
+      const float gt = a.gate[((size_t)bb * a.W + sq) * a.H_I + h];
+      float* out = a.qt + (((size_t)bb * a.W + sq) * a.H_I + h) * 64;
+      out[m] = gt * gk0 * acc0[j] * r * isd;
+      out[32 + m] = gt * gk1 * acc1[j] * r * isd;
+    }
   }
 }
 
@@ -321,12 +442,13 @@ __global__ __launch_bounds__(256) void score_valu_kernel(IndexArgs a) {
   if (t < a.L) a.I[(size_t)bb * a.L + t] = best;
 }
 
-struct IndexWs { size_t kh, qt, total; };
+struct IndexWs { size_t kh, qt, gate, total; };
 static IndexWs index_ws(const kvm_index_desc* d) {
   IndexWs w;
-  w.kh = kCounterBytes;
+  w.kh = 0;
   w.qt = align_up(w.kh + (size_t)d->b * d->L * d->d_I * sizeof(float), 256);
-  w.total = align_up(w.qt + (size_t)d->b * d->W * d->H_I * d->d_I * sizeof(float), 256);
+  w.gate = align_up(w.qt + (size_t)d->b * d->W * d->H_I * d->d_I * sizeof(float), 256);
+  w.total = align_up(w.gate + (size_t)d->b * d->W * d->H_I * sizeof(float), 256);
   return w;
 }
 
@@ -356,7 +478,9 @@ extern "C" kvm_status kvm_index_score(const kvm_index_desc* d, const void* X, co
   const IndexWs w = index_ws(d);
   KVM_REQUIRE(ws != nullptr && ws_bytes >= w.total, KVM_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
   KVM_ALIGNED(ws);
-  const size_t qsmem = (size_t)(d->D + d->H_q * d->d + d->H_I * d->d_I + d->H_I) * sizeof(float);
+  const size_t esz = d->dtype == KVM_BF16 ? 2 : 4;
+  const size_t qsmem = (size_t)((kQB * (d->H_I * d->d_I + d->H_I) + 3) & ~3) * sizeof(float) +
+                       (size_t)kQB * (d->D + d->H_q * d->d) * esz;
   KVM_REQUIRE(qsmem <= 64 * 1024, KVM_ERR_SHAPE, "D + H_q*d too large for the query kernel");
   kvm_status st = require_gfx950();
   if (st != KVM_OK) return st;
@@ -371,16 +495,22 @@ extern "C" kvm_status kvm_index_score(const kvm_index_desc* d, const void* X, co
   a.eps = d->eps_rms;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = d->dtype == KVM_BF16;
-  if (bf && d->d_I == 64 && d->D % 64 == 0)
+  // matrix-core path: bf16, d_I = 64, H_I <= 32, d = 128, D % 64 == 0, W % 32 == 0
+  const bool mfma = bf && d->d_I == 64 && d->H_I <= 32 && d->d == 128 && d->D % 64 == 0 && d->W % 32 == 0;
+  a.gate = mfma ? reinterpret_cast<float*>(base + w.gate) : nullptr;
+  if (mfma)
     hipLaunchKernelGGL(keyproj_mfma_kernel, dim3((d->L + 127) / 128, d->b), dim3(256), 0, s, a);
   else if (bf)
     hipLaunchKernelGGL(keyproj_valu_kernel<uint16_t>, dim3((d->L + 15) / 16, d->b), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(keyproj_valu_kernel<float>, dim3((d->L + 15) / 16, d->b), dim3(256), 0, s, a);
-  if (bf)
-    hipLaunchKernelGGL(query_kernel<uint16_t>, dim3(d->W, d->b), dim3(256), qsmem, s, a);
+  const dim3 qgrid((d->W + kQB - 1) / kQB, d->b);
+  if (mfma)
+    hipLaunchKernelGGL(query_mfma_kernel, dim3((d->H_I + 3) / 4, d->b), dim3(256), 0, s, a);
+  else if (bf)
+    hipLaunchKernelGGL(query_kernel<uint16_t>, qgrid, dim3(256), qsmem, s, a);
   else
-    hipLaunchKernelGGL(query_kernel<float>, dim3(d->W, d->b), dim3(256), qsmem, s, a);
+    hipLaunchKernelGGL(query_kernel<float>, qgrid, dim3(256), qsmem, s, a);
   if (d->H_I == 32 && d->d_I == 64)
     hipLaunchKernelGGL(score_mfma_kernel, dim3((d->L + 511) / 512, d->b), dim3(512), 0, s, a);
   else

@@ -74,7 +74,7 @@ def test_prefill_end_to_end(cfg):
     cap = api.cache_cap(keep + cfg.T)
     M = torch.zeros((cfg.b, cfg.H_kv, cfg.d, cfg.d), dtype=torch.float32, device="cuda")
     bv = torch.zeros((cfg.b, cfg.H_kv, cfg.d), dtype=torch.float32, device="cuda")
-    Kc, Vc = api.kvm_compact_kv(Kt, Vt, sm, keep, cap, M=M, bvec=bv, lam=lam)
+    Kc, Vc = api.kvm_compact_kv(Kt, Vt, sm, idx, keep, cap, M=M, bvec=bv, lam=lam)
     torch.cuda.synchronize()
     f = lambda x: gen.from_storage(x, cfg.dtype)
     for i in range(cfg.b):

@@ -82,7 +82,9 @@ def test_compact_and_memory_build(dtype, b, L, H, d, B, R, lam, extra):
     from tests.gpu_util import to_dev, to_np, assert_output, normwise, maxabs
     Kt, Vt = _kv(dtype, b, L, H, d, seed=L + d)
     I = _scores(b, L, seed=L)
-    smaps = [im.topk_select(I[i].astype(np.float64), B, R)[1] for i in range(b)]
+    sel = [im.topk_select(I[i].astype(np.float64), B, R) for i in range(b)]
+    smaps = [x[1] for x in sel]
+    idxs = np.stack([x[0] for x in sel]).astype(np.int32)
     keep = L - int((smaps[0] < 0).sum())
     cap = keep + extra
     rM = gen.rng(92, L, 0, 0)
@@ -90,7 +92,7 @@ def test_compact_and_memory_build(dtype, b, L, H, d, B, R, lam, extra):
     b0 = np.abs(rM.standard_normal((b, H, d))).astype(np.float32)
     M = to_dev(M0.copy())
     bv = to_dev(b0.copy())
-    Kc, Vc = api.kvm_compact_kv(to_dev(Kt), to_dev(Vt), to_dev(np.stack(smaps).astype(np.int32)), keep, cap,
+    Kc, Vc = api.kvm_compact_kv(to_dev(Kt), to_dev(Vt), to_dev(np.stack(smaps).astype(np.int32)), to_dev(idxs), keep, cap,
                                 M=M, bvec=bv, lam=lam)
     torch.cuda.synchronize()
     gK, gV, gM, gb = to_np(Kc), to_np(Vc), to_np(M), to_np(bv)
@@ -120,14 +122,16 @@ def test_moment_update_per_head(head_major):
     if head_major:
         Kt, Vt = np.ascontiguousarray(Kt.transpose(0, 2, 1, 3)), np.ascontiguousarray(Vt.transpose(0, 2, 1, 3))
     I = _scores(b * H, L, seed=9)
-    smaps = np.stack([im.topk_select(I[r].astype(np.float64), keep, 0)[1] for r in range(b * H)]).astype(np.int32)
+    sel = [im.topk_select(I[r].astype(np.float64), keep, 0) for r in range(b * H)]
+    smaps = np.stack([x[1] for x in sel]).astype(np.int32)
+    idxs = np.stack([x[0] for x in sel]).astype(np.int32)
     r0 = gen.rng(93, 0, 0, 0)
     n0 = np.full((b, H), 17, np.int32)
     sk0, sv0 = r0.standard_normal((b, H, d)).astype(np.float32), r0.standard_normal((b, H, d)).astype(np.float32)
     S0 = r0.standard_normal((b, H, d, d)).astype(np.float32)
     mom = dict(n_e=to_dev(n0.copy()), s_k=to_dev(sk0.copy()), s_v=to_dev(sv0.copy()), S=to_dev(S0.copy()))
-    Kc, Vc = api.kvm_compact_kv(to_dev(Kt), to_dev(Vt), to_dev(smaps), keep, keep + 5, moments=mom, per_head=True,
-                                kv_head_major=head_major)
+    Kc, Vc = api.kvm_compact_kv(to_dev(Kt), to_dev(Vt), to_dev(smaps), to_dev(idxs), keep, keep + 5, moments=mom,
+                                per_head=True, kv_head_major=head_major)
     torch.cuda.synchronize()
     Kd, Vd = gen.from_storage(Kt, "bf16"), gen.from_storage(Vt, "bf16")
     gK = to_np(Kc)
