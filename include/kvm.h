@@ -179,7 +179,7 @@ kvm_status kvm_gather_rows(int32_t rows, int32_t L, int32_t cap, int32_t elem_by
  *   M <- lam^r M + sum_i lam^(r-i) v_i phi(k_i)^T,  bvec <- lam^r bvec + sum_i lam^(r-i) phi(k_i).
  * K_rows, V_rows: [b, r, H_kv, d] (dtype), or, with row_slot != NULL, r = 1 and the row
  * is taken from the caches Kc [b, H_kv, cap, d] and Vc [b, H_kv, d, cap] at slot
- * row_slot[b] (device i32).
+ * row_slot[b] (device i32); a sequence whose row_slot is outside [0, cap) is left as is.
  * ------------------------------------------------------------------------------------ */
 typedef struct {
   int32_t b, H_kv, d, r, cap;
@@ -189,6 +189,51 @@ typedef struct {
 
 kvm_status kvm_mem_update(const kvm_mem_desc* desc, const void* K_rows, const void* V_rows,
                           const int32_t* row_slot, float* M, float* bvec, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * A7  Streaming eviction step during decode                    [IM 2.A; IM 2.B]
+ *
+ * Each sequence keeps a full pool of P tokens in slots 0..P-1 of the compact caches, with
+ * per slot its position slot_pos, its normalised indexer key khat_pool and its importance
+ * I_pool (initially the gathered prefill outputs: positions idx, khat and I).  For the new
+ * token at position p = next_pos[b] (hidden state x_new, model query q_new):
+ *   1. k_hat_new = RMSNorm_{gamma_k}(W_kI x_new);  q_hat_h, g_h as in kvm_index_score;
+ *      score(k) = sum_h g_h relu(q_hat_h . k / sqrt(d_I));
+ *      I_pool[j] <- max(I_pool[j], score(khat_pool[j])) for every slot; I_new = score(k_hat_new);
+ *   2. candidates: slots with slot_pos <= p - R (the pool's older tokens and the one leaving
+ *      the recent window); e = the candidate with the lowest I_pool, ties evicting the
+ *      higher position (NaN orders as -inf, -0 as +0);
+ *   3. M <- lam M + v_e phi(k_e)^T, bvec <- lam bvec + phi(k_e) per KV head, with the
+ *      evicted row read from Kc [b, H_kv, cap, d] / Vc [b, H_kv, d, cap] at slot e;
+ *   4. slot e takes the new token: slot_pos[e] = p, I_pool[e] = I_new, khat_pool[e] =
+ *      k_hat_new; next_pos[b] = p + 1; evict_slot[b] = e.
+ * The new token's K/V go into slot e with the following kvm_decode_attn_mem call
+ * (append_slot = evict_slot, len = P).  The step order is this library's reading: the
+ * section states that evicted tokens update the memory online during inference.
+ * x_new [b, D], q_new [b, H_q, d] (dtype); W_kI, W_qI, W_g, gamma_k, gamma_q as in
+ * kvm_index_score; khat_pool [b, P, d_I] f32, I_pool [b, P] f32, slot_pos [b, P] i32,
+ * next_pos [b] i32 (read-modify-write); M, bvec as in kvm_mem_update; evict_slot [b] i32
+ * (output; -1 if no slot qualifies, which a pool consistent with step 2 never gives).
+ * Supported: d_I <= 64, H_I <= 64, d in {64, 128}, D % 8 == 0; requires P > R, cap >= P.
+ * Arithmetic: fp32 projections and scores.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t b, D, H_q, H_kv, d;
+  int32_t H_I, d_I;
+  int32_t P;               /* pool slots per sequence (all occupied)                      */
+  int32_t cap;             /* slot capacity of Kc / Vc                                    */
+  int32_t R;               /* recent window                                               */
+  int32_t dtype;           /* kvm_dtype of x_new, q_new, the weights and the caches       */
+  float lam, eps_rms;
+} kvm_stream_desc;
+
+size_t kvm_stream_workspace_size(const kvm_stream_desc* desc);
+kvm_status kvm_stream_evict(const kvm_stream_desc* desc, const void* x_new, const void* q_new,
+                            const void* W_kI, const float* gamma_k, const void* W_qI,
+                            const float* gamma_q, const void* W_g, float* khat_pool, float* I_pool,
+                            int32_t* slot_pos, int32_t* next_pos, const void* Kc, const void* Vc,
+                            float* M, float* bvec, int32_t* evict_slot, void* ws, size_t ws_bytes,
+                            void* stream);
 
 /* ------------------------------------------------------------------------------------ *
  * A8 + A9 / V3  Split-K decode attention with memory read-out          [IM 2.B; ASM; MKV 4]

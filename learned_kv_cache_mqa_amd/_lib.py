@@ -46,7 +46,7 @@ class DecodeDesc(C.Structure):
 
 class StreamDesc(C.Structure):
     _fields_ = [("b", i32), ("D", i32), ("H_q", i32), ("H_kv", i32), ("d", i32), ("H_I", i32),
-                ("d_I", i32), ("cap", i32), ("R", i32), ("dtype", i32), ("lam", f32),
+                ("d_I", i32), ("P", i32), ("cap", i32), ("R", i32), ("dtype", i32), ("lam", f32),
                 ("eps_rms", f32)]
 
 
@@ -75,8 +75,7 @@ SIGNATURES = {
                                       vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     "kvm_len_add": (C.c_int, [vp, i32, i32, vp]),
     "kvm_stream_workspace_size": (sz, [C.POINTER(StreamDesc)]),
-    "kvm_stream_evict": (C.c_int, [C.POINTER(StreamDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                   vp, vp, vp, vp, vp, sz, vp]),
+    "kvm_stream_evict": (C.c_int, [C.POINTER(StreamDesc)] + [vp] * 17 + [sz, vp]),
     "kvm_moment_workspace_size": (sz, [C.POINTER(MScoreDesc)]),
     "kvm_moment_alpha": (C.c_int, [C.POINTER(MScoreDesc), vp, vp, vp, vp, sz, vp]),
     "kvm_moment_score": (C.c_int, [C.POINTER(MScoreDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),

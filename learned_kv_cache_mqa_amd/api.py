@@ -191,3 +191,31 @@ def kvm_index_score(X, Qwin, W_kI, gamma_k, W_qI, gamma_q, W_g, I=None, khat=Non
     check(lib().kvm_index_score(C.byref(desc), _p(X), _p(Qwin), _p(W_kI), _p(gamma_k), _p(W_qI), _p(gamma_q),
                                 _p(W_g), _p(I), _p(khat), _p(ws), ws.numel(), _stream(stream)))
     return I
+
+
+# ------------------------------------------------------------------------------- streaming
+
+def kvm_stream_evict(x_new, q_new, W_kI, gamma_k, W_qI, gamma_q, W_g, khat_pool, I_pool, slot_pos, next_pos,
+                     Kc, Vc, M, bvec, lam, R, evict_slot=None, eps=1e-6, stream=None, ws=None):
+    """One streaming eviction step: pool scoring with the new token's indexer query,
+    running-max importance, eviction of the weakest non-recent slot into (M, bvec) and the
+    slot's hand-over to the new token.  Returns evict_slot [b] i32 (the slot that the next
+    kvm_decode_attn_mem call, with append_slot = evict_slot, fills with the new K/V)."""
+    _contig(x_new, q_new, W_kI, gamma_k, W_qI, gamma_q, W_g, khat_pool, I_pool, slot_pos, next_pos, Kc, Vc, M,
+            bvec, evict_slot)
+    b, D = x_new.shape
+    _, H_q, d = q_new.shape
+    H_I, d_I, _ = W_qI.shape
+    _, P = I_pool.shape
+    _, H_kv, cap, _ = Kc.shape
+    desc = K.StreamDesc(b=b, D=D, H_q=H_q, H_kv=H_kv, d=d, H_I=H_I, d_I=d_I, P=P, cap=cap, R=R,
+                        dtype=_dtype(x_new), lam=lam, eps_rms=eps)
+    if evict_slot is None:
+        evict_slot = torch.empty((b,), dtype=torch.int32, device=x_new.device)
+    nb = lib().kvm_stream_workspace_size(C.byref(desc))
+    if ws is None:
+        ws = workspace(nb, x_new.device, stream, "stream")
+    check(lib().kvm_stream_evict(C.byref(desc), _p(x_new), _p(q_new), _p(W_kI), _p(gamma_k), _p(W_qI), _p(gamma_q),
+                                 _p(W_g), _p(khat_pool), _p(I_pool), _p(slot_pos), _p(next_pos), _p(Kc), _p(Vc),
+                                 _p(M), _p(bvec), _p(evict_slot), _p(ws), ws.numel(), _stream(stream)))
+    return evict_slot

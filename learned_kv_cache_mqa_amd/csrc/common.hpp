@@ -116,6 +116,15 @@ template <int N> __device__ __forceinline__ float group_max(float x) {
 }
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 
+// Order-preserving u32 key of a score (ascending with the value): NaN orders as -inf and
+// -0 as +0, so equal keys mean equal scores.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;  // NaN -> -inf
+  if (u == 0x80000000u) u = 0u;                           // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 __device__ __forceinline__ float sigmoid_f(float x) {
   float e = __expf(-fabsf(x));

@@ -486,6 +486,7 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
   // grid (D*D/1024, H_kv, b): each thread updates 4 consecutive elements of one row
   const int g = blockIdx.y, bb = blockIdx.z;
   const size_t pair = (size_t)bb * a.H_kv + g;
+  if (a.row_slot && (a.row_slot[bb] < 0 || a.row_slot[bb] >= a.cap)) return;   // nothing evicted
   __shared__ float sv[32][D], su[32][D];
   const int e0 = (blockIdx.x * 256 + threadIdx.x) * 4;
   const int row = e0 / D, col = e0 % D;

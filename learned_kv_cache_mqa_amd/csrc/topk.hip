@@ -15,13 +15,6 @@ namespace kvm {
 static constexpr int kTopkThreads = 1024;
 static constexpr int kTopkWaves = kTopkThreads / 64;
 
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;  // NaN -> -inf
-  if (u == 0x80000000u) u = 0u;                           // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 // Exclusive prefix count of `flag` over the block in thread order; returns the prefix and
 // writes the block total to *total.  Uses s_cnt[kTopkWaves + 1].
 __device__ __forceinline__ int block_prefix(bool flag, int* s_cnt, int* total) {
