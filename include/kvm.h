@@ -157,6 +157,8 @@ typedef struct {
   int32_t kv_head_major;   /* layout of K, V                                             */
   int32_t flags;           /* KVM_FUSE_MEM or KVM_FUSE_MOMENTS (or 0: copy only)          */
   float lam;               /* memory decay, 0 <= lam <= 1                                */
+  int32_t v_row_major;     /* 1: Vc [b, H_kv, cap, d] like Kc (input layout for a further
+                              selection round); 0: the dim-major decode layout             */
 } kvm_compact_desc;
 
 size_t kvm_compact_workspace_size(const kvm_compact_desc* desc);
@@ -234,6 +236,58 @@ kvm_status kvm_stream_evict(const kvm_stream_desc* desc, const void* x_new, cons
                             int32_t* slot_pos, int32_t* next_pos, const void* Kc, const void* Vc,
                             float* M, float* bvec, int32_t* evict_slot, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * V1  MomentKV eviction score                                         [MKV part 3]
+ *
+ * Per sequence bb and KV head g (rows r = bb * H_kv + g of alpha and score):
+ *   alpha[r, j] = (1 / (W G)) sum_{s < W} sum_{h in group g} softmax_j(q_{s,h} . k_j * scale),
+ *     the softmax over the keys j <= L - W + s that window query s (position L - W + s) sees;
+ *   score[r, j] = alpha[r, j] * ||r_j||,  r_j = v_j - s_v/n_e - S~ k_j / (n_e sqrt d),
+ *     S~ = S - s_v s_k^T / n_e;  r_j = v_j while n_e = 0.
+ * The attention weight alpha_j as the window- and group-averaged causal softmax mass is
+ * this library's reading of the section's attention weight of token j.
+ * Qwin [b, W, H_q, d]; K, V [b, L, H_kv, d] (kv_head_major = 0) or [b, H_kv, L, d];
+ * alpha, score [b, H_kv, L] f32; moments as in kvm_compact_kv (n_e [b,H_kv] i32, s_k,
+ * s_v [b,H_kv,d], S [b,H_kv,d,d] f32).  kvm_moment_alpha needs the workspace; W G <= 256.
+ * Supported: bf16 inputs, d in {64, 128}.
+ * Arithmetic: logits on the matrix cores from exact bf16 operands with fp32 accumulation;
+ * S~ / (n_e sqrt d) enters the residual as three bf16 terms (~24 bits).
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t b, L, H_q, H_kv, d, W;
+  int32_t dtype;
+  int32_t kv_head_major;
+  float scale;             /* logit scale, 1/sqrt(d)                                      */
+} kvm_moment_desc;
+
+size_t kvm_moment_workspace_size(const kvm_moment_desc* desc);
+kvm_status kvm_moment_alpha(const kvm_moment_desc* desc, const void* Qwin, const void* K, float* alpha,
+                            void* ws, size_t ws_bytes, void* stream);
+kvm_status kvm_moment_score(const kvm_moment_desc* desc, const void* K, const void* V,
+                            const float* alpha, const int32_t* n_e, const float* s_k, const float* s_v,
+                            const float* S, float* score, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * V3  MomentKV read-out from a retained-attention output              [MKV parts 2, 4]
+ *
+ * Per query head h (KV head g = h / G), from the retained output f_R = o_R[b, h] and its
+ * log-partition lse_R[b, h] (natural log, as written by kvm_decode_attn_mem):
+ *   f_E = s_v/n_e + (S q - s_v (s_k . q)/n_e) * scale / n_e;
+ *   log Z_E = log n_e + (q . s_k / n_e) * scale;  w_R = sigmoid(lse_R - log Z_E);
+ *   o = w_R f_R + (1 - w_R) f_E   (o = f_R where n_e = 0).
+ * q [b, H_q, d] (dtype), o_R, o [b, H_q, d] f32, lse_R [b, H_q] f32; moments as above.
+ * kvm_decode_attn_mem with mode KVM_READ_MOMENTS computes the same in its merge step.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t b, H_q, H_kv, d;
+  int32_t dtype;
+  float scale;
+} kvm_mread_desc;
+
+kvm_status kvm_moment_readout(const kvm_mread_desc* desc, const void* q, const float* o_R,
+                              const float* lse_R, const int32_t* n_e, const float* s_k,
+                              const float* s_v, const float* S, float* o, void* stream);
 
 /* ------------------------------------------------------------------------------------ *
  * A8 + A9 / V3  Split-K decode attention with memory read-out          [IM 2.B; ASM; MKV 4]

@@ -31,7 +31,7 @@ class TopkDesc(C.Structure):
 class CompactDesc(C.Structure):
     _fields_ = [("b", i32), ("L", i32), ("H_kv", i32), ("d", i32), ("cap", i32), ("keep", i32),
                 ("dtype", i32), ("per_head", i32), ("kv_head_major", i32), ("flags", i32),
-                ("lam", f32)]
+                ("lam", f32), ("v_row_major", i32)]
 
 
 class MemDesc(C.Structure):
@@ -50,9 +50,13 @@ class StreamDesc(C.Structure):
                 ("eps_rms", f32)]
 
 
-class MScoreDesc(C.Structure):
+class MomentDesc(C.Structure):
     _fields_ = [("b", i32), ("L", i32), ("H_q", i32), ("H_kv", i32), ("d", i32), ("W", i32),
-                ("n", i32), ("dtype", i32), ("scale", f32)]
+                ("dtype", i32), ("kv_head_major", i32), ("scale", f32)]
+
+
+class MReadDesc(C.Structure):
+    _fields_ = [("b", i32), ("H_q", i32), ("H_kv", i32), ("d", i32), ("dtype", i32), ("scale", f32)]
 
 
 # name -> (restype, argtypes); symbols that the header declares
@@ -76,10 +80,10 @@ SIGNATURES = {
     "kvm_len_add": (C.c_int, [vp, i32, i32, vp]),
     "kvm_stream_workspace_size": (sz, [C.POINTER(StreamDesc)]),
     "kvm_stream_evict": (C.c_int, [C.POINTER(StreamDesc)] + [vp] * 17 + [sz, vp]),
-    "kvm_moment_workspace_size": (sz, [C.POINTER(MScoreDesc)]),
-    "kvm_moment_alpha": (C.c_int, [C.POINTER(MScoreDesc), vp, vp, vp, vp, sz, vp]),
-    "kvm_moment_score": (C.c_int, [C.POINTER(MScoreDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
-    "kvm_moment_readout": (C.c_int, [C.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+    "kvm_moment_workspace_size": (sz, [C.POINTER(MomentDesc)]),
+    "kvm_moment_alpha": (C.c_int, [C.POINTER(MomentDesc), vp, vp, vp, vp, sz, vp]),
+    "kvm_moment_score": (C.c_int, [C.POINTER(MomentDesc)] + [vp] * 9),
+    "kvm_moment_readout": (C.c_int, [C.POINTER(MReadDesc)] + [vp] * 9),
 }
 
 

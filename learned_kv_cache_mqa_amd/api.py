@@ -117,7 +117,7 @@ def cache_cap(n):
 
 
 def kvm_compact_kv(Kt, Vt, slot_map, idx, keep, cap=None, Kc=None, Vc=None, M=None, bvec=None, moments=None,
-                   lam=1.0, per_head=False, kv_head_major=False, copy=True, stream=None, ws=None):
+                   lam=1.0, per_head=False, kv_head_major=False, copy=True, v_row_major=False, stream=None, ws=None):
     """Compact kept rows of K, V ([b,L,H_kv,d], or [b,H_kv,L,d] if kv_head_major) into
     Kc [b,H_kv,cap,d] (slot-major) and Vc [b,H_kv,d,cap] (dim-major); fold evicted rows into
     (M, bvec) or into moments dict(n_e, s_k, s_v, S).  slot_map and idx are the two outputs
@@ -130,10 +130,11 @@ def kvm_compact_kv(Kt, Vt, slot_map, idx, keep, cap=None, Kc=None, Vc=None, M=No
     cap = keep if cap is None else cap
     if copy and Kc is None:
         Kc = torch.zeros((b, H_kv, cap, d), dtype=Kt.dtype, device=Kt.device)
-        Vc = torch.zeros((b, H_kv, d, cap), dtype=Vt.dtype, device=Vt.device)
+        vshape = (b, H_kv, cap, d) if v_row_major else (b, H_kv, d, cap)
+        Vc = torch.zeros(vshape, dtype=Vt.dtype, device=Vt.device)
     flags = K.KVM_FUSE_MEM if M is not None else (K.KVM_FUSE_MOMENTS if moments is not None else 0)
     desc = K.CompactDesc(b=b, L=L, H_kv=H_kv, d=d, cap=cap, keep=keep, dtype=_dtype(Kt), per_head=int(per_head),
-                         kv_head_major=int(kv_head_major), flags=flags, lam=lam)
+                         kv_head_major=int(kv_head_major), flags=flags, lam=lam, v_row_major=int(v_row_major))
     nb = lib().kvm_compact_workspace_size(C.byref(desc))
     if ws is None:
         ws = workspace(nb, Kt.device, stream, "compact")
@@ -219,3 +220,56 @@ def kvm_stream_evict(x_new, q_new, W_kI, gamma_k, W_qI, gamma_q, W_g, khat_pool,
                                  _p(W_g), _p(khat_pool), _p(I_pool), _p(slot_pos), _p(next_pos), _p(Kc), _p(Vc),
                                  _p(M), _p(bvec), _p(evict_slot), _p(ws), ws.numel(), _stream(stream)))
     return evict_slot
+
+
+# ------------------------------------------------------------------------------- MomentKV
+
+def _moment_desc(K_, H_q, W, kv_head_major, scale):
+    if kv_head_major:
+        b, H_kv, L, d = K_.shape
+    else:
+        b, L, H_kv, d = K_.shape
+    return K.MomentDesc(b=b, L=L, H_q=H_q, H_kv=H_kv, d=d, W=W, dtype=_dtype(K_), kv_head_major=int(kv_head_major),
+                        scale=(1.0 / math.sqrt(d)) if scale is None else scale)
+
+
+def kvm_moment_alpha(Qwin, K_, kv_head_major=False, alpha=None, scale=None, stream=None, ws=None):
+    """alpha [b, H_kv, L] f32: the causal softmax weight of each key averaged over the window
+    queries Qwin [b, W, H_q, d] (positions L-W..L-1) and the query heads of its KV group."""
+    _contig(Qwin, K_, alpha)
+    _, W, H_q, _ = Qwin.shape
+    desc = _moment_desc(K_, H_q, W, kv_head_major, scale)
+    if alpha is None:
+        alpha = torch.empty((desc.b, desc.H_kv, desc.L), dtype=torch.float32, device=K_.device)
+    nb = lib().kvm_moment_workspace_size(C.byref(desc))
+    if ws is None:
+        ws = workspace(nb, K_.device, stream, "moment")
+    check(lib().kvm_moment_alpha(C.byref(desc), _p(Qwin), _p(K_), _p(alpha), _p(ws), ws.numel(), _stream(stream)))
+    return alpha
+
+
+def kvm_moment_score(K_, V_, alpha, moments, kv_head_major=False, score=None, stream=None):
+    """score [b, H_kv, L] = alpha * ||v - v_bar - S~ k / (n_e sqrt d)|| with moments
+    dict(n_e, s_k, s_v, S)."""
+    _contig(K_, V_, alpha, score)
+    desc = _moment_desc(K_, 1, 1, kv_head_major, None)
+    if score is None:
+        score = torch.empty((desc.b, desc.H_kv, desc.L), dtype=torch.float32, device=K_.device)
+    check(lib().kvm_moment_score(C.byref(desc), _p(K_), _p(V_), _p(alpha), _p(moments["n_e"]), _p(moments["s_k"]),
+                                 _p(moments["s_v"]), _p(moments["S"]), _p(score), _stream(stream)))
+    return score
+
+
+def kvm_moment_readout(q, o_R, lse_R, moments, o=None, scale=None, stream=None):
+    """Normalization-corrected mix of the retained output o_R [b,H_q,d] (log-partition
+    lse_R [b,H_q]) with the moments' first-order estimate of the evicted output."""
+    _contig(q, o_R, lse_R, o)
+    b, H_q, d = q.shape
+    H_kv = moments["n_e"].shape[1]
+    desc = K.MReadDesc(b=b, H_q=H_q, H_kv=H_kv, d=d, dtype=_dtype(q),
+                       scale=(1.0 / math.sqrt(d)) if scale is None else scale)
+    if o is None:
+        o = torch.empty((b, H_q, d), dtype=torch.float32, device=q.device)
+    check(lib().kvm_moment_readout(C.byref(desc), _p(q), _p(o_R), _p(lse_R), _p(moments["n_e"]), _p(moments["s_k"]),
+                                   _p(moments["s_v"]), _p(moments["S"]), _p(o), _stream(stream)))
+    return o

@@ -411,7 +411,7 @@ struct GatherArgs {
   const int32_t* idx;
   void* Kc;
   void* Vc;
-  int L, H_kv, cap, keep, per_head;
+  int L, H_kv, cap, keep, per_head, v_row_major;
   long long tok_stride, head_stride, batch_stride;  // elements
 };
 
@@ -445,11 +445,16 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(GatherArgs a) {
       vv = *reinterpret_cast<const uint4*>(Vb + t * a.tok_stride + cc * E16);
     }
     *reinterpret_cast<uint4*>(Kcb + (size_t)sl * D + cc * E16) = kv;
+    if (a.v_row_major) {   // Vc [b, H_kv, cap, d]
+      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.Vc) + (pair * a.cap + s0 + sl) * D + cc * E16) = vv;
+      continue;
+    }
     T ve[E16];
     __builtin_memcpy(ve, &vv, 16);
 #pragma unroll
     for (int e = 0; e < E16; ++e) sVt[(cc * E16 + e) * SP + sl] = ve[e];
   }
+  if (a.v_row_major) return;   // block-uniform
   __syncthreads();
   for (int i = tid; i < D * 64; i += 256) {
     const int dim = i / 64, sl = i % 64;
@@ -648,7 +653,8 @@ extern "C" kvm_status kvm_compact_kv(const kvm_compact_desc* d, const void* K, c
     else hipLaunchKernelGGL(compact_reduce_kernel<64>, rgrid, dim3(256), 0, s, a);
   }
   if (Kc && d->keep > 0) {
-    GatherArgs ga{K, V, idx, Kc, Vc, d->L, d->H_kv, d->cap, d->keep, d->per_head, tok_stride, head_stride, batch_stride};
+    GatherArgs ga{K, V, idx, Kc, Vc, d->L, d->H_kv, d->cap, d->keep, d->per_head, d->v_row_major, tok_stride,
+                  head_stride, batch_stride};
     const dim3 grid((d->keep + 63) / 64, d->H_kv, d->b);
     if (bf) {
       if (d->d == 128) hipLaunchKernelGGL((gather_kv_kernel<uint16_t, 128>), grid, dim3(256), 0, s, ga);

@@ -1,0 +1,486 @@
+// V1 / V3: MomentKV's eviction score and its normalization-corrected read-out [MKV].
+//
+// alpha_j = (1 / (W G)) sum over the window's queries s and the G query heads of the KV
+// group of the causal softmax weight of key j (the attention mass each key receives);
+// score_j = alpha_j ||r_j||, r_j = v_j - v_bar - S~ k_j / (n_e sqrt d) (r_j = v_j while
+// nothing is evicted) [MKV part 3]; the read-out mixes the retained attention output with
+// the first-order estimate of the evicted one [MKV parts 2 and 4].
+//
+// alpha runs on the matrix cores in two passes over the same 32 x 32 logit tiles:
+//   pass 1: C = K Q^T (keys as rows): each lane owns one query column and keeps an online
+//           (max, sum) of exp2 over its key rows -> partial log-sum-exp per query and chunk;
+//   merge:  log-sum-exp per query over the chunks;
+//   pass 2: C = Q K^T (queries as rows): each lane owns one key column and sums
+//           exp2(logit - lse) over its query rows -> alpha per key.
+// Swapping the operands between the passes keeps every reduction inside a lane (plus one
+// exchange between the two half-waves), so no cross-lane row reductions are needed.
+#include "common.hpp"
+
+namespace kvm {
+
+struct AlphaArgs {
+  const uint16_t* Q;   // [b, W, H_q, d]
+  const uint16_t* K;
+  float* alpha;        // [b, H_kv, L]
+  float2* part;        // ws [pairs, chunks, WG]  (max, sum) in log2 units
+  float* lse2;         // ws [pairs, WG]
+  int L, H_q, H_kv, W, G, WG, n_chunks;
+  long long tok_stride, head_stride, batch_stride;
+  float scale_log2;    // scale * log2(e)
+};
+
+constexpr int kAlphaChunk = 512;   // keys per block
+constexpr int kAlphaQPW = 2;       // 32-row query tiles per wave (W G <= 256)
+constexpr int kKPitch = 8;         // LDS row pad (elements) of a key tile
+
+template <int D, int PASS>
+__global__ __launch_bounds__(256) void moment_alpha_kernel(AlphaArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int RP = D + kKPitch;             // LDS pitch (elements)
+  constexpr int PER = 32 * D / 8 / 256;       // 16-byte pieces of a key tile per thread
+  const int c = blockIdx.x, pair = blockIdx.y;
+  const int bb = pair / a.H_kv, g = pair % a.H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  __shared__ uint16_t sK[2][32 * RP];
+  __shared__ float s_alpha[4][kAlphaChunk];
+
+  // query operands of this wave's tiles: rows r = s G + hh of the group (q of position L-W+s)
+  bf16x8_t qop[kAlphaQPW][KS];
+#pragma unroll
+  for (int x = 0; x < kAlphaQPW; ++x) {
+    const int r = (wave * kAlphaQPW + x) * 32 + col;
+    const bool ok = r < a.WG;
+    const int s = ok ? r / a.G : 0, hh = ok ? r % a.G : 0;
+    const uint16_t* qp = a.Q + (((size_t)bb * a.W + s) * a.H_q + g * a.G + hh) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (ok) v = *reinterpret_cast<const uint4*>(qp + ks * 16);
+      __builtin_memcpy(&qop[x][ks], &v, 16);
+    }
+  }
+  // pass 2: log-sum-exp of the 16 query rows this lane holds per tile
+  float lq[kAlphaQPW][16];
+  if (PASS == 2) {
+#pragma unroll
+    for (int x = 0; x < kAlphaQPW; ++x)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = (wave * kAlphaQPW + x) * 32 + 8 * (j / 4) + 4 * half + (j % 4);
+        lq[x][j] = r < a.WG ? a.lse2[(size_t)pair * a.WG + r] : INFINITY;
+      }
+  }
+  float m[kAlphaQPW], l[kAlphaQPW];
+#pragma unroll
+  for (int x = 0; x < kAlphaQPW; ++x) { m[x] = -INFINITY; l[x] = 0.f; }
+
+  const uint16_t* Kb = a.K + bb * a.batch_stride + g * a.head_stride;
+  const int k0 = c * kAlphaChunk;
+  const int ntile = min(kAlphaChunk, a.L - k0 + 31) / 32;
+  const int p0 = a.L - a.W;   // position of window query 0
+  // key tile t -> LDS buffer (t & 1); rows past L are zero
+  uint4 kr[PER];
+  auto kload = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int piece = tid + i * 256, row = piece / (D / 8), cc = piece % (D / 8);
+      const int j = k0 + t * 32 + row;
+      kr[i] = j < a.L ? *reinterpret_cast<const uint4*>(Kb + (size_t)j * a.tok_stride + cc * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto kstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int piece = tid + i * 256, row = piece / (D / 8), cc = piece % (D / 8);
+      *reinterpret_cast<uint4*>(&sK[buf][row * RP + cc * 8]) = kr[i];
+    }
+  };
+  kload(0);
+  kstore(0);
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    if (t + 1 < ntile) kload(t + 1);
+    const int buf = t & 1;
+    const int kb = k0 + t * 32;
+    // key operand: key row `col`, k-slice half*8 .. +8 of each k-step
+    bf16x8_t kop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&sK[buf][col * RP + ks * 16 + half * 8]);
+      __builtin_memcpy(&kop[ks], &v, 16);
+    }
+    float asum = 0.f;
+#pragma unroll
+    for (int x = 0; x < kAlphaQPW; ++x) {
+      f32x16_t acc;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = PASS == 1 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[x][ks], acc, 0, 0, 0)
+                        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[x][ks], kop[ks], acc, 0, 0, 0);
+      const int rbase = (wave * kAlphaQPW + x) * 32;
+      if (PASS == 1) {
+        // rows = keys, this lane's column = query r
+        const int r = rbase + col;
+        const int lim = r < a.WG ? min(a.L - 1, p0 + r / a.G) : -1;   // last visible key
+        float z[16], mt = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = kb + 8 * (j / 4) + 4 * half + (j % 4);
+          z[j] = key <= lim ? acc[j] * a.scale_log2 : -INFINITY;
+          mt = fmaxf(mt, z[j]);
+        }
+        const float mn = fmaxf(m[x], mt);
+        if (mn != -INFINITY) {
+          float sacc = l[x] * __builtin_amdgcn_exp2f(m[x] - mn);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sacc += __builtin_amdgcn_exp2f(z[j] - mn);
+          l[x] = sacc;
+          m[x] = mn;
+        }
+      } else {
+        // rows = queries, this lane's column = key kb + col
+        const int key = kb + col;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = rbase + 8 * (j / 4) + 4 * half + (j % 4);
+          const bool vis = r < a.WG && key < a.L && key <= p0 + r / a.G;
+          asum += vis ? __builtin_amdgcn_exp2f(acc[j] * a.scale_log2 - lq[x][j]) : 0.f;
+        }
+      }
+    }
+    if (PASS == 2) {
+      asum += shfl_xor32(asum);
+      if (half == 0) s_alpha[wave][t * 32 + col] = asum;
+    }
+    if (t + 1 < ntile) kstore(buf ^ 1);
+    __syncthreads();
+  }
+  if (PASS == 1) {
+    // combine the two half-waves (same query column, different key rows)
+#pragma unroll
+    for (int x = 0; x < kAlphaQPW; ++x) {
+      const float om = shfl_xor32(m[x]), ol = shfl_xor32(l[x]);
+      const float mn = fmaxf(m[x], om);
+      float sum = 0.f;
+      if (mn != -INFINITY) sum = l[x] * __builtin_amdgcn_exp2f(m[x] - mn) + ol * __builtin_amdgcn_exp2f(om - mn);
+      const int r = (wave * kAlphaQPW + x) * 32 + col;
+      if (half == 0 && r < a.WG) a.part[((size_t)pair * a.n_chunks + c) * a.WG + r] = make_float2(mn, sum);
+    }
+  } else {
+    const float inv = 1.f / (float)a.WG;
+    for (int i = tid; i < ntile * 32; i += 256) {
+      const int j = k0 + i;
+      if (j < a.L) {
+        const float s = ((s_alpha[0][i] + s_alpha[1][i]) + s_alpha[2][i]) + s_alpha[3][i];
+        a.alpha[(size_t)pair * a.L + j] = s * inv;
+      }
+    }
+  }
+}
+
+// grid (pairs), 256 threads: log-sum-exp (log2 units) of each query row over the chunks.
+__global__ __launch_bounds__(256) void alpha_merge_kernel(AlphaArgs a) {
+  const int pair = blockIdx.x;
+  for (int r = threadIdx.x; r < a.WG; r += 256) {
+    float mx = -INFINITY;
+    for (int c = 0; c < a.n_chunks; ++c) mx = fmaxf(mx, a.part[((size_t)pair * a.n_chunks + c) * a.WG + r].x);
+    float s = 0.f;
+    if (mx != -INFINITY)
+      for (int c = 0; c < a.n_chunks; ++c) {
+        const float2 p = a.part[((size_t)pair * a.n_chunks + c) * a.WG + r];
+        if (p.x != -INFINITY) s += p.y * __builtin_amdgcn_exp2f(p.x - mx);
+      }
+    a.lse2[(size_t)pair * a.WG + r] = mx + log2f(s);
+  }
+}
+
+// ------------------------------------------------------------------ residual score
+// grid (ceil(L / kScoreKeys), pairs), D / 32 waves.  Wave w owns dims 32w .. 32w+32 of the
+// residual: C[i][key] = sum_c S'[i][c] k[key][c] with S' = S~ / (n_e sqrt d) split into
+// three bf16 terms (hi + mid + lo, ~24 bits) as the A operand and the exact bf16 keys as
+// the B operand; r = v - v_bar - C; ||r||^2 sums the lane's rows, the two half-waves and
+// the waves.
+struct ScoreArgs {
+  const uint16_t* K;
+  const uint16_t* V;
+  const float* alpha;   // [pairs, L]
+  const int32_t* n_e;
+  const float* s_k;
+  const float* s_v;
+  const float* S;
+  float* score;         // [pairs, L]
+  int L, H_kv;
+  long long tok_stride, head_stride, batch_stride;
+  float inv_sqrt_d;
+};
+
+constexpr int kScoreKeys = 256;
+
+__device__ __forceinline__ void split3(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
+  h = f32_to_bf16_bits(x);
+  const float r1 = x - __uint_as_float((uint32_t)h << 16);
+  m = f32_to_bf16_bits(r1);
+  const float r2 = r1 - __uint_as_float((uint32_t)m << 16);
+  l = f32_to_bf16_bits(r2);
+}
+
+template <int D>
+__global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int NW = D / 32;
+  const int c = blockIdx.x, pair = blockIdx.y;
+  const int bb = pair / a.H_kv, g = pair % a.H_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  __shared__ float s_ss[NW][kScoreKeys];
+
+  const int ne = a.n_e[pair];
+  const float inv_n = ne > 0 ? 1.f / (float)ne : 0.f;
+  const float* sk = a.s_k + (size_t)pair * D;
+  const float* sv = a.s_v + (size_t)pair * D;
+  // A operands: row i = 32 wave + col of S' (zero while nothing is evicted)
+  const int i_row = wave * 32 + col;
+  bf16x8_t sh[KS], sm[KS], sl[KS];
+  {
+    const float* Sr = a.S + ((size_t)pair * D + i_row) * D;
+    const float svi = sv[i_row];
+    const float f = inv_n * a.inv_sqrt_d;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint16_t hv[8], mv[8], lv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int cc = ks * 16 + half * 8 + e;
+        const float x = ne > 0 ? (Sr[cc] - svi * sk[cc] * inv_n) * f : 0.f;
+        split3(x, hv[e], mv[e], lv[e]);
+      }
+      __builtin_memcpy(&sh[ks], hv, 16);
+      __builtin_memcpy(&sm[ks], mv, 16);
+      __builtin_memcpy(&sl[ks], lv, 16);
+    }
+  }
+  // v_bar of the 16 dims this lane holds in the C layout
+  float vbar[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) vbar[j] = sv[wave * 32 + 8 * (j / 4) + 4 * half + (j % 4)] * inv_n;
+
+  const uint16_t* Kb = a.K + bb * a.batch_stride + g * a.head_stride;
+  const uint16_t* Vb = a.V + bb * a.batch_stride + g * a.head_stride;
+  const int k0 = c * kScoreKeys;
+  const int ntile = min(kScoreKeys, a.L - k0 + 31) / 32;
+  for (int t = 0; t < ntile; ++t) {
+    const int key = k0 + t * 32 + col;
+    const bool ok = key < a.L;
+    const uint16_t* kp = Kb + (size_t)(ok ? key : 0) * a.tok_stride + half * 8;
+    const uint16_t* vp = Vb + (size_t)(ok ? key : 0) * a.tok_stride + wave * 32 + 4 * half;
+    f32x16_t acc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 kv = ok ? *reinterpret_cast<const uint4*>(kp + ks * 16) : make_uint4(0, 0, 0, 0);
+      bf16x8_t B;
+      __builtin_memcpy(&B, &kv, 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh[ks], B, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sm[ks], B, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl[ks], B, acc, 0, 0, 0);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      // rows 8 q4 + 4 half + 0..3: four consecutive dims of this key's v
+      uint2 vv = ok ? *reinterpret_cast<const uint2*>(vp + 8 * q4) : make_uint2(0, 0);
+      const float v4[4] = {bf16_lo(vv.x), bf16_hi(vv.x), bf16_lo(vv.y), bf16_hi(vv.y)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float r = v4[e] - vbar[q4 * 4 + e] - acc[q4 * 4 + e];
+        ss = fmaf(r, r, ss);
+      }
+    }
+    ss += shfl_xor32(ss);
+    if (half == 0) s_ss[wave][t * 32 + col] = ss;
+  }
+  __syncthreads();
+  for (int i = tid; i < ntile * 32; i += NW * 64) {
+    const int j = k0 + i;
+    if (j < a.L) {
+      float ss = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) ss += s_ss[w][i];
+      a.score[(size_t)pair * a.L + j] = a.alpha[(size_t)pair * a.L + j] * sqrtf(ss);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ read-out (V3)
+// grid (H_kv, b), 256 threads.  Per query head h of the group:
+//   f_E = v_bar + (S q - s_v (s_k . q) / n_e) / (n_e sqrt d),  log Z_E = log n_e + (q . s_k / n_e) / sqrt d,
+//   w_R = sigmoid(lse_R - log Z_E),  o = w_R f_R + (1 - w_R) f_E   (o = f_R while n_e = 0).
+template <typename T>
+__global__ __launch_bounds__(256) void moment_readout_kernel(const T* q, const float* fR, const float* lseR,
+                                                             const int32_t* n_e, const float* s_k, const float* s_v,
+                                                             const float* S, float* o, int H_q, int H_kv, int D,
+                                                             float scale) {
+  const int g = blockIdx.x, bb = blockIdx.y, tid = threadIdx.x;
+  const int G = H_q / H_kv;
+  const size_t pair = (size_t)bb * H_kv + g;
+  extern __shared__ float smem[];
+  float* sq = smem;              // [G][D]
+  float* sr = smem + G * D;      // [G]: s_k . q
+  for (int i = tid; i < G * D; i += 256) sq[i] = load_scalar<T>(q + ((size_t)bb * H_q + g * G) * D + i);
+  __syncthreads();
+  const int ne = n_e[pair];
+  const float* sk = s_k + pair * D;
+  if (tid < 64) {
+    for (int h = 0; h < G; ++h) {
+      float x = 0.f;
+      for (int i = tid; i < D; i += 64) x = fmaf(sk[i], sq[h * D + i], x);
+      x = wave_sum(x);
+      if (tid == 0) sr[h] = x;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, i = idx % D;
+    const size_t oh = ((size_t)bb * H_q + g * G + h) * D + i;
+    const float f = fR[oh];
+    if (ne <= 0) { o[oh] = f; continue; }
+    const float* Sr = S + (pair * D + i) * D;
+    float sq_i = 0.f;
+    for (int cc = 0; cc < D; ++cc) sq_i = fmaf(Sr[cc], sq[h * D + cc], sq_i);
+    const float inv = 1.f / (float)ne;
+    const float sv = s_v[pair * D + i];
+    const float fE = sv * inv + scale * (sq_i - sv * sr[h] * inv) * inv;
+    const float logZ = __logf((float)ne) + scale * sr[h] * inv;
+    const float w = sigmoid_f(lseR[(size_t)bb * H_q + g * G + h] - logZ);
+    o[oh] = w * f + (1.f - w) * fE;
+  }
+}
+
+struct MomentWs { size_t part, lse, total; };
+static MomentWs moment_ws(const kvm_moment_desc* d) {
+  const size_t pairs = (size_t)d->b * d->H_kv;
+  const int nc = (d->L + kAlphaChunk - 1) / kAlphaChunk;
+  const int WG = d->W * (d->H_q / d->H_kv);
+  MomentWs w;
+  w.part = 0;
+  w.lse = align_up(pairs * nc * WG * sizeof(float2), 256);
+  w.total = align_up(w.lse + pairs * WG * sizeof(float), 256);
+  return w;
+}
+
+static void strides(const kvm_moment_desc* d, long long& ts, long long& hs, long long& bs) {
+  if (d->kv_head_major) {
+    ts = d->d; hs = (long long)d->L * d->d; bs = (long long)d->H_kv * d->L * d->d;
+  } else {
+    ts = (long long)d->H_kv * d->d; hs = d->d; bs = (long long)d->L * d->H_kv * d->d;
+  }
+}
+
+static kvm_status check_moment_desc(const kvm_moment_desc* d) {
+  KVM_PTR(d);
+  KVM_REQUIRE(d->b > 0 && d->L > 0 && d->H_kv > 0, KVM_ERR_SHAPE, "b, L, H_kv must be positive");
+  KVM_REQUIRE(d->d == 64 || d->d == 128, KVM_ERR_SHAPE, "head dim %d not in {64, 128}", d->d);
+  KVM_REQUIRE(d->dtype == KVM_BF16, KVM_ERR_DTYPE, "MomentKV scoring takes bf16 K, V, Q (dtype %d)", d->dtype);
+  return KVM_OK;
+}
+
+}  // namespace kvm
+
+using namespace kvm;
+
+extern "C" size_t kvm_moment_workspace_size(const kvm_moment_desc* d) {
+  if (!d || d->b <= 0 || d->L <= 0 || d->H_kv <= 0 || d->H_q <= 0 || d->W <= 0) return 0;
+  return moment_ws(d).total;
+}
+
+extern "C" kvm_status kvm_moment_alpha(const kvm_moment_desc* d, const void* Qwin, const void* K, float* alpha,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  kvm_status st = check_moment_desc(d);
+  if (st != KVM_OK) return st;
+  KVM_REQUIRE(d->H_q > 0 && d->H_q % d->H_kv == 0, KVM_ERR_SHAPE, "H_q %d not a multiple of H_kv %d", d->H_q, d->H_kv);
+  KVM_REQUIRE(d->W >= 1 && d->W <= d->L, KVM_ERR_RANGE, "window %d outside [1, L]", d->W);
+  const int G = d->H_q / d->H_kv;
+  KVM_REQUIRE(d->W * G <= 4 * kAlphaQPW * 32, KVM_ERR_SHAPE, "W * G = %d exceeds %d", d->W * G, 4 * kAlphaQPW * 32);
+  KVM_REQUIRE(d->scale > 0.f, KVM_ERR_RANGE, "scale %g must be positive", d->scale);
+  KVM_PTR_ALIGNED(Qwin); KVM_PTR_ALIGNED(K); KVM_PTR_ALIGNED(alpha);
+  const MomentWs w = moment_ws(d);
+  KVM_REQUIRE(ws != nullptr && ws_bytes >= w.total, KVM_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+  KVM_ALIGNED(ws);
+  st = require_gfx950();
+  if (st != KVM_OK) return st;
+  AlphaArgs a{};
+  a.Q = static_cast<const uint16_t*>(Qwin);
+  a.K = static_cast<const uint16_t*>(K);
+  a.alpha = alpha;
+  a.part = reinterpret_cast<float2*>(static_cast<char*>(ws) + w.part);
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + w.lse);
+  a.L = d->L; a.H_q = d->H_q; a.H_kv = d->H_kv; a.W = d->W; a.G = G; a.WG = d->W * G;
+  a.n_chunks = (d->L + kAlphaChunk - 1) / kAlphaChunk;
+  strides(d, a.tok_stride, a.head_stride, a.batch_stride);
+  a.scale_log2 = d->scale * 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(a.n_chunks, d->b * d->H_kv);
+  if (d->d == 128) {
+    hipLaunchKernelGGL((moment_alpha_kernel<128, 1>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(alpha_merge_kernel, dim3(d->b * d->H_kv), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((moment_alpha_kernel<128, 2>), grid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((moment_alpha_kernel<64, 1>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(alpha_merge_kernel, dim3(d->b * d->H_kv), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((moment_alpha_kernel<64, 2>), grid, dim3(256), 0, s, a);
+  }
+  return check_hip(hipGetLastError(), "moment alpha launch");
+}
+
+extern "C" kvm_status kvm_moment_score(const kvm_moment_desc* d, const void* K, const void* V, const float* alpha,
+                                       const int32_t* n_e, const float* s_k, const float* s_v, const float* S,
+                                       float* score, void* stream) {
+  kvm_status st = check_moment_desc(d);
+  if (st != KVM_OK) return st;
+  KVM_PTR_ALIGNED(K); KVM_PTR_ALIGNED(V); KVM_PTR_ALIGNED(alpha); KVM_PTR_ALIGNED(n_e);
+  KVM_PTR_ALIGNED(s_k); KVM_PTR_ALIGNED(s_v); KVM_PTR_ALIGNED(S); KVM_PTR_ALIGNED(score);
+  st = require_gfx950();
+  if (st != KVM_OK) return st;
+  ScoreArgs a{};
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.alpha = alpha; a.n_e = n_e; a.s_k = s_k; a.s_v = s_v; a.S = S; a.score = score;
+  a.L = d->L; a.H_kv = d->H_kv;
+  strides(d, a.tok_stride, a.head_stride, a.batch_stride);
+  a.inv_sqrt_d = 1.f / sqrtf((float)d->d);
+  const dim3 grid((d->L + kScoreKeys - 1) / kScoreKeys, d->b * d->H_kv);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->d == 128) hipLaunchKernelGGL(moment_score_kernel<128>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(moment_score_kernel<64>, grid, dim3(128), 0, s, a);
+  return check_hip(hipGetLastError(), "moment score launch");
+}
+
+extern "C" kvm_status kvm_moment_readout(const kvm_mread_desc* d, const void* q, const float* o_R,
+                                         const float* lse_R, const int32_t* n_e, const float* s_k,
+                                         const float* s_v, const float* S, float* o, void* stream) {
+  KVM_PTR(d);
+  KVM_REQUIRE(d->b > 0 && d->H_q > 0 && d->H_kv > 0 && d->H_q % d->H_kv == 0, KVM_ERR_SHAPE,
+              "b, H_q, H_kv positive with H_q a multiple of H_kv required");
+  KVM_REQUIRE(d->d == 64 || d->d == 128, KVM_ERR_SHAPE, "head dim %d not in {64, 128}", d->d);
+  KVM_REQUIRE(d->dtype == KVM_F32 || d->dtype == KVM_BF16, KVM_ERR_DTYPE, "dtype %d", d->dtype);
+  KVM_REQUIRE(d->H_q / d->H_kv <= 64, KVM_ERR_SHAPE, "group size %d exceeds 64", d->H_q / d->H_kv);
+  KVM_PTR_ALIGNED(q); KVM_PTR_ALIGNED(o_R); KVM_PTR_ALIGNED(lse_R); KVM_PTR_ALIGNED(n_e);
+  KVM_PTR_ALIGNED(s_k); KVM_PTR_ALIGNED(s_v); KVM_PTR_ALIGNED(S); KVM_PTR_ALIGNED(o);
+  kvm_status st = require_gfx950();
+  if (st != KVM_OK) return st;
+  const int G = d->H_q / d->H_kv;
+  const size_t smem = (size_t)(G * d->d + G) * sizeof(float);
+  const dim3 grid(d->H_kv, d->b);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->dtype == KVM_BF16)
+    hipLaunchKernelGGL(moment_readout_kernel<uint16_t>, grid, dim3(256), smem, s, static_cast<const uint16_t*>(q),
+                       o_R, lse_R, n_e, s_k, s_v, S, o, d->H_q, d->H_kv, d->d, d->scale);
+  else
+    hipLaunchKernelGGL(moment_readout_kernel<float>, grid, dim3(256), smem, s, static_cast<const float*>(q), o_R,
+                       lse_R, n_e, s_k, s_v, S, o, d->H_q, d->H_kv, d->d, d->scale);
+  return check_hip(hipGetLastError(), "moment readout launch");
+}

@@ -1,0 +1,205 @@
+"""MomentKV on the GPU against the oracle: the attention weight alpha (two matrix-core
+passes), the residual score, the stand-alone read-out, and the whole moment-informed
+prefill (halving rounds of score -> per-head top-k -> moment fold) followed by decode
+with the normalization-corrected mix."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import indexmem as im
+from oracle import momentkv as mk
+from synth import CONFIGS, gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _qkv(b, L, W, H_q, H_kv, d, seed):
+    r = gen.rng(95, seed, 0, 0)
+    st = lambda x: gen.to_storage(x, "bf16")
+    return st(r.standard_normal((b, W, H_q, d))), st(r.standard_normal((b, L, H_kv, d))), \
+        st(r.standard_normal((b, L, H_kv, d)))
+
+
+ALPHA_CASES = [
+    # b, L, W, H_q, H_kv, d, head_major
+    (2, 1000, 64, 32, 8, 128, False),
+    (1, 777, 64, 32, 8, 128, True),
+    (1, 531, 32, 8, 8, 64, False),
+    (2, 64, 64, 16, 4, 128, False),      # every key inside the window
+    (1, 2048, 16, 4, 2, 64, True),
+]
+
+
+@pytest.mark.parametrize("b,L,W,H_q,H_kv,d,hm", ALPHA_CASES)
+def test_alpha_matches_oracle(b, L, W, H_q, H_kv, d, hm):
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, normwise
+    Q, Kt, _ = _qkv(b, L, W, H_q, H_kv, d, seed=L + W)
+    Kin = np.ascontiguousarray(Kt.transpose(0, 2, 1, 3)) if hm else Kt
+    got = to_np(api.kvm_moment_alpha(to_dev(Q), to_dev(Kin), kv_head_major=hm))
+    Qd, Kd = gen.from_storage(Q, "bf16"), gen.from_storage(Kt, "bf16")
+    for i in range(b):
+        ref = mk.alpha(Qd[i], Kd[i], np.arange(L - W, L), 1 / math.sqrt(d), H_q // H_kv)
+        assert normwise(got[i], ref) < 1e-5
+        np.testing.assert_allclose(got[i], ref, rtol=1e-4, atol=1e-6 * ref.max())
+        # each query's weights sum to one, so alpha sums to 1 per KV head
+        np.testing.assert_allclose(got[i].sum(-1), 1.0, rtol=1e-4)
+
+
+def _moments(b, H, d, n, seed):
+    """Moments of n random evicted rows per (sequence, KV head), in fp64 and as device
+    arrays (n = 0 gives empty moments)."""
+    r = gen.rng(96, seed, 0, 0)
+    moms = []
+    for i in range(b):
+        row = []
+        for g in range(H):
+            m = mk.empty(d)
+            if n:
+                m = mk.add(m, gen.bf16_to_f32(gen.to_storage(r.standard_normal((n, d)), "bf16")),
+                           gen.bf16_to_f32(gen.to_storage(r.standard_normal((n, d)), "bf16")))
+            row.append(m)
+        moms.append(row)
+    return moms
+
+
+def _dev_moments(moms):
+    from tests.gpu_util import to_dev
+    return dict(n_e=to_dev(np.array([[m["n"] for m in row] for row in moms], np.int32)),
+                s_k=to_dev(np.array([[m["sk"] for m in row] for row in moms], np.float32)),
+                s_v=to_dev(np.array([[m["sv"] for m in row] for row in moms], np.float32)),
+                S=to_dev(np.array([[m["S"] for m in row] for row in moms], np.float32)))
+
+
+@pytest.mark.parametrize("L,d,n,hm", [(1000, 128, 300, False), (513, 64, 50, True), (300, 128, 0, False),
+                                      (4097, 128, 4000, True)])
+def test_residual_score_matches_oracle(L, d, n, hm):
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, normwise
+    b, H = 2, 4
+    _, Kt, Vt = _qkv(b, L, 1, 1, H, d, seed=L + n)
+    moms = _moments(b, H, d, n, seed=L)
+    alpha = gen.rng(97, L, 0, 0).random((b, H, L)).astype(np.float32)
+    tr = (lambda x: np.ascontiguousarray(x.transpose(0, 2, 1, 3))) if hm else (lambda x: x)
+    mom_d = _dev_moments(moms)
+    got = to_np(api.kvm_moment_score(to_dev(tr(Kt)), to_dev(tr(Vt)), to_dev(alpha), mom_d, kv_head_major=hm))
+    Kd, Vd = gen.from_storage(Kt, "bf16"), gen.from_storage(Vt, "bf16")
+    for i in range(b):
+        for g in range(H):
+            m32 = {k: (np.float32(v).astype(np.float64) if k != "n" else v) for k, v in moms[i][g].items()}
+            ref = mk.score(alpha[i, g].astype(np.float64), Kd[i, :, g], Vd[i, :, g], m32, d)
+            assert normwise(got[i, g], ref) < 1e-5
+            np.testing.assert_allclose(got[i, g], ref, rtol=2e-5, atol=1e-6 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("dtype,G", [("bf16", 4), ("f32", 1), ("bf16", 8)])
+def test_moment_readout_matches_oracle(dtype, G):
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np
+    b, H, d = 2, 4, 128
+    H_q = H * G
+    r = gen.rng(98, G, 0, 0)
+    q = gen.to_storage(r.standard_normal((b, H_q, d)), dtype)
+    fR = r.standard_normal((b, H_q, d)).astype(np.float32)
+    lse = (r.standard_normal((b, H_q)) * 3 + 5).astype(np.float32)
+    moms = _moments(b, H, d, 40, seed=G)
+    moms[1][2] = mk.empty(d)   # a head with nothing evicted
+    got = to_np(api.kvm_moment_readout(to_dev(q), to_dev(fR), to_dev(lse), _dev_moments(moms)))
+    qd = gen.from_storage(q, dtype)
+    for i in range(b):
+        for h in range(H_q):
+            m32 = {k: (np.float32(v).astype(np.float64) if k != "n" else v) for k, v in moms[i][h // G].items()}
+            ref, _ = mk.mix(qd[i, h], fR[i, h].astype(np.float64), float(lse[i, h]), m32, d)
+            np.testing.assert_allclose(got[i, h], ref, rtol=1e-5, atol=1e-5 * np.abs(ref).max())
+
+
+def _kept_check(gpu_kept, scores_ref, keep, rel=1e-5):
+    """Per-head round decision: the GPU's kept set equals the oracle's top `keep` of its
+    scores rounded to fp32 (the kernel's precision) outside the band within `rel` of the
+    keep-th score.  Returns the number of in-band differences."""
+    s32 = np.asarray(scores_ref, np.float64).astype(np.float32).astype(np.float64)
+    ref_kept, _ = mk.select_round(s32, np.arange(len(s32)), keep)
+    g, rf = set(int(x) for x in gpu_kept), set(int(x) for x in ref_kept)
+    assert len(g) == len(rf)
+    tau = min(s32[j] for j in ref_kept)
+    band = np.abs(s32 - tau) <= rel * abs(tau)
+    bad = [j for j in g ^ rf if not band[j]]
+    assert not bad, f"kept-set mismatch outside the band at {bad[:8]}"
+    return len(g ^ rf)
+
+
+@pytest.mark.parametrize("L,B,b,T", [(2048, 128, 1, 6), (1500, 200, 2, 4)])
+def test_momentkv_prefill_and_decode(L, B, b, T):
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, normwise, assert_output
+    cfg = CONFIGS[5].with_(L=L, B=B, b=b, T=T)
+    H, d, W, H_q = cfg.H_kv, cfg.d, cfg.W, cfg.H_q
+    p = gen.make_prefill(cfg)
+    dec = gen.make_decode(cfg, steps=T)
+    f = lambda x: gen.from_storage(x, "bf16")
+    Q, Kt, Vt = p["Qwin"], p["K"], p["V"]
+    refs = [mk.prefill(f(Q[i]), f(Kt[i]), f(Vt[i]), B) for i in range(b)]
+
+    alpha = api.kvm_moment_alpha(to_dev(Q), to_dev(Kt))
+    for i in range(b):
+        assert normwise(to_np(alpha)[i], refs[i]["alpha"]) < 1e-5
+    mom = dict(n_e=torch.zeros((b, H), dtype=torch.int32, device="cuda"),
+               s_k=torch.zeros((b, H, d), device="cuda"), s_v=torch.zeros((b, H, d), device="cuda"),
+               S=torch.zeros((b, H, d, d), device="cuda"))
+    Kc, Vc = to_dev(Kt), to_dev(Vt)
+    al = alpha.view(b * H, L)
+    pos = torch.arange(L, dtype=torch.int32, device="cuda").repeat(b * H, 1).contiguous()
+    n, rnd, hm = L, 0, False
+    same = True
+    cap = api.cache_cap(B + T)
+    while n > B:
+        keep = max(B, -(-n // 2))
+        last = keep == B
+        sc = api.kvm_moment_score(Kc, Vc, al.view(b, H, n), mom, kv_head_major=hm)
+        idx, sm = api.kvm_topk_select(sc.view(b * H, n), keep, 0)
+        # this round against the oracle's, while every head has made the same choices
+        g_sc, g_idx = to_np(sc).reshape(b * H, n), to_np(idx)
+        for i in range(b):
+            for g in range(H):
+                rr = refs[i]["heads"][g]["rounds"][rnd]
+                if same:
+                    assert normwise(g_sc[i * H + g], rr["scores"]) < 1e-5, f"round {rnd} scores, head {g}"
+                    kept_local = g_idx[i * H + g]
+                    diff = _kept_check(kept_local, rr["scores"], keep)
+                    if diff:
+                        same = False
+        Kn, Vn = api.kvm_compact_kv(Kc, Vc, sm, idx, keep, cap=cap if last else keep, moments=mom, per_head=True,
+                                    kv_head_major=hm, v_row_major=not last)
+        al = api.kvm_gather_rows(al, sm, keep)
+        pos = api.kvm_gather_rows(pos, sm, keep)
+        Kc, Vc, n, hm, rnd = Kn, Vn, keep, True, rnd + 1
+    torch.cuda.synchronize()
+    if not same:
+        pytest.skip("a near-tie in an early round changed the kept set within the 1e-5 band")
+    g_pos = to_np(pos)
+    for i in range(b):
+        for g in range(H):
+            np.testing.assert_array_equal(np.sort(g_pos[i * H + g][:B]), refs[i]["heads"][g]["kept"])
+            m = refs[i]["heads"][g]["mom"]
+            assert int(to_np(mom["n_e"])[i, g]) == m["n"]
+            assert normwise(to_np(mom["S"])[i, g], m["S"]) < 1e-5
+            assert normwise(to_np(mom["s_k"])[i, g], m["sk"]) < 1e-5
+            assert normwise(to_np(mom["s_v"])[i, g], m["sv"]) < 1e-5
+    # decode with the NC mix over each head's retained tokens
+    lens = torch.full((b,), B, dtype=torch.int32, device="cuda")
+    outs = []
+    for t in range(T):
+        o = api.kvm_decode_attn_mem(to_dev(dec["q"][t]), Kc, Vc, lens, k_new=to_dev(dec["k_new"][t]),
+                                    v_new=to_dev(dec["v_new"][t]), moments=mom)
+        outs.append(to_np(o))
+        api.kvm_len_add(lens, 1)
+    torch.cuda.synchronize()
+    for i in range(b):
+        ref, _, _ = mk.decode(f(dec["q"][:, i]), f(dec["k_new"][:, i]), f(dec["v_new"][:, i]), f(Kt[i]), f(Vt[i]),
+                              refs[i]["heads"])
+        got = np.stack([o[i] for o in outs])
+        assert_output(got, ref, "bf16", "MomentKV decode")
+        np.testing.assert_allclose(got, ref, rtol=1e-3, atol=1e-3 * np.abs(ref).max())
