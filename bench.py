@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--n-split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-decode-steps", type=int, default=32)
+    ap.add_argument("--no-rows", action="store_true", help="skip the streaming and MomentKV row timings")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy a few times (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -87,6 +90,129 @@ def prefill_bytes(cfg, keep, elem=2):
     return tok * cfg.D * elem + tok * cfg.H_kv * cfg.d * 2 * elem + cfg.b * keep * cfg.H_kv * cfg.d * 2 * elem
 
 
+PMC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "decode_layer_step_cfg3_pmc.txt")
+DECODE_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "learned_kv_cache_mqa_amd", "csrc", "decode.hip")
+
+
+def measured_traffic():
+    """HBM bytes per decode layer-step from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE scaled by a plain copy's counters), or None if the decode source changed
+    since the counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        with open(PMC_SUMMARY) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        with open(DECODE_SRC, "rb") as fh:
+            src = hashlib.sha256(fh.read()).hexdigest()
+        if kv.get("source_sha256") != src:
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 4}), flush=True)
+    return 0
+
+
+def time_rows(torch, api, KL, dev):
+    """Timings of the rows outside the IndexMem decode path, at their workloads' shapes
+    (device-drawn inputs): the streaming step (131072-token workload, pool 1024 + 64) and
+    MomentKV's alpha, one score round and the read-out (Qwen3-4B shape, 32K tokens, batch 4)."""
+    from synth import CONFIGS
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(4_000_000)
+    rn = lambda *sh, std=1.0: (torch.randn(*sh, generator=g, device=dev) * std).to(bf)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    rows = {}
+    # A7: streaming eviction step + decode over the pool
+    c4 = CONFIGS[4]
+    P = c4.B + c4.R
+    cap = api.cache_cap(P)
+    Kc = rn(1, c4.H_kv, cap, c4.d)
+    Vc = rn(1, c4.H_kv, c4.d, cap)
+    M = torch.zeros((1, c4.H_kv, c4.d, c4.d), device=dev)
+    bv = torch.ones((1, c4.H_kv, c4.d), device=dev)
+    kh = torch.randn((1, P, c4.d_I), generator=g, device=dev)
+    Ip = torch.rand((1, P), generator=g, device=dev)
+    pos = torch.cat([torch.arange(0, c4.L - c4.R, (c4.L - c4.R) // c4.B, device=dev)[:c4.B],
+                     torch.arange(c4.L - c4.R, c4.L, device=dev)]).to(torch.int32)[None].contiguous()
+    npos = torch.full((1,), c4.L, dtype=torch.int32, device=dev)
+    lens = torch.full((1,), P, dtype=torch.int32, device=dev)
+    W = [rn(c4.d_I, c4.D, std=c4.D ** -0.5), torch.ones(c4.d_I, device=dev), rn(c4.H_I, c4.d_I, c4.d, std=c4.d ** -0.5),
+         torch.ones(c4.d_I, device=dev), rn(c4.H_I, c4.D, std=c4.D ** -0.5)]
+    wg = rn(c4.H_q, c4.d, std=c4.d ** -0.5)
+    steps = 64
+    xs, qs, ks, vs = rn(steps, 1, c4.D), rn(steps, 1, c4.H_q, c4.d), rn(steps, 1, c4.H_kv, c4.d), rn(steps, 1, c4.H_kv, c4.d)
+    es = torch.empty((1,), dtype=torch.int32, device=dev)
+    o = torch.empty((1, c4.H_q, c4.d), device=dev)
+
+    def stream_steps():
+        for t in range(steps):
+            api.kvm_stream_evict(xs[t], qs[t], *W, kh, Ip, pos, npos, Kc, Vc, M, bv, c4.lam, c4.R, evict_slot=es)
+            api.kvm_decode_attn_mem(qs[t], Kc, Vc, lens, k_new=ks[t], v_new=vs[t], append_slot=es, M=M, bvec=bv,
+                                    w_g=wg, o=o)
+    stream_steps()
+    st = torch.cuda.Stream()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(gr, stream=st):
+            stream_steps()
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    with torch.cuda.stream(st):
+        e0.record(st)
+        gr.replay()
+        e1.record(st)
+    torch.cuda.synchronize()
+    rows["A7_stream_step_us"] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+    rows["A7_workload"] = f"1 sequence, pool {P} slots, D {c4.D}, stream step + decode per token, HIP graph"
+    # V1 / V3: MomentKV at the Qwen3-4B shape
+    c5 = CONFIGS[5]
+    Q = rn(c5.b, c5.W, c5.H_q, c5.d)
+    K5, V5 = rn(c5.b, c5.L, c5.H_kv, c5.d), rn(c5.b, c5.L, c5.H_kv, c5.d)
+    mom = dict(n_e=torch.full((c5.b, c5.H_kv), 1000, dtype=torch.int32, device=dev),
+               s_k=torch.randn((c5.b, c5.H_kv, c5.d), generator=g, device=dev),
+               s_v=torch.randn((c5.b, c5.H_kv, c5.d), generator=g, device=dev),
+               S=torch.randn((c5.b, c5.H_kv, c5.d, c5.d), generator=g, device=dev))
+    al = api.kvm_moment_alpha(Q, K5)
+    sc = api.kvm_moment_score(K5, V5, al, mom)
+    q5 = rn(c5.b, c5.H_q, c5.d)
+    oR = torch.randn((c5.b, c5.H_q, c5.d), generator=g, device=dev)
+    lR = torch.randn((c5.b, c5.H_q), generator=g, device=dev)
+    o5 = api.kvm_moment_readout(q5, oR, lR, mom)
+    torch.cuda.synchronize()
+    reps = 10
+    for name, fn in (("V1_alpha_ms", lambda: api.kvm_moment_alpha(Q, K5, alpha=al)),
+                     ("V1_score_round_ms", lambda: api.kvm_moment_score(K5, V5, al, mom, score=sc)),
+                     ("V3_readout_ms", lambda: api.kvm_moment_readout(q5, oR, lR, mom, o=o5))):
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        rows[name] = round(e0.elapsed_time(e1) / reps, 4)
+    rows["V_workload"] = (f"MomentKV, batch {c5.b}, {c5.L} tokens, {c5.H_q}/{c5.H_kv} heads, d {c5.d}, window {c5.W}: "
+                          "alpha (two passes), first score round over all tokens, read-out")
+    return rows
+
+
 def cpu_baseline(cfg, decode_steps):
     """The fp64 oracle on one (layer, sequence) of the workload: prefill index+evict and
     `decode_steps` decode steps, scaled to the workload's units."""
@@ -124,6 +250,8 @@ def main():
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path shards "
               "by sequence with no communication; see the design notes)", file=sys.stderr)
         return 2
+    if args.calibrate_copy:
+        return calibrate_copy()
     import torch
     from synth import CONFIGS
     from learned_kv_cache_mqa_amd import api
@@ -232,8 +360,10 @@ def main():
     achieved = avg_bytes / (launch_us * 1e-6) / 1e9
     pbytes = prefill_bytes(cfg, keep) * layers
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "decode_kernel<bf16,128,4,4> (one layer-step: split-K attention + memory read-out)",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "kernel": "kvm_decode_attn_mem layer-step: decode_mfma_kernel<4> (split-K attention + memory "
+                          "read-out rows) then decode_merge_kernel<128,4>; launch_us = decode phase time / "
+                          "(steps x layers), HIP events on the launch stream",
                 "bytes_per_launch": round(avg_bytes), "launch_us": round(launch_us, 3)}
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
@@ -249,6 +379,9 @@ def main():
         "decode_ms_per_step": round(dec_mean / T, 4),
         "roofline": roofline,
     }
+    if not args.no_rows:
+        log("rows: streaming step and MomentKV timings ...")
+        out["rows"] = time_rows(torch, api, KL, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on one layer x one sequence ...")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_decode_steps)

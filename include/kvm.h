@@ -303,7 +303,8 @@ kvm_status kvm_moment_readout(const kvm_mread_desc* desc, const void* q, const f
  *                          log Z_E = log n_e + (q.s_k/n_e)/sqrt d,
  *                          w = sigmoid(lse - log Z_E), o = w a + (1 - w) f_E (o = a if n_e = 0)
  * q [b,H_q,d], k_new/v_new [b,H_kv,d] (dtype, nullable), Kc [b,H_kv,cap,d] slot-major and
- * Vc [b,H_kv,d,cap] dim-major (dtype; as written by kvm_compact_kv), cap % 8 == 0,
+ * Vc [b,H_kv,d,cap] dim-major (dtype; as written by kvm_compact_kv), cap % 8 == 0 (a
+ * multiple of 64 keeps every V row on 128-byte lines, the bandwidth-friendly choice),
  * len [b] i32 (not modified), append_slot [b] i32 (nullable), o [b,H_q,d] f32,
  * lse [b,H_q] f32 (nullable: log-partition of the retained attention, scale applied).
  * The library never reads or writes a slot >= cap (n is clamped to cap).

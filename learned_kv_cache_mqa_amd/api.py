@@ -112,8 +112,9 @@ def kvm_topk_select(I, B, R=0, recent_inclusive=True, idx=None, slot_map=None, s
 # ------------------------------------------------------------------------------- compaction
 
 def cache_cap(n):
-    """Smallest cache capacity >= n accepted by the decode kernel (a multiple of 8)."""
-    return (int(n) + 7) // 8 * 8
+    """Cache capacity for n slots: the decode kernel needs a multiple of 8; a multiple of 64
+    puts every V row (dim-major, cap bf16 values) on a 128-byte line boundary."""
+    return (int(n) + 63) // 64 * 64
 
 
 def kvm_compact_kv(Kt, Vt, slot_map, idx, keep, cap=None, Kc=None, Vc=None, M=None, bvec=None, moments=None,

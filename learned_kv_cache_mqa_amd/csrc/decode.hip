@@ -509,7 +509,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 
   const size_t pair = (size_t)bb * a.H_kv + g;
   const ReadoutRegs<D> rregs = readout_load<uint16_t, D, G, NW * 64>(a, c, pair);
-  const Span sp = block_span(a, bb, c, TILE);
+  // split boundaries on 64-slot multiples: with a cap of a multiple of 64 every 128-byte
+  // line of a V row belongs to one block
+  const Span sp = block_span(a, bb, c, 2 * TILE);
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)bb * a.H_q + (size_t)g * G) * D;
   uint16_t* Kp = reinterpret_cast<uint16_t*>(a.Kc) + pair * (size_t)a.cap * D;
   uint16_t* Vt = reinterpret_cast<uint16_t*>(a.Vc) + pair * (size_t)a.cap * D;
