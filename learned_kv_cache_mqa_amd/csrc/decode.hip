@@ -138,21 +138,33 @@ __device__ __forceinline__ ReadoutRegs<D> readout_load(const DecodeArgs& a, int 
   return r;
 }
 
+// Read-out rows of this block: num[h][row] = M_row . feat(q_h) for its slice of rows,
+// feat = phi (memory) or identity (moments); split 0 also writes the per-head scalars
+// (b . phi(q) + eps and the gate, or s_k . q).  Every thread derives the features it needs
+// from q directly (q is a few KB and cached), so no LDS staging and no block barrier
+// hold back the waves whose K/V loads are already in flight.
 template <typename T, int D, int G, int NT>
 __device__ __forceinline__ void readout_compute(const DecodeArgs& a, int c, int g, size_t pair, const T* qp,
-                                                const ReadoutRegs<D>& r, float (*s_feat)[D]) {
+                                                const ReadoutRegs<D>& r) {
   if (a.mode == KVM_READ_NONE) return;
+  const bool mem = a.mode == KVM_READ_MEMORY;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < G * D; i += NT) {
-    const float x = load_scalar<T>(qp + i);
-    s_feat[i / D][i % D] = a.mode == KVM_READ_MEMORY ? phi_f(x) : x;
-  }
-  __syncthreads();
   constexpr int TPR = D / 8;
   static_assert(TPR == 8 || TPR == 16, "row split");
+  constexpr int N = Vec16<T>::N;
   const int rps = (D + a.n_split - 1) / a.n_split;
   constexpr int RPP = NT / TPR;          // rows per pass
   const int c0 = (tid % TPR) * 8;
+  float f[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e0 = 0; e0 < 8; e0 += N) {
+      float x[N];
+      Vec16<T>::load(qp + h * D + c0 + e0, x);
+#pragma unroll
+      for (int e = 0; e < N; ++e) f[h][e0 + e] = mem ? phi_f(x[e]) : x[e];
+    }
   for (int pass = 0; pass * RPP < rps; ++pass) {
     const int rl = pass * RPP + tid / TPR, row = c * rps + rl;
     float mv[8] = {r.m0.x, r.m0.y, r.m0.z, r.m0.w, r.m1.x, r.m1.y, r.m1.z, r.m1.w};
@@ -170,7 +182,7 @@ __device__ __forceinline__ void readout_compute(const DecodeArgs& a, int c, int 
     for (int h = 0; h < G; ++h) {
       float x = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x = fmaf(mv[e], s_feat[h][c0 + e], x);
+      for (int e = 0; e < 8; ++e) x = fmaf(mv[e], f[h][e], x);
       x = group_sum<TPR>(x);
       if (tid % TPR == 0 && rl < rps && row < D) a.num[(pair * G + h) * D + row] = x;
     }
@@ -179,18 +191,19 @@ __device__ __forceinline__ void readout_compute(const DecodeArgs& a, int c, int 
     for (int h = wave; h < G; h += NT / 64) {
       float x0 = 0.f, x1 = 0.f;
       for (int k = lane; k < D; k += 64) {
-        if (a.mode == KVM_READ_MEMORY) {
-          x0 = fmaf(a.bvec[pair * D + k], s_feat[h][k], x0);
+        const float qv = load_scalar<T>(qp + h * D + k);
+        if (mem) {
+          x0 = fmaf(a.bvec[pair * D + k], phi_f(qv), x0);
           const T* wg = reinterpret_cast<const T*>(a.w_g) + (size_t)(g * G + h) * D;
-          x1 = fmaf(load_scalar<T>(wg + k), load_scalar<T>(qp + h * D + k), x1);
+          x1 = fmaf(load_scalar<T>(wg + k), qv, x1);
         } else {
-          x0 = fmaf(a.s_k[pair * D + k], s_feat[h][k], x0);
+          x0 = fmaf(a.s_k[pair * D + k], qv, x0);
         }
       }
       x0 = wave_sum(x0);
       x1 = wave_sum(x1);
       if (lane == 0) {
-        a.red[(pair * 2 + 0) * G + h] = a.mode == KVM_READ_MEMORY ? x0 + a.eps : x0;
+        a.red[(pair * 2 + 0) * G + h] = mem ? x0 + a.eps : x0;
         a.red[(pair * 2 + 1) * G + h] = sigmoid_f(x1);
       }
     }
@@ -208,6 +221,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const size_t pair = (size_t)bb * a.H_kv + g;
   const float* pl = a.part_lse + pair * a.n_split * G + h;
   const float* pa = a.part_a + pair * a.n_split * (size_t)(G * D) + (size_t)h * D + dd;
+  // every load first: the first 8 partial states and the read-out values, in one round
+  float lv[8], av[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    lv[e] = e < a.n_split ? pl[e * G] : -INFINITY;
+    av[e] = e < a.n_split ? pa[(size_t)e * G * D] : 0.f;
+  }
   float num = 0.f, r0 = 1.f, r1 = 0.f, sv = 0.f;
   int ne = 0;
   if (a.mode != KVM_READ_NONE) {
@@ -219,15 +239,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
       ne = a.n_e[pair];
     }
   }
-  // online merge over groups of 8 partial states (one round of loads for n_split <= 8)
+  // online merge of the partial states in chunk order, 8 at a time
   float mx = -INFINITY, z = 0.f, acc = 0.f;
   for (int c0 = 0; c0 < a.n_split; c0 += 8) {
-    float lv[8], av[8];
+    if (c0 > 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int cc = c0 + e;
-      lv[e] = cc < a.n_split ? pl[cc * G] : -INFINITY;
-      av[e] = cc < a.n_split ? pa[(size_t)cc * G * D] : 0.f;
+      for (int e = 0; e < 8; ++e) {
+        const int cc = c0 + e;
+        lv[e] = cc < a.n_split ? pl[cc * G] : -INFINITY;
+        av[e] = cc < a.n_split ? pa[(size_t)cc * G * D] : 0.f;
+      }
     }
     float gm = lv[0];
 #pragma unroll
@@ -285,10 +306,9 @@ __global__ __launch_bounds__(NW * 64) void decode_fma_kernel(DecodeArgs a) {
   const T* kn = a.k_new ? reinterpret_cast<const T*>(a.k_new) + ((size_t)bb * a.H_kv + g) * D : nullptr;
   const T* vn = a.v_new ? reinterpret_cast<const T*>(a.v_new) + ((size_t)bb * a.H_kv + g) * D : nullptr;
   {
-    __shared__ float s_feat[G][D];
     const size_t pair = (size_t)bb * a.H_kv + g;
     const ReadoutRegs<D> rr = readout_load<T, D, G, NW * 64>(a, c, pair);
-    readout_compute<T, D, G, NW * 64>(a, c, g, pair, qp, rr, s_feat);
+    readout_compute<T, D, G, NW * 64>(a, c, g, pair, qp, rr);
   }
 
   float qf[G][EPL];
@@ -505,7 +525,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ float s_acc[NW][G][D];
   __shared__ uint32_t s_p[NW][2][8][TILE / 2];   // per wave: hi/lo, head row, slot pairs
-  __shared__ float s_feat[G][D];
 
   const size_t pair = (size_t)bb * a.H_kv + g;
   const ReadoutRegs<D> rregs = readout_load<uint16_t, D, G, NW * 64>(a, c, pair);
@@ -551,7 +570,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     tile_load_k(ta, t0, sp, Kp, kn, m16, kg);
     tile_load_v(ta, t0, sp, Vt, a.cap, m16, kg);
   }
-  readout_compute<uint16_t, D, G, NW * 64>(a, c, g, pair, qp, rregs, s_feat);
+  readout_compute<uint16_t, D, G, NW * 64>(a, c, g, pair, qp, rregs);
   for (; t0 < sp.j1; t0 += NW * TILE) {
     const int tn = t0 + NW * TILE;
     f32x4_t sc[2];
