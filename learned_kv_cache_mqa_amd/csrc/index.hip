@@ -46,13 +46,27 @@ constexpr int kKpPitch = 36;  // words per LDS row of a weight chunk (64 bf16 + 
 // blocks that hold window positions, a third tile with the H_I (<= 32) gate logits
 // W_g[h] . x, so X is read once for both.  X streams through a ring of XS k-steps in
 // registers; the weight chunk of each k-step is staged in LDS (double-buffered).
-__global__ __launch_bounds__(256) void keyproj_mfma_kernel(IndexArgs a) {
-  constexpr int XS = 4;   // k-steps of X in flight per wave
+// Key projection launch shape: 16 waves x 32 tokens per block share each staged weight
+// chunk, so the weights' L2 traffic per token is a sixteenth of the X stream's; 4 waves per
+// SIMD with two k-steps of X in flight per wave.
+#ifndef KVM_KEYPROJ_WPE
+#define KVM_KEYPROJ_WPE 4
+#endif
+#ifndef KVM_KEYPROJ_XS
+#define KVM_KEYPROJ_XS 2
+#endif
+#ifndef KVM_KEYPROJ_NW
+#define KVM_KEYPROJ_NW 16
+#endif
+constexpr int kKpNW = KVM_KEYPROJ_NW;       // waves per block, 32 tokens each
+constexpr int kKpTB = kKpNW * 32;           // tokens per block
+__global__ __launch_bounds__(kKpNW * 64) __attribute__((amdgpu_waves_per_eu(KVM_KEYPROJ_WPE, KVM_KEYPROJ_WPE))) void keyproj_mfma_kernel(IndexArgs a) {
+  constexpr int XS = KVM_KEYPROJ_XS;   // k-steps of X in flight per wave
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bb = blockIdx.y;
-  const int tb0 = blockIdx.x * 128, t0 = tb0 + wave * 32;
+  const int tb0 = blockIdx.x * kKpTB, t0 = tb0 + wave * 32;
   const int m = lane & 31, kg = lane >> 5;
-  const bool gate = tb0 + 127 >= a.L - a.W && a.gate != nullptr;   // block-uniform
+  const bool gate = tb0 + kKpTB - 1 >= a.L - a.W && a.gate != nullptr;   // block-uniform
   __shared__ uint32_t sW[2][96 * kKpPitch];
   const uint16_t* X = reinterpret_cast<const uint16_t*>(a.X) + (size_t)bb * a.L * a.D;
   const uint16_t* Wk = reinterpret_cast<const uint16_t*>(a.W_kI);
@@ -64,15 +78,16 @@ __global__ __launch_bounds__(256) void keyproj_mfma_kernel(IndexArgs a) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) { acc0[j] = 0.f; acc1[j] = 0.f; acc2[j] = 0.f; }
 
-  // weight chunk rows: 0..63 W_kI, 64..95 W_g (zero beyond H_I); 768 uint4 over 256 threads
+  // weight chunk rows: 0..63 W_kI, 64..95 W_g (zero beyond H_I); 768 uint4 over the threads
+  constexpr int NT = kKpNW * 64, NE = (768 + NT - 1) / NT;
   const int wq = tid & 7;
+  const int wrows = gate ? 96 : 64;   // rows in use
   auto wsrc = [&](int i, int k0) -> uint4 {
-    const int row = (tid + i * 256) >> 3;
+    const int row = (tid + i * NT) >> 3;
     if (row < 64) return *reinterpret_cast<const uint4*>(Wk + (size_t)row * a.D + k0 + wq * 8);
-    if (row - 64 < a.H_I) return *reinterpret_cast<const uint4*>(Wg + (size_t)(row - 64) * a.D + k0 + wq * 8);
+    if (row < wrows && row - 64 < a.H_I) return *reinterpret_cast<const uint4*>(Wg + (size_t)(row - 64) * a.D + k0 + wq * 8);
     return make_uint4(0, 0, 0, 0);
   };
-  const int nwl = gate ? 3 : 2;   // rows in use: 64 or 96
   const int nk = a.D / 64;
   // Each block starts its k loop at a different k-step so that the blocks' concurrent X
   // reads (rows 2*D bytes apart) spread over the HBM channels instead of all hitting the
@@ -81,17 +96,23 @@ __global__ __launch_bounds__(256) void keyproj_mfma_kernel(IndexArgs a) {
   auto kofs = [&](int ks) { int k = ks + rot; return (k >= nk ? k - nk : k) * 64; };
   // Weight chunks run two k-steps ahead: the chunk of step ks + 2 is loaded at step ks into
   // one register set while the other set (step ks + 1) is written to the idle LDS buffer.
-  uint4 w[2][3];
+  uint4 w[2][NE];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) w[h][0] = w[h][1] = w[h][2] = make_uint4(0, 0, 0, 0);
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < NE; ++i) w[h][i] = make_uint4(0, 0, 0, 0);
   auto wload = [&](int h, int ks) {
     const int k = kofs(ks);
-    w[h][0] = wsrc(0, k); w[h][1] = wsrc(1, k); if (nwl == 3) w[h][2] = wsrc(2, k);
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+      if (((tid + i * NT) >> 3) < wrows) w[h][i] = wsrc(i, k);
   };
   auto wstore = [&](int h, int buf) {
-    *reinterpret_cast<uint4*>(&sW[buf][((tid) >> 3) * kKpPitch + wq * 4]) = w[h][0];
-    *reinterpret_cast<uint4*>(&sW[buf][((tid + 256) >> 3) * kKpPitch + wq * 4]) = w[h][1];
-    if (nwl == 3) *reinterpret_cast<uint4*>(&sW[buf][((tid + 512) >> 3) * kKpPitch + wq * 4]) = w[h][2];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int e = tid + i * NT;
+      if ((e >> 3) < wrows) *reinterpret_cast<uint4*>(&sW[buf][(e >> 3) * kKpPitch + wq * 4]) = w[h][i];
+    }
   };
   wload(0, 0);
   if (nk > 1) wload(1, 1);
@@ -499,7 +520,7 @@ extern "C" kvm_status kvm_index_score(const kvm_index_desc* d, const void* X, co
   const bool mfma = bf && d->d_I == 64 && d->H_I <= 32 && d->d == 128 && d->D % 64 == 0 && d->W % 32 == 0;
   a.gate = mfma ? reinterpret_cast<float*>(base + w.gate) : nullptr;
   if (mfma)
-    hipLaunchKernelGGL(keyproj_mfma_kernel, dim3((d->L + 127) / 128, d->b), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(keyproj_mfma_kernel, dim3((d->L + kKpTB - 1) / kKpTB, d->b), dim3(kKpNW * 64), 0, s, a);
   else if (bf)
     hipLaunchKernelGGL(keyproj_valu_kernel<uint16_t>, dim3((d->L + 15) / 16, d->b), dim3(256), 0, s, a);
   else
