@@ -125,6 +125,12 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Buffer resource over `bytes` bytes from `base`: loads at offsets past the end return zeros
+// without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 __device__ __forceinline__ float sigmoid_f(float x) {
   float e = __expf(-fabsf(x));

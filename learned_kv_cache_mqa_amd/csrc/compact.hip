@@ -86,11 +86,6 @@ __global__ __launch_bounds__(256) void compact_reduce_kernel(CompactArgs a) {
 constexpr int kTok = 32;
 constexpr int kPitch = 18;
 
-// Buffer resource over `bytes` bytes from `base`: loads at offsets past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-
 // Stages one tile of 32 tokens for the contraction: this thread holds tokens (2 pr, 2 pr + 1)
 // x dims db*8 .. db*8+8 of K and V.  Writes V^T (exact bf16) to sV and u = w phi(k) (memory)
 // or k (moments) to sH (+ the bf16 remainder of u to sL in memory mode), one word per token

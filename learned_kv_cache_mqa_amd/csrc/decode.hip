@@ -1,31 +1,39 @@
 // A8 + A9 (+ V3): split-K decode attention over the retained cache, merged with the
 // online-softmax identity, plus the latent-memory (or moment) read-out.
 //
-// Attention states: each block reduces one slot range of one (sequence, KV head) to a
-// state (a_c, lse_c) per query head of the GQA group -- the attention output and the log
-// of its normaliser [ASM, Method: attention state (a, Z)].  The last block to finish for a
-// (sequence, KV head) merges the states in chunk order: lse = log sum exp(lse_c),
-// a = sum exp(lse_c - lse) a_c [ASM, Method: online-softmax merge], then adds the read-out
+// Attention states: a state (a_c, lse_c) per query head of the GQA group is the attention
+// output over a set of slots and the log of its normaliser [ASM, Method: attention state
+// (a, Z)].  States over disjoint sets merge in a fixed order: lse = log sum exp(lse_c),
+// a = sum exp(lse_c - lse) a_c [ASM, Method: online-softmax merge].  The read-out adds
 // o = a + g(q) m(q) with m(q) = M phi(q) / (b . phi(q) + eps), g(q) = sigmoid(w_g . q)
 // [IM 2.B, output], or mixes with the moment estimate [MKV 2, 4].
 //
 // Cache layout: Kc [b, H_kv, cap, d] (slot-major), Vc [b, H_kv, d, cap] (dim-major).
 //
-// bf16, d = 128 (matrix-core path): a wave takes 32-slot tiles.  S = q K^T runs on
-// v_mfma_f32_16x16x32_bf16 with the G query heads as rows (padded to 16) and K read
-// straight from HBM into B-operand registers (4 lanes x 16 bytes = 64 contiguous bytes of
-// a row per instruction).  P V runs on the same instruction with P (bf16 hi + lo, 16-bit
-// accurate) as the A operand and the dim-major V cache as the B operand: each lane reads
-// 8 consecutive slots of one dim, 16 contiguous bytes.  Loads roll: the next tile's K
-// loads are issued into the K registers as soon as S is computed and its V loads as soon
-// as P V is done, so one tile of loads is always in flight per wave.  K/V bytes are read
-// once for all G heads.  Other shapes (fp32, d = 64) use an FMA path.
+// Two kernels:
+//  attention  grid (n_split, H_kv, b): each block reduces the cached slots of one slot range
+//             of one (sequence, KV head) to a state per query head.  The slot that takes
+//             the new token is skipped (its cached contents are stale); the block writes its
+//             share of the new token's dims into that slot.  The block also computes its
+//             slice of the read-out rows M phi(q).
+//  merge      grid (d / 32, H_kv, b): thread (h, dim) merges the block states in chunk order,
+//             then the new token's own state (a = v_new, lse = scale q . k_new), and adds the
+//             read-out.  The kernel boundary makes the block states visible across the
+//             chip's XCDs; a per-block release/acquire handshake inside one kernel would cost
+//             an L2 write-back per block on this part.
 //
-// Two kernels: the attention kernel writes one partial state per block; the merge kernel
-// (one block per 32 output dims of a (sequence, KV head)) merges them in chunk order and
-// computes the read-out rows M phi(q) for its dims.  The kernel boundary makes the partial
-// states visible across the chip's XCDs; a per-block release/acquire handshake inside one
-// kernel costs an L2 write-back and invalidate per block on this part.
+// bf16, d = 128 (matrix-core path): a wave takes 32-slot tiles.  The scores run on
+// v_mfma_f32_16x16x32_bf16 as S^T = K q^T: K rows (read straight from HBM, 4 lanes x 16
+// bytes = 64 contiguous bytes of a row per instruction) are the A operand, in a slot order
+// chosen so that each lane ends up holding one head's scores for 8 consecutive slots.  That
+// is the A-operand layout of P V, which runs on the same instruction with P (bf16 hi + lo,
+// 16-bit accurate) and the dim-major V cache as the B operand (each lane reads 8 consecutive
+// slots of one dim, 16 contiguous bytes).  So P stays in registers, and the softmax needs a
+// cross-lane step only for the tile max.  Every K/V load is a raw buffer load: lanes whose
+// slots lie past the block's range use an offset past the buffer's end and read zeros
+// without touching memory, so no load sits behind a branch and each wait is for exactly the
+// tile being consumed.  K/V bytes are read once for all G heads.  Other shapes (fp32,
+// d = 64) use an FMA path.
 #include "common.hpp"
 
 namespace kvm {
@@ -51,7 +59,6 @@ struct DecodeArgs {
   float* part_a;    // [b, H_kv, n_split, G, D]
   float* part_lse;  // [b, H_kv, n_split, G]
   float* num;       // [b, H_kv, G, D]   read-out numerator rows
-  float* red;       // [b, H_kv, 2, G]   read-out denominator (+eps) and gate, or s_k . q
   int b, H_q, H_kv, cap, n_split, mode;
   float scale, eps;
 };
@@ -67,13 +74,32 @@ struct Span {
   int n, app, j0, j1;
 };
 
+// The sequence's cache length and append slot (read once, early: their latency overlaps
+// the loads that do not depend on them).
+struct SeqLen {
+  int len0, aslot;
+};
+// Read as vector loads: they count in order with the other vector loads, so waiting for
+// them does not wait for loads issued after (scalar loads return out of order, and a wait
+// for any later kernel argument would wait for these too).  Callers issue their other
+// loads, then a scheduling barrier, then use the values: the compiler would otherwise move
+// the values to scalar registers, and so wait for them, ahead of the other loads.
+__device__ __forceinline__ SeqLen seq_len(const DecodeArgs& a, int bb) {
+  const int l = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.len + bb, 4), 0, 0, 0);
+  // no append_slot: a zero-sized buffer, whose load reads 0 without touching memory
+  const int s = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.append_slot + bb, a.append_slot ? 4 : 0), 0, 0, 0);
+  return SeqLen{l, s};
+}
+__device__ __forceinline__ SeqLen uniform(SeqLen q) {
+  return SeqLen{__builtin_amdgcn_readfirstlane(q.len0), __builtin_amdgcn_readfirstlane(q.aslot)};
+}
+
 // tokens attended, append slot and this block's slot range (multiples of `align`)
-__device__ __forceinline__ Span block_span(const DecodeArgs& a, int bb, int c, int align) {
+__device__ __forceinline__ Span block_span(const DecodeArgs& a, int c, int align, SeqLen q) {
   Span s;
-  const int len0 = a.len[bb];
-  if (!a.k_new) { s.n = len0; s.app = -1; }
-  else if (a.append_slot) { s.n = len0; s.app = a.append_slot[bb]; }
-  else { s.n = len0 + 1; s.app = len0; }
+  if (!a.k_new) { s.n = q.len0; s.app = -1; }
+  else if (a.append_slot) { s.n = q.len0; s.app = q.aslot; }
+  else { s.n = q.len0 + 1; s.app = q.len0; }
   s.n = min(max(s.n, 0), a.cap);
   if (s.app < 0 || s.app >= a.cap) s.app = -1;
   int per = (s.n + a.n_split - 1) / a.n_split;
@@ -81,6 +107,62 @@ __device__ __forceinline__ Span block_span(const DecodeArgs& a, int bb, int c, i
   s.j0 = c * per;
   s.j1 = min(s.n, s.j0 + per);
   return s;
+}
+
+// ------------------------------------------------------------------ new token -> caches
+// Each attention block writes its share of dims [c*dpb, (c+1)*dpb) of the new token into slot
+// app of the caches (when the token is attended: app < n).  No block reads that slot's
+// contents (it is masked), so the write may land at any time during the launch.
+template <typename T, int D>
+struct NewTok {
+  T k, v;
+};
+
+template <typename T>
+__device__ __forceinline__ T buffer_elem(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(T) == 2) {
+    return (T)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  } else {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+}
+
+// NB bytes (4, 8 or 16) at byte offset `off` of a buffer, as raw bits into `out`
+template <int NB, typename U>
+__device__ __forceinline__ void buffer_bytes(__amdgpu_buffer_rsrc_t r, uint32_t off, U* out) {
+  static_assert(NB == 4 || NB == 8 || NB == 16, "bytes");
+  if constexpr (NB == 4) {
+    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    __builtin_memcpy(out, &v, 4);
+  } else if constexpr (NB == 8) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    __builtin_memcpy(out, &v, 8);
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    __builtin_memcpy(out, &v, 16);
+  }
+}
+
+// branch-free: lanes without a dim (or calls without a new token) read past a buffer's end
+template <typename T, int D>
+__device__ __forceinline__ NewTok<T, D> new_token_load(const DecodeArgs& a, int c, size_t pair) {
+  const int dpb = (D + a.n_split - 1) / a.n_split, d = c * dpb + (int)threadIdx.x;
+  const int bytes = a.k_new ? D * (int)sizeof(T) : 0;
+  const uint32_t off = ((int)threadIdx.x < dpb && d < D) ? d * sizeof(T) : D * sizeof(T);
+  NewTok<T, D> r;
+  r.k = buffer_elem<T>(make_rsrc(reinterpret_cast<const T*>(a.k_new) + pair * D, bytes), off);
+  r.v = buffer_elem<T>(make_rsrc(reinterpret_cast<const T*>(a.v_new) + pair * D, bytes), off);
+  return r;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void new_token_store(const DecodeArgs& a, int c, size_t pair, const Span& sp,
+                                                const NewTok<T, D>& r) {
+  const int dpb = (D + a.n_split - 1) / a.n_split, d = c * dpb + (int)threadIdx.x;
+  if (sp.app >= 0 && sp.app < sp.n && (int)threadIdx.x < dpb && d < D) {
+    reinterpret_cast<T*>(a.Kc)[(pair * a.cap + sp.app) * D + d] = r.k;
+    reinterpret_cast<T*>(a.Vc)[(pair * D + d) * a.cap + sp.app] = r.v;
+  }
 }
 
 // ------------------------------------------------------------------ block partial state
@@ -101,145 +183,158 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, int c, int g,
     if (mx != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float f = exp2f(s_m[w][h] - mx);
+        const float f = __builtin_amdgcn_exp2f(s_m[w][h] - mx);   // exp2(-inf) = 0
         L = fmaf(s_l[w][h], f, L);
         A = fmaf(s_acc[w][h][dd], f, A);
       }
     }
-    pa[i] = L > 0.f ? A / L : 0.f;
-    if (dd == 0) a.part_lse[(pair * a.n_split + c) * G + h] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
+    // L >= 1 when positive (the max term contributes 2^0), so the hardware reciprocal and
+    // log2 are in their accurate range
+    pa[i] = L > 0.f ? A * __builtin_amdgcn_rcpf(L) : 0.f;
+    if (dd == 0) a.part_lse[(pair * a.n_split + c) * G + h] = L > 0.f ? (mx + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
   }
 }
 
-// ------------------------------------------------------------------ read-out inputs
-// Run by every attention block before its tile loop: the block's slice of read-out rows
-// num[h][r] = Mat[r] . feat_h (feat = phi(q) for the memory, q for the moments), and in
-// block 0 the per-head scalars (b . phi(q) + eps and the gate sigmoid(w_g . q), or s_k . q).
-// The row loads are issued by the caller before the first K/V tile, so their latency
-// overlaps the K/V stream.
-template <int D>
+// ------------------------------------------------------------------ read-out rows
+// Each attention block computes a slice of the read-out rows num[h][r] = Mat[r] . feat(q_h)
+// (feat = phi for the memory, the identity for the moments): thread t takes 8 consecutive
+// columns c0 = (t % (D/8)) * 8 of row t / (D/8) of its slice.  The first pass's operands
+// (the Mat row piece and q[h][c0 .. c0+8] for every head) are loaded before the K/V stream,
+// so their latency overlaps it; rows beyond the first pass (only with very few splits) are
+// done after the stream.
+template <typename T, int G>
 struct ReadoutRegs {
-  float4 m0, m1;   // 8 consecutive floats of one Mat row
+  float4 m0, m1;                    // Mat[row][c0 .. c0+8]
+  uint4 qr[G][8 / Vec16<T>::N];     // q[h][c0 .. c0+8], raw
 };
 
+// Branch-free: without a read-out (or for lanes without a row) the Mat loads read past a
+// buffer's end; q is always there.
 template <typename T, int D, int G, int NT>
-__device__ __forceinline__ ReadoutRegs<D> readout_load(const DecodeArgs& a, int c, size_t pair) {
-  ReadoutRegs<D> r;
-  r.m0 = r.m1 = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (a.mode == KVM_READ_NONE) return r;
-  constexpr int TPR = D / 8;             // threads per row
-  const int rps = (D + a.n_split - 1) / a.n_split;
-  const int row = c * rps + threadIdx.x / TPR;
-  if (threadIdx.x / TPR < rps && row < D && threadIdx.x < NT) {
-    const float* p = a.rmat + pair * (size_t)(D * D) + (size_t)row * D + (threadIdx.x % TPR) * 8;
-    r.m0 = *reinterpret_cast<const float4*>(p);
-    r.m1 = *reinterpret_cast<const float4*>(p + 4);
-  }
-  return r;
-}
-
-// Read-out rows of this block: num[h][row] = M_row . feat(q_h) for its slice of rows,
-// feat = phi (memory) or identity (moments); split 0 also writes the per-head scalars
-// (b . phi(q) + eps and the gate, or s_k . q).  Every thread derives the features it needs
-// from q directly (q is a few KB and cached), so no LDS staging and no block barrier
-// hold back the waves whose K/V loads are already in flight.
-template <typename T, int D, int G, int NT>
-__device__ __forceinline__ void readout_compute(const DecodeArgs& a, int c, int g, size_t pair, const T* qp,
-                                                const ReadoutRegs<D>& r) {
-  if (a.mode == KVM_READ_NONE) return;
-  const bool mem = a.mode == KVM_READ_MEMORY;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int TPR = D / 8;
-  static_assert(TPR == 8 || TPR == 16, "row split");
-  constexpr int N = Vec16<T>::N;
-  const int rps = (D + a.n_split - 1) / a.n_split;
-  constexpr int RPP = NT / TPR;          // rows per pass
-  const int c0 = (tid % TPR) * 8;
-  float f[G][8];
+__device__ __forceinline__ void readout_load(ReadoutRegs<T, G>& r, const DecodeArgs& a, int c, size_t pair,
+                                             const T* qp) {
+  constexpr int N = Vec16<T>::N, TPR = D / 8;
+  const int c0 = (threadIdx.x % TPR) * 8;
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e0 = 0; e0 < 8; e0 += N) {
-      float x[N];
-      Vec16<T>::load(qp + h * D + c0 + e0, x);
+    for (int j = 0; j < 8 / N; ++j) r.qr[h][j] = *reinterpret_cast<const uint4*>(qp + h * D + c0 + j * N);
+  const int rps = (D + a.n_split - 1) / a.n_split;
+  const int row = c * rps + threadIdx.x / TPR;
+  const bool on = a.mode != KVM_READ_NONE;
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(a.rmat + pair * (size_t)(D * D), on ? D * D * 4 : 0);
+  const uint32_t off = (on && (int)threadIdx.x / TPR < rps && row < D) ? (row * D + c0) * 4 : D * D * 4;
+  const auto m0 = __builtin_amdgcn_raw_buffer_load_b128(rm, off, 0, 0);
+  const auto m1 = __builtin_amdgcn_raw_buffer_load_b128(rm, off + 16, 0, 0);
+  r.m0 = make_float4(__uint_as_float(m0[0]), __uint_as_float(m0[1]), __uint_as_float(m0[2]), __uint_as_float(m0[3]));
+  r.m1 = make_float4(__uint_as_float(m1[0]), __uint_as_float(m1[1]), __uint_as_float(m1[2]), __uint_as_float(m1[3]));
+}
+
+// num[h][row] for one pass of rows, from operands in registers
+template <typename T, int D, int G>
+__device__ __forceinline__ void readout_pass(const DecodeArgs& a, size_t pair, int rl, int rps, int row,
+                                             const float4& m0, const float4& m1, const uint4 (&qr)[G][8 / Vec16<T>::N]) {
+  constexpr int N = Vec16<T>::N, TPR = D / 8;
+  static_assert(TPR == 8 || TPR == 16, "row split");
+  const bool mem = a.mode == KVM_READ_MEMORY;
+  const float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
-      for (int e = 0; e < N; ++e) f[h][e0 + e] = mem ? phi_f(x[e]) : x[e];
-    }
-  for (int pass = 0; pass * RPP < rps; ++pass) {
-    const int rl = pass * RPP + tid / TPR, row = c * rps + rl;
-    float mv[8] = {r.m0.x, r.m0.y, r.m0.z, r.m0.w, r.m1.x, r.m1.y, r.m1.z, r.m1.w};
-    if (pass > 0) {   // rows beyond the first pass (few split blocks): load them now
-      float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0;
-      if (rl < rps && row < D) {
-        const float* p = a.rmat + pair * (size_t)(D * D) + (size_t)row * D + c0;
-        m0 = *reinterpret_cast<const float4*>(p);
-        m1 = *reinterpret_cast<const float4*>(p + 4);
-      }
-      mv[0] = m0.x; mv[1] = m0.y; mv[2] = m0.z; mv[3] = m0.w;
-      mv[4] = m1.x; mv[5] = m1.y; mv[6] = m1.z; mv[7] = m1.w;
-    }
+  for (int h = 0; h < G; ++h) {
+    float x = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float x = 0.f;
+    for (int j = 0; j < 8 / N; ++j) {
+      float f[N];
+      Vec16<T>::unpack(qr[h][j], f);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x = fmaf(mv[e], f[h][e], x);
-      x = group_sum<TPR>(x);
-      if (tid % TPR == 0 && rl < rps && row < D) a.num[(pair * G + h) * D + row] = x;
+      for (int e = 0; e < N; ++e) x = fmaf(mv[j * N + e], mem ? phi_f(f[e]) : f[e], x);
     }
+    x = group_sum<TPR>(x);
+    if (threadIdx.x % TPR == 0 && rl < rps && row < D) a.num[(pair * G + h) * D + row] = x;
   }
-  if (c == 0) {
-    for (int h = wave; h < G; h += NT / 64) {
-      float x0 = 0.f, x1 = 0.f;
-      for (int k = lane; k < D; k += 64) {
-        const float qv = load_scalar<T>(qp + h * D + k);
-        if (mem) {
-          x0 = fmaf(a.bvec[pair * D + k], phi_f(qv), x0);
-          const T* wg = reinterpret_cast<const T*>(a.w_g) + (size_t)(g * G + h) * D;
-          x1 = fmaf(load_scalar<T>(wg + k), qv, x1);
-        } else {
-          x0 = fmaf(a.s_k[pair * D + k], qv, x0);
-        }
-      }
-      x0 = wave_sum(x0);
-      x1 = wave_sum(x1);
-      if (lane == 0) {
-        a.red[(pair * 2 + 0) * G + h] = mem ? x0 + a.eps : x0;
-        a.red[(pair * 2 + 1) * G + h] = sigmoid_f(x1);
-      }
+}
+
+template <typename T, int D, int G, int NT>
+__device__ __forceinline__ void readout_first(const DecodeArgs& a, int c, size_t pair, const ReadoutRegs<T, G>& r) {
+  if (a.mode == KVM_READ_NONE) return;
+  constexpr int TPR = D / 8;
+  const int rps = (D + a.n_split - 1) / a.n_split;
+  const int rl = threadIdx.x / TPR;
+  readout_pass<T, D, G>(a, pair, rl, rps, c * rps + rl, r.m0, r.m1, r.qr);
+}
+
+template <typename T, int D, int G, int NT>
+__device__ __forceinline__ void readout_rest(const DecodeArgs& a, int c, size_t pair, const T* qp) {
+  constexpr int N = Vec16<T>::N, TPR = D / 8, RPP = NT / TPR;
+  const int rps = (D + a.n_split - 1) / a.n_split;
+  if (a.mode == KVM_READ_NONE || rps <= RPP) return;
+  const int c0 = (threadIdx.x % TPR) * 8;
+  uint4 qr[G][8 / N];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int j = 0; j < 8 / N; ++j) qr[h][j] = *reinterpret_cast<const uint4*>(qp + h * D + c0 + j * N);
+  for (int pass = 1; pass * RPP < rps; ++pass) {
+    const int rl = pass * RPP + threadIdx.x / TPR, row = c * rps + rl;
+    float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0;
+    if (rl < rps && row < D) {
+      const float* p = a.rmat + pair * (size_t)(D * D) + (size_t)row * D + c0;
+      m0 = *reinterpret_cast<const float4*>(p);
+      m1 = *reinterpret_cast<const float4*>(p + 4);
     }
+    readout_pass<T, D, G>(a, pair, rl, rps, row, m0, m1, qr);
   }
 }
 
 // ------------------------------------------------------------------ merge
-// grid (D / 32, H_kv, b), 32 * G threads: thread (h, dim) merges the n_split partial states
-// of one output element in chunk order and adds the read-out.  One round of loads.
-template <int D, int G>
+// grid (D / 32, H_kv, b), 32 * G threads: thread (h, dim) merges the n_split block states of
+// one output element in chunk order, then the new token's state, and adds the read-out.
+// The 32 threads of a head also form the head's dot products (q . k_new, b . phi(q),
+// w_g . q or s_k . q) from D / 32 elements each.  Every load goes out in one round, before
+// anything waits: values are kept as raw bits until all loads are issued.
+template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int E = D / 32;
   const int rb = blockIdx.x, g = blockIdx.y, bb = blockIdx.z;
-  const int h = threadIdx.x >> 5, dd = rb * 32 + (threadIdx.x & 31);
+  const int h = threadIdx.x >> 5, l32 = threadIdx.x & 31, dd = rb * 32 + l32;
   if (h >= G) return;
   const size_t pair = (size_t)bb * a.H_kv + g;
+  const SeqLen sl = seq_len(a, bb);
   const float* pl = a.part_lse + pair * a.n_split * G + h;
   const float* pa = a.part_a + pair * a.n_split * (size_t)(G * D) + (size_t)h * D + dd;
-  // every load first: the first 8 partial states and the read-out values, in one round
+  const T* qh = reinterpret_cast<const T*>(a.q) + ((size_t)bb * a.H_q + (size_t)g * G + h) * D + l32 * E;
+  const bool mem = a.mode == KVM_READ_MEMORY, mom = a.mode == KVM_READ_MOMENTS;
   float lv[8], av[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     lv[e] = e < a.n_split ? pl[e * G] : -INFINITY;
     av[e] = e < a.n_split ? pa[(size_t)e * G * D] : 0.f;
   }
-  float num = 0.f, r0 = 1.f, r1 = 0.f, sv = 0.f;
-  int ne = 0;
-  if (a.mode != KVM_READ_NONE) {
-    num = a.num[(pair * G + h) * D + dd];
-    r0 = a.red[(pair * 2 + 0) * G + h];
-    r1 = a.red[(pair * 2 + 1) * G + h];
-    if (a.mode == KVM_READ_MOMENTS) {
-      sv = a.s_v[pair * D + dd];
-      ne = a.n_e[pair];
-    }
-  }
-  // online merge of the partial states in chunk order, 8 at a time
+  // optional inputs through buffers of size 0 when absent (their loads read zeros), so no
+  // load sits behind a branch
+  constexpr int EB = E * (int)sizeof(T);   // bytes of a head's D / 32 elements
+  T qr[E], kr[E], wr[E];
+  float xr[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) qr[e] = qh[e];
+  const int tb = (int)sizeof(T);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k_new) + pair * D, a.k_new ? D * tb : 0);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v_new) + pair * D, a.k_new ? D * tb : 0);
+  // (resource bases are per (sequence, KV head), uniform across the wave; the head goes in
+  // the offset)
+  const __amdgpu_buffer_rsrc_t rn = make_rsrc(a.num + pair * G * D, (mem || mom) ? G * D * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc((mem ? a.bvec : a.s_k) + pair * D, (mem || mom) ? D * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(reinterpret_cast<const T*>(a.w_g) + (size_t)g * G * D, mem ? G * D * tb : 0);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.s_v + pair * D, mom ? D * 4 : 0);
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(a.n_e + pair, mom ? 4 : 0);
+  buffer_bytes<EB>(rk, l32 * EB, kr);
+  buffer_bytes<EB>(rw, h * D * tb + l32 * EB, wr);
+  buffer_bytes<E * 4>(rx, l32 * E * 4, xr);
+  const T vr = buffer_elem<T>(rv, dd * tb);
+  const float num = buffer_elem<float>(rn, (h * D + dd) * 4);
+  const float sv = buffer_elem<float>(rs, dd * 4);
+  const int ne = (int)__builtin_amdgcn_raw_buffer_load_b32(re, 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // online merge of the block states in chunk order, 8 at a time
   float mx = -INFINITY, z = 0.f, acc = 0.f;
   for (int c0 = 0; c0 < a.n_split; c0 += 8) {
     if (c0 > 0) {
@@ -267,17 +362,40 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
       mx = nm;
     }
   }
+  // head dot products: q . k_new, b . phi(q) or s_k . q, w_g . q
+  float s_new = 0.f, x0 = 0.f, x1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float qv = load_scalar<T>(&qr[e]);
+    s_new = fmaf(qv, load_scalar<T>(&kr[e]), s_new);
+    x0 = fmaf(xr[e], mem ? phi_f(qv) : qv, x0);
+    x1 = fmaf(load_scalar<T>(&wr[e]), qv, x1);
+  }
+  s_new = group_sum<32>(s_new);
+  x0 = group_sum<32>(x0);
+  x1 = group_sum<32>(x1);
+  // the new token's state: a = v_new, lse = scale q . k_new
+  const Span sp = block_span(a, 0, 1, uniform(sl));
+  if (sp.app >= 0 && sp.app < sp.n) {
+    const float ls = a.scale * s_new;
+    const float nm = fmaxf(mx, ls);
+    const float f = mx == -INFINITY ? 0.f : __expf(mx - nm);
+    const float w = __expf(ls - nm);
+    z = fmaf(z, f, w);
+    acc = fmaf(acc, f, w * load_scalar<T>(&vr));
+    mx = nm;
+  }
   float lse = -INFINITY, o = 0.f;
   if (mx != -INFINITY && z > 0.f) {
     lse = mx + __logf(z);
     o = acc / z;
   }
-  if (a.mode == KVM_READ_MEMORY) {
-    o = fmaf(r1, num / r0, o);
-  } else if (a.mode == KVM_READ_MOMENTS && ne > 0) {
+  if (mem) {
+    o = fmaf(sigmoid_f(x1), num / (x0 + a.eps), o);
+  } else if (mom && ne > 0) {
     const float inv = 1.f / (float)ne;
-    const float fE = sv * inv + a.scale * (num - sv * r0 * inv) * inv;
-    const float logZ = __logf((float)ne) + a.scale * r0 * inv;
+    const float fE = sv * inv + a.scale * (num - sv * x0 * inv) * inv;
+    const float logZ = __logf((float)ne) + a.scale * x0 * inv;
     const float w = sigmoid_f(lse - logZ);
     o = w * o + (1.f - w) * fE;
   }
@@ -298,17 +416,17 @@ __global__ __launch_bounds__(NW * 64) void decode_fma_kernel(DecodeArgs a) {
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ float s_acc[NW][G][D];
 
-  const Span sp = block_span(a, bb, c, 1);
+  const Span sp = block_span(a, c, 1, uniform(seq_len(a, bb)));
   const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)bb * a.H_q + (size_t)g * G) * D;
   const size_t cache_off = ((size_t)bb * a.H_kv + g) * (size_t)a.cap * D;
   T* Kp = reinterpret_cast<T*>(a.Kc) + cache_off;
   T* Vt = reinterpret_cast<T*>(a.Vc) + cache_off;   // [D][cap]
-  const T* kn = a.k_new ? reinterpret_cast<const T*>(a.k_new) + ((size_t)bb * a.H_kv + g) * D : nullptr;
-  const T* vn = a.v_new ? reinterpret_cast<const T*>(a.v_new) + ((size_t)bb * a.H_kv + g) * D : nullptr;
+  const size_t pair = (size_t)bb * a.H_kv + g;
+  const NewTok<T, D> nt = new_token_load<T, D>(a, c, pair);
   {
-    const size_t pair = (size_t)bb * a.H_kv + g;
-    const ReadoutRegs<D> rr = readout_load<T, D, G, NW * 64>(a, c, pair);
-    readout_compute<T, D, G, NW * 64>(a, c, g, pair, qp, rr);
+    ReadoutRegs<T, G> rr;
+    readout_load<T, D, G, NW * 64>(rr, a, c, pair, qp);
+    readout_first<T, D, G, NW * 64>(a, c, pair, rr);
   }
 
   float qf[G][EPL];
@@ -329,22 +447,14 @@ __global__ __launch_bounds__(NW * 64) void decode_fma_kernel(DecodeArgs a) {
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
   for (int j = sp.j0 + wave * TPI + grp; j < sp.j1; j += NW * TPI) {
-    const bool is_new = (j == sp.app);
+    // the slot that takes the new token is skipped: its cached contents are stale
+    const bool skip = (j == sp.app);
     float kf[EPL], vf[EPL];
-    if (is_new) {
-      const uint4 kraw = *reinterpret_cast<const uint4*>(kn + sub * EPL);
-      *reinterpret_cast<uint4*>(Kp + (size_t)j * D + sub * EPL) = kraw;
-      Vec16<T>::unpack(kraw, kf);
+    Vec16<T>::load(Kp + (size_t)j * D + sub * EPL, kf);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const T v = vn[sub * EPL + e];
-        Vt[(size_t)(sub * EPL + e) * a.cap + j] = v;
-        vf[e] = load_scalar<T>(&v);
-      }
-    } else {
-      Vec16<T>::load(Kp + (size_t)j * D + sub * EPL, kf);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) vf[e] = load_scalar<T>(Vt + (size_t)(sub * EPL + e) * a.cap + j);
+    for (int e = 0; e < EPL; ++e) {
+      const float v = load_scalar<T>(Vt + (size_t)(sub * EPL + e) * a.cap + j);
+      vf[e] = skip ? 0.f : v;
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -352,15 +462,17 @@ __global__ __launch_bounds__(NW * 64) void decode_fma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) s = fmaf(qf[h][e], kf[e], s);
       s = group_sum<LPT>(s);
-      const float mn = fmaxf(m[h], s);
-      const float cf = exp2f(m[h] - mn);
-      const float p = exp2f(s - mn);
+      const float mn = skip ? m[h] : fmaxf(m[h], s);
+      const float cf = skip ? 1.f : exp2f(m[h] - mn);
+      const float p = skip ? 0.f : exp2f(s - mn);
       l[h] = fmaf(l[h], cf, p);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(acc[h][e], cf, p * vf[e]);
       m[h] = mn;
     }
   }
+  readout_rest<T, D, G, NW * 64>(a, c, pair, qp);
+  new_token_store<T, D>(a, c, pair, sp, nt);
   // merge the TPI lane groups of the wave
 #pragma unroll
   for (int msk = LPT; msk < 64; msk <<= 1) {
@@ -398,199 +510,241 @@ struct TileRegs {
   uint4 v[8];      // V dims dt*16 + m16, slots t0 + kg*8 .. +8
 };
 
-__device__ __forceinline__ void tile_load_k(TileRegs& T, int t0, const Span& sp, const uint16_t* Kp,
-                                            const uint16_t* kn, int m16, int kg) {
-  constexpr int D = 128;
+// The K rows [cap][D] and V rows [D][cap] of a (sequence, KV head) as buffers; `*_oob` is an
+// offset past each buffer's end (loads there read zeros).
+struct TileBufs {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t k_oob, v_oob, v_row;   // v_row: bytes per V row (2 cap)
+};
+
+__device__ __forceinline__ uint4 as_uint4(const __attribute__((ext_vector_type(4))) unsigned int& v) {
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// K rows of a tile, permuted: for slot group gq, MFMA row m = 4a + i holds slot a*8 + gq*4 + i.
+// With K as the A operand and q as the B operand, S^T = K q^T then leaves the scores of head
+// h for slots kg*8 .. kg*8+8 in lane (h, kg) -- the layout in which the P V product takes P
+// as its A operand, so P never leaves the registers.
+// (slots >= lim read zeros)
+__device__ __forceinline__ void tile_load_k(TileRegs& T, int t0, int lim, const TileBufs& B, int m16, int kg) {
 #pragma unroll
   for (int gq = 0; gq < 2; ++gq) {
-    const int t = t0 + gq * 16 + m16;
+    const int t = t0 + (m16 >> 2) * 8 + gq * 4 + (m16 & 3);
+    const uint32_t off = t < lim ? (uint32_t)t * 256u + kg * 16 : B.k_oob;
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < sp.j1) {
-        const uint16_t* src = (t == sp.app) ? kn + cc * 32 + kg * 8 : Kp + (size_t)t * D + cc * 32 + kg * 8;
-        v = *reinterpret_cast<const uint4*>(src);
-      }
-      T.k[gq][cc] = v;
-    }
+    for (int cc = 0; cc < 4; ++cc) T.k[gq][cc] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(B.rk, off + cc * 64, 0, 0));
   }
 }
 
-__device__ __forceinline__ void tile_load_v(TileRegs& T, int t0, const Span& sp, const uint16_t* Vt, int cap,
-                                            int m16, int kg) {
+// (8-slot groups starting at or past lim read zeros)
+__device__ __forceinline__ void tile_load_v(TileRegs& T, int t0, int lim, const TileBufs& B, int m16, int kg) {
   const int tv = t0 + kg * 8;
+  const uint32_t off = tv < lim ? (uint32_t)m16 * B.v_row + (uint32_t)tv * 2u : B.v_oob;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (tv < sp.j1) v = *reinterpret_cast<const uint4*>(Vt + (size_t)(dt * 16 + m16) * cap + tv);
-    T.v[dt] = v;
-  }
+  for (int dt = 0; dt < 8; ++dt)
+    T.v[dt] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(B.rv, off, dt * 16 * B.v_row, 0));
 }
 
-// S = q K^T for slots t0 + gq*16 + m16
-__device__ __forceinline__ void tile_scores(const TileRegs& T, const bf16x8_t (&qa)[4], f32x4_t (&sc)[2]) {
+// sc[gq][i] = q[m16] . K[slot kg*8 + gq*4 + i]
+__device__ __forceinline__ void tile_scores(const TileRegs& T, const bf16x8_t (&qb)[4], f32x4_t (&sc)[2]) {
 #pragma unroll
   for (int gq = 0; gq < 2; ++gq) {
     sc[gq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      bf16x8_t kb;
-      __builtin_memcpy(&kb, &T.k[gq][cc], 16);
-      sc[gq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[cc], kb, sc[gq], 0, 0, 0);
+      bf16x8_t ka;
+      __builtin_memcpy(&ka, &T.k[gq][cc], 16);
+      sc[gq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[cc], sc[gq], 0, 0, 0);
     }
   }
 }
 
-// online softmax of one tile's scores, then acc = acc * cf + P V
+// bf16 hi + lo split of 8 probabilities (16-bit accurate P)
+__device__ __forceinline__ void split_bf16(const float (&p)[8], bf16x8_t& hi, bf16x8_t& lo) {
+  float r[8];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const bf16x2_t h = __builtin_convertvector(f32x2_t{p[j], p[j + 1]}, bf16x2_t);
+    hi[j] = h[0];
+    hi[j + 1] = h[1];
+    r[j] = p[j] - (float)h[0];
+    r[j + 1] = p[j + 1] - (float)h[1];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const bf16x2_t l2 = __builtin_convertvector(f32x2_t{r[j], r[j + 1]}, bf16x2_t);
+    lo[j] = l2[0];
+    lo[j + 1] = l2[1];
+  }
+}
+
+// Online softmax of one tile and acc = acc * cf + P V.  Lane (h = m16, kg) holds head h's
+// scores for slots kg*8 .. +8; m is head h's running max (equal in its four lanes), l this
+// lane's share of the running sum.  Slots >= lim (the length) and the new token's slot app
+// are masked; tiles with neither skip the masking.
 template <int G>
-__device__ __forceinline__ void tile_pv(const TileRegs& T, const f32x4_t (&sc)[2], int t0, const Span& sp,
-                                        const uint16_t* vn, float qs, int m16, int kg, bool real_rows,
-                                        uint32_t (*s_p)[8][16], float (&m)[4], float (&l)[4], f32x4_t (&acc)[8]) {
-  // online softmax on the real head rows (4*kg + i < G)
-  float cf[4];
-  const bool ok0 = t0 + m16 < sp.j1, ok1 = t0 + 16 + m16 < sp.j1;
+__device__ __forceinline__ void tile_pv(TileRegs& T, const f32x4_t (&sc)[2], int t0, int lim, int app, float qs,
+                                        int m16, int kg, float& m, float& l, f32x4_t (&acc)[8]) {
+  const int s0 = t0 + kg * 8;
+  const bool full = t0 + 32 <= lim && (unsigned)(app - t0) >= 32u;   // wave-uniform
+  float x[8];
+#pragma unroll
+  for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[gq * 4 + i] = sc[gq][i] * qs;
+  const int valid = lim - s0;   // slots of this lane's group below the length
+  const int ap = app - s0;      // position of the new token's slot in the group
+  if (!full) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j >= valid || j == ap) x[j] = -INFINITY;
+    // V fix-ups (P is 0 there, but the bytes may be stale or not finite): zero the slots
+    // at or past the length and the new token's slot.
+    if (valid < 8 || (ap >= 0 && ap < 8)) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        uint32_t w[4] = {T.v[dt].x, T.v[dt].y, T.v[dt].z, T.v[dt].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t keep = (e >= valid || e == ap) ? 0u : 0xffffu;
+          w[e >> 1] &= (e & 1) ? ((keep << 16) | 0xffffu) : (keep | 0xffff0000u);
+        }
+        T.v[dt] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
+  float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  mx = fmaxf(mx, swz_xor16(mx));
+  mx = fmaxf(mx, shfl_xor32(mx));
+  const float mn = fmaxf(m, mx);
+  const float msafe = mn == -INFINITY ? 0.f : mn;
+  const float cf = __builtin_amdgcn_exp2f(m - msafe);
+  float p[8], ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = __builtin_amdgcn_exp2f(x[j] - msafe);
+    ps += p[j];
+  }
+  l = fmaf(l, cf, ps);
+  m = mn;
+  bf16x8_t pha, pla;
+  split_bf16(p, pha, pla);
+  // acc rows are heads 4*kg + i: their rescale factors come from lanes 4*kg + i
+  float cr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float x0 = ok0 ? sc[0][i] * qs : -INFINITY;
-    const float x1 = ok1 ? sc[1][i] * qs : -INFINITY;
-    const float mx = group_max<16>(fmaxf(x0, x1));
-    const float mn = fmaxf(m[i], mx);
-    const float msafe = mn == -INFINITY ? 0.f : mn;
-    cf[i] = exp2f(m[i] - msafe);
-    const float p0 = exp2f(x0 - msafe), p1 = exp2f(x1 - msafe);
-    l[i] = fmaf(l[i], cf[i], p0 + p1);
-    m[i] = mn;
-    // P (bf16 hi + lo) -> LDS as [row][slot]
-    if (real_rows && 4 * kg + i < G) {
-      const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
-      const uint32_t lo0 = f32_to_bf16_bits(p0 - __uint_as_float(h0 << 16));
-      const uint32_t lo1 = f32_to_bf16_bits(p1 - __uint_as_float(h1 << 16));
-      uint16_t* ph = reinterpret_cast<uint16_t*>(&s_p[0][4 * kg + i][0]);
-      uint16_t* pl = reinterpret_cast<uint16_t*>(&s_p[1][4 * kg + i][0]);
-      ph[m16] = (uint16_t)h0; ph[16 + m16] = (uint16_t)h1;
-      pl[m16] = (uint16_t)lo0; pl[16 + m16] = (uint16_t)lo1;
+    const float c0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cf), i));
+    if (G > 4) {
+      const float c1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cf), 4 + i));
+      cr[i] = kg == 1 ? c1 : c0;
+    } else {
+      cr[i] = c0;
     }
   }
-  // A operand of P V: lane (row m16, kg) holds P[m16][kg*8 .. +8]
-  uint4 phv = make_uint4(0, 0, 0, 0), plv = make_uint4(0, 0, 0, 0);
-  if (m16 < G) {
-    phv = *reinterpret_cast<const uint4*>(&s_p[0][m16][kg * 4]);
-    plv = *reinterpret_cast<const uint4*>(&s_p[1][m16][kg * 4]);
-  }
-  bf16x8_t pha, pla;
-  __builtin_memcpy(&pha, &phv, 16);
-  __builtin_memcpy(&pla, &plv, 16);
-  // V fragment fix-ups: zero slots >= j1, insert the appended token
-  const int tv = t0 + kg * 8;
-  const int valid = sp.j1 - tv;
-  const int ap = sp.app - tv;
-  const bool fix = valid < 8 || (ap >= 0 && ap < 8);
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
-    uint4 v = T.v[dt];
-    if (fix) {
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t val = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
-        if (e == ap) val = vn[dt * 16 + m16];
-        if (e >= valid) val = 0;
-        w[e >> 1] = (e & 1) ? ((w[e >> 1] & 0xffffu) | (val << 16)) : ((w[e >> 1] & 0xffff0000u) | val);
-      }
-      v = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[dt][i] *= cf[i];
+    for (int i = 0; i < 4; ++i) acc[dt][i] *= cr[i];
     bf16x8_t vb;
-    __builtin_memcpy(&vb, &v, 16);
+    __builtin_memcpy(&vb, &T.v[dt], 16);
     acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pha, vb, acc[dt], 0, 0, 0);
     acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pla, vb, acc[dt], 0, 0, 0);
   }
 }
 
 // ------------------------------------------------------------------ matrix-core path
-// bf16, D = 128.  One 32-slot tile per wave iteration.
+// bf16, D = 128.  Tiles of 32 slots, one per wave in flight.  The slots are dealt to the
+// n_split blocks of a (sequence, KV head) in chunks of 128 (a tile per wave), round robin:
+// block c takes chunks c, c + n_split, ...  So a block's first chunk does not depend on the
+// sequence length, and its loads go out before the length has arrived (it is bounded by
+// cap; slots at or past the length are masked once it is known); the blocks' shares differ
+// by at most one chunk for any length; and 128-slot chunks keep every 128-byte line of a V
+// row (cap a multiple of 64) within one block.
 #ifndef KVM_DECODE_WPE
 #define KVM_DECODE_WPE 2
 #endif
 constexpr int WPE = KVM_DECODE_WPE;
 template <int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int D = 128, NW = 4, TILE = 32;
+  constexpr int D = 128, NW = 4, TILE = 32, STEP = NW * TILE;
   static_assert(G <= 8, "G");
   const int c = blockIdx.x, g = blockIdx.y, bb = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile starts live in SGPRs
   const int m16 = lane & 15, kg = lane >> 4;
 
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ float s_acc[NW][G][D];
-  __shared__ uint32_t s_p[NW][2][8][TILE / 2];   // per wave: hi/lo, head row, slot pairs
 
   const size_t pair = (size_t)bb * a.H_kv + g;
-  const ReadoutRegs<D> rregs = readout_load<uint16_t, D, G, NW * 64>(a, c, pair);
-  // split boundaries on 64-slot multiples: with a cap of a multiple of 64 every 128-byte
-  // line of a V row belongs to one block
-  const Span sp = block_span(a, bb, c, 2 * TILE);
+  // q and the read-out operands do not depend on the sequence length: their loads go out
+  // while the length is still being read
+  const SeqLen sl = seq_len(a, bb);
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)bb * a.H_q + (size_t)g * G) * D;
-  uint16_t* Kp = reinterpret_cast<uint16_t*>(a.Kc) + pair * (size_t)a.cap * D;
-  uint16_t* Vt = reinterpret_cast<uint16_t*>(a.Vc) + pair * (size_t)a.cap * D;
-  const uint16_t* kn = a.k_new ? reinterpret_cast<const uint16_t*>(a.k_new) + pair * D : nullptr;
-  const uint16_t* vn = a.v_new ? reinterpret_cast<const uint16_t*>(a.v_new) + pair * D : nullptr;
+  ReadoutRegs<uint16_t, G> rr;
+  readout_load<uint16_t, D, G, NW * 64>(rr, a, c, pair, qp);
+  const NewTok<uint16_t, D> nt = new_token_load<uint16_t, D>(a, c, pair);
 
-  // A operand of S = q K^T: lane (row m16, k group kg) holds q[m16][cc*32 + kg*8 .. +8]
-  bf16x8_t qa[4];
+  // B operand of S^T = K q^T: lane (head m16, k group kg) holds q[m16][cc*32 + kg*8 .. +8]
+  // (heads >= G read past the buffer: zeros)
+  bf16x8_t qb[4];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qp, G * D * 2);
+    const uint32_t off = m16 < G ? (uint32_t)m16 * D * 2 + kg * 16 : G * D * 2;
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (m16 < G) v = *reinterpret_cast<const uint4*>(qp + m16 * D + cc * 32 + kg * 8);
-    __builtin_memcpy(&qa[cc], &v, 16);
-  }
-  const float qs = a.scale * kLog2e;
-  float m[4], l[4];
-  f32x4_t acc[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.f; }
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const bool real_rows = 4 * kg < G;
-
-  // the block that owns the appended slot writes it into the caches
-  if (sp.app >= sp.j0 && sp.app < sp.j1 && wave == 0) {
-    for (int i = lane; i < D; i += 64) {
-      Kp[(size_t)sp.app * D + i] = kn[i];
-      Vt[(size_t)i * a.cap + sp.app] = vn[i];
+    for (int cc = 0; cc < 4; ++cc) {
+      const uint4 v = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rq, off + cc * 64, 0, 0));
+      __builtin_memcpy(&qb[cc], &v, 16);
     }
   }
-
-  // Rolling loads: the next tile's K goes into the K registers once S is computed, its V
-  // into the V registers once P V is done, so a tile of loads stays in flight per wave.
+  TileBufs B;
+  B.rk = make_rsrc(reinterpret_cast<const uint16_t*>(a.Kc) + pair * (size_t)a.cap * D, a.cap * D * 2);
+  B.rv = make_rsrc(reinterpret_cast<const uint16_t*>(a.Vc) + pair * (size_t)a.cap * D, a.cap * D * 2);
+  B.k_oob = (uint32_t)a.cap * D * 2;
+  B.v_oob = (uint32_t)a.cap * D * 2;
+  B.v_row = (uint32_t)a.cap * 2;
+  // the first tile, bounded by cap
   TileRegs ta;
-  int t0 = sp.j0 + wave * TILE;
-  if (t0 < sp.j1) {
-    tile_load_k(ta, t0, sp, Kp, kn, m16, kg);
-    tile_load_v(ta, t0, sp, Vt, a.cap, m16, kg);
-  }
-  readout_compute<uint16_t, D, G, NW * 64>(a, c, g, pair, qp, rregs);
-  for (; t0 < sp.j1; t0 += NW * TILE) {
-    const int tn = t0 + NW * TILE;
+  int t0 = c * STEP + wave * TILE;
+  tile_load_k(ta, t0, a.cap, B, m16, kg);
+  tile_load_v(ta, t0, a.cap, B, m16, kg);
+  __builtin_amdgcn_sched_barrier(0);
+  const Span sp = block_span(a, 0, 1, uniform(sl));   // n, app (j0, j1 unused)
+
+  // One tile in flight per wave: once a tile's scores are done its registers take the next
+  // tile's K loads (bounded by the length n), once P V is done its V loads.  (Two tiles in
+  // flight per wave measured slower: with every load of the launch issued at once, each
+  // wave's data arrives late.)  Loads past the bound read zeros, so the loop's loads are
+  // unconditional.
+  readout_first<uint16_t, D, G, NW * 64>(a, c, pair, rr);
+  const int stride = a.n_split * STEP;
+
+  const float qs = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (; t0 < sp.n; t0 += stride) {
     f32x4_t sc[2];
-    tile_scores(ta, qa, sc);
-    if (tn < sp.j1) tile_load_k(ta, tn, sp, Kp, kn, m16, kg);
-    tile_pv<G>(ta, sc, t0, sp, vn, qs, m16, kg, real_rows, s_p[wave], m, l, acc);
-    if (tn < sp.j1) tile_load_v(ta, tn, sp, Vt, a.cap, m16, kg);
+    tile_scores(ta, qb, sc);
+    tile_load_k(ta, t0 + stride, sp.n, B, m16, kg);
+    tile_pv<G>(ta, sc, t0, sp.n, sp.app, qs, m16, kg, m, l, acc);
+    tile_load_v(ta, t0 + stride, sp.n, B, m16, kg);
   }
-  // wave state -> LDS: rows 4*kg + i < G live in lanes of group kg
+  readout_rest<uint16_t, D, G, NW * 64>(a, c, pair, qp);
+  new_token_store<uint16_t, D>(a, c, pair, sp, nt);
+  // wave state -> LDS: head h's max and sum (over its four lanes) from lane h, acc rows
+  // 4*kg + i from the lanes of group kg
+  l += swz_xor16(l);
+  l += shfl_xor32(l);
+  if (kg == 0 && m16 < G) { s_m[wave][m16] = m; s_l[wave][m16] = l; }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) l[i] = group_sum<16>(l[i]);
-  if (real_rows) {
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * kg + i;
+    if (h < G) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * kg + i;
-      if (h < G) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) s_acc[wave][h][dt * 16 + m16] = acc[dt][i];
-        if (m16 == 0) { s_m[wave][h] = m[i]; s_l[wave][h] = l[i]; }
-      }
+      for (int dt = 0; dt < 8; ++dt) s_acc[wave][h][dt * 16 + m16] = acc[dt][i];
     }
   }
   __syncthreads();
@@ -611,7 +765,7 @@ static int auto_split(const kvm_decode_desc* d) {
 }
 
 struct DecodeWs {
-  size_t a, lse, num, red, total;
+  size_t a, lse, num, total;
 };
 static DecodeWs decode_ws(const kvm_decode_desc* d, int ns) {
   const int G = d->H_q / d->H_kv;
@@ -620,8 +774,7 @@ static DecodeWs decode_ws(const kvm_decode_desc* d, int ns) {
   w.a = 0;
   w.lse = align_up(w.a + pairs * ns * G * d->d * sizeof(float), 256);
   w.num = align_up(w.lse + pairs * ns * G * sizeof(float), 256);
-  w.red = align_up(w.num + pairs * G * d->d * sizeof(float), 256);
-  w.total = align_up(w.red + pairs * 2 * G * sizeof(float), 256);
+  w.total = align_up(w.num + pairs * G * d->d * sizeof(float), 256);
   return w;
 }
 
@@ -632,7 +785,7 @@ static void launch_decode(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((decode_fma_kernel<T, D, G, 4>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((decode_merge_kernel<D, G>), dim3(D / 32, a.H_kv, a.b), dim3(32 * G), 0, st, a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(D / 32, a.H_kv, a.b), dim3(32 * G), 0, st, a);
 }
 
 template <typename T, int D>
@@ -666,6 +819,7 @@ extern "C" kvm_status kvm_decode_attn_mem(const kvm_decode_desc* d, const void* 
   KVM_REQUIRE(d->b > 0 && d->H_q > 0 && d->H_kv > 0 && d->cap > 0, KVM_ERR_SHAPE,
               "b, H_q, H_kv and cap must be positive");
   KVM_REQUIRE(d->cap % 8 == 0, KVM_ERR_SHAPE, "cap %d is not a multiple of 8", d->cap);
+  KVM_REQUIRE((int64_t)d->cap * 256 <= INT32_MAX, KVM_ERR_SHAPE, "cap %d above 8388607 slots", d->cap);
   KVM_REQUIRE(d->d == 64 || d->d == 128, KVM_ERR_SHAPE, "head dim %d not in {64, 128}", d->d);
   KVM_REQUIRE(d->H_q % d->H_kv == 0, KVM_ERR_SHAPE, "H_q %% H_kv != 0");
   const int G = d->H_q / d->H_kv;
@@ -697,7 +851,6 @@ extern "C" kvm_status kvm_decode_attn_mem(const kvm_decode_desc* d, const void* 
   a.part_a = reinterpret_cast<float*>(base + w.a);
   a.part_lse = reinterpret_cast<float*>(base + w.lse);
   a.num = reinterpret_cast<float*>(base + w.num);
-  a.red = reinterpret_cast<float*>(base + w.red);
   a.b = d->b; a.H_q = d->H_q; a.H_kv = d->H_kv; a.cap = d->cap; a.n_split = ns; a.mode = d->mode;
   a.scale = d->scale; a.eps = d->eps;
   hipStream_t s = static_cast<hipStream_t>(stream);
