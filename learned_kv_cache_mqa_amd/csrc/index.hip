@@ -17,7 +17,10 @@
 //                split fp16 hi + lo (lo scaled by 2^11): q.k = hi.hi + 2^-11 (hi.lo' + lo'.hi)
 //                on v_mfma_f32_32x32x16_f16, ~22 bits per operand, so I keeps near-fp32
 //                accuracy.  Each wave keeps its 64 keys' operands in registers and streams
-//                the window queries through LDS; the running max stays in registers.
+//                the window queries through LDS (4 per block barrier); the running max
+//                stays in registers.  The MFMAs of one key tile run beside the VALU
+//                epilogue of the other.  The three products per q.k bound it: without
+//                the epilogue the kernel takes ~80% of its time, on the matrix cores.
 //  keyproj_valu / score_valu: fp32 FMA versions for the other shapes.
 #include "common.hpp"
 
@@ -349,13 +352,19 @@ __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   lo = (_Float16)((x - (float)hi) * 2048.f);
 }
 
+// Window queries are staged kSQ at a time (split fp16 hi + lo, double-buffered in dynamic LDS),
+// so the block synchronises once per kSQ queries instead of once per query.
+constexpr int kSQ = 4;
+constexpr int kSQWords = 32 * kQPitch;                                   // one operand plane
+constexpr size_t kScoreLds = (size_t)2 * kSQ * 2 * kSQWords * sizeof(uint32_t);   // 73,728 B
+
 __global__ __launch_bounds__(512) void score_mfma_kernel(IndexArgs a) {
   // block: 512 keys (8 waves x 2 tiles x 32); H_I = 32, d_I = 64
+  extern __shared__ uint32_t sQd[];   // [buf][query][hi/lo][head row * kQPitch]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bb = blockIdx.y;
   const int kbase = blockIdx.x * 512 + wave * 64;
   const int m = lane & 31, kg = lane >> 5;
-  __shared__ uint32_t sQ[2][2][32 * kQPitch];   // [buf][hi/lo][head row]
 
   // B operands (keys): tile nt, k-step ks: lane holds k_hat[key][ks*16 + kg*8 .. +8]
   f16x8_t bh[2][4], bl[2][4];
@@ -377,55 +386,113 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(IndexArgs a) {
       }
     }
   }
-  // query staging: 32 heads x 64 dims fp32 = 2048 floats; 512 threads x 4
+  // query staging: a query is 32 heads x 64 dims fp32 = 512 float4, one per thread; a group
+  // of kSQ queries is kSQ float4 per thread (queries past the window repeat the last one and
+  // are never used)
   const float* qbase = a.qt + (size_t)bb * a.W * 2048;
-  auto fetch = [&](int s) { return *reinterpret_cast<const float4*>(qbase + (size_t)s * 2048 + tid * 4); };
-  auto stage = [&](float4 v, int buf) {
+  float4 pf[kSQ];
+  auto fetch = [&](int g0) {
+#pragma unroll
+    for (int r = 0; r < kSQ; ++r)
+      pf[r] = *reinterpret_cast<const float4*>(qbase + (size_t)min(g0 + r, a.W - 1) * 2048 + tid * 4);
+  };
+  auto stage = [&](int buf) {
     const int row = (tid * 4) >> 6, col = (tid * 4) & 63;
-    _Float16 h[4], l[4];
-    split_f16(v.x, h[0], l[0]); split_f16(v.y, h[1], l[1]);
-    split_f16(v.z, h[2], l[2]); split_f16(v.w, h[3], l[3]);
-    uint2 hw, lw;
-    __builtin_memcpy(&hw, h, 8);
-    __builtin_memcpy(&lw, l, 8);
-    *reinterpret_cast<uint2*>(&sQ[buf][0][row * kQPitch + col / 2]) = hw;
-    *reinterpret_cast<uint2*>(&sQ[buf][1][row * kQPitch + col / 2]) = lw;
+#pragma unroll
+    for (int r = 0; r < kSQ; ++r) {
+      _Float16 h[4], l[4];
+      split_f16(pf[r].x, h[0], l[0]); split_f16(pf[r].y, h[1], l[1]);
+      split_f16(pf[r].z, h[2], l[2]); split_f16(pf[r].w, h[3], l[3]);
+      uint2 hw, lw;
+      __builtin_memcpy(&hw, h, 8);
+      __builtin_memcpy(&lw, l, 8);
+      uint32_t* q = sQd + (size_t)((buf * kSQ + r) * 2) * kSQWords;
+      *reinterpret_cast<uint2*>(&q[row * kQPitch + col / 2]) = hw;
+      *reinterpret_cast<uint2*>(&q[kSQWords + row * kQPitch + col / 2]) = lw;
+    }
   };
   float best0 = -INFINITY, best1 = -INFINITY;
-  stage(fetch(0), 0);
+  fetch(0);
+  stage(0);
   __syncthreads();
-  for (int s = 0; s < a.W; ++s) {
-    const int buf = s & 1;
-    float4 nxt = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (s + 1 < a.W) nxt = fetch(s + 1);
-    f32x16_t c0 = {}, c1 = {}, x0 = {}, x1 = {};
+  const int ng = (a.W + kSQ - 1) / kSQ;
+  for (int gi = 0; gi < ng; ++gi) {
+    const int buf = gi & 1, g0 = gi * kSQ;
+    if (gi + 1 < ng) fetch(g0 + kSQ);
+    const int nq = min(kSQ, a.W - g0);
+    // A operands (query heads x dims, hi and lo) of query r are read from LDS while the
+    // epilogue of query r - 1 runs
+    auto read_a = [&](int r, f16x8_t (&Ah)[4], f16x8_t (&Al)[4]) {
+      const uint32_t* qh = sQd + (size_t)((buf * kSQ + r) * 2) * kSQWords;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 ah = *reinterpret_cast<const uint4*>(&sQ[buf][0][m * kQPitch + ks * 8 + kg * 4]);
-      const uint4 al = *reinterpret_cast<const uint4*>(&sQ[buf][1][m * kQPitch + ks * 8 + kg * 4]);
-      f16x8_t Ah, Al;
-      __builtin_memcpy(&Ah, &ah, 16);
-      __builtin_memcpy(&Al, &al, 16);
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, bh[0][ks], c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, bh[1][ks], c1, 0, 0, 0);
-      x0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, bl[0][ks], x0, 0, 0, 0);
-      x1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah, bl[1][ks], x1, 0, 0, 0);
-      x0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al, bh[0][ks], x0, 0, 0, 0);
-      x1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al, bh[1][ks], x1, 0, 0, 0);
-    }
-    // rows = heads, column = key; relu, head sum, causal mask, running max
-    float s0 = 0.f, s1 = 0.f;
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 ah = *reinterpret_cast<const uint4*>(&qh[m * kQPitch + ks * 8 + kg * 4]);
+        const uint4 al = *reinterpret_cast<const uint4*>(&qh[kSQWords + m * kQPitch + ks * 8 + kg * 4]);
+        __builtin_memcpy(&Ah[ks], &ah, 16);
+        __builtin_memcpy(&Al[ks], &al, 16);
+      }
+    };
+    // One key tile of one query: 12 MFMAs into c = hi.hi and x = hi.lo' + lo'.hi; and its
+    // epilogue: rows = heads, column = key; relu, head sum (in-lane over 16 rows, then the
+    // other half-wave's 16 via a lane swap), causal mask, running max.
+    auto mfma_tile = [&](int t, const f16x8_t (&Ah)[4], const f16x8_t (&Al)[4], f32x16_t& c, f32x16_t& x) {
+      c = x = f32x16_t{};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      s0 += fmaxf(fmaf(x0[j], 1.f / 2048.f, c0[j]), 0.f);
-      s1 += fmaxf(fmaf(x1[j], 1.f / 2048.f, c1[j]), 0.f);
+      for (int ks = 0; ks < 4; ++ks) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah[ks], bh[t][ks], c, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_32x32x16_f16(Ah[ks], bl[t][ks], x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_32x32x16_f16(Al[ks], bh[t][ks], x, 0, 0, 0);
+      }
+    };
+    auto epi_tile = [&](int t, int r, const f32x16_t& c, const f32x16_t& x, float& best) {
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sum += fmaxf(fmaf(x[j], 1.f / 2048.f, c[j]), 0.f);
+      const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
+      sum = __uint_as_float(w[0]) + __uint_as_float(w[1]);
+      if (kbase + t * 32 + m <= a.L - a.W + g0 + r) best = fmaxf(best, sum);
+    };
+    // interleave: one MFMA, then 4 VALU of the epilogue running beside it
+    auto interleave = [&]() {
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    };
+    f16x8_t Ah[4], Al[4];
+    f32x16_t c0, x0, c1, x1;
+    if (nq == kSQ) {
+      // software-pipelined over the two key tiles: tile 1's MFMAs of query r run beside
+      // tile 0's epilogue of r, and tile 0's MFMAs of r + 1 beside tile 1's epilogue of r,
+      // so the matrix core and the VALU work at the same time
+      read_a(0, Ah, Al);
+      mfma_tile(0, Ah, Al, c0, x0);
+#pragma unroll
+      for (int r = 0; r < kSQ; ++r) {
+        mfma_tile(1, Ah, Al, c1, x1);
+        epi_tile(0, r, c0, x0, best0);
+        interleave();
+        if (r + 1 < kSQ) {
+          read_a(r + 1, Ah, Al);
+          mfma_tile(0, Ah, Al, c0, x0);
+        }
+        epi_tile(1, r, c1, x1, best1);
+        if (r + 1 < kSQ) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the DS reads of query r + 1
+          interleave();
+        }
+      }
+    } else {
+      for (int r = 0; r < nq; ++r) {
+        read_a(r, Ah, Al);
+        mfma_tile(0, Ah, Al, c0, x0);
+        mfma_tile(1, Ah, Al, c1, x1);
+        epi_tile(0, r, c0, x0, best0);
+        epi_tile(1, r, c1, x1, best1);
+      }
     }
-    s0 += shfl_xor32(s0);
-    s1 += shfl_xor32(s1);
-    const int pos = a.L - a.W + s;
-    if (kbase + m <= pos) best0 = fmaxf(best0, s0);
-    if (kbase + 32 + m <= pos) best1 = fmaxf(best1, s1);
-    if (s + 1 < a.W) stage(nxt, buf ^ 1);
+    if (gi + 1 < ng) stage(buf ^ 1);
     __syncthreads();
   }
   float* Ir = a.I + (size_t)bb * a.L;
@@ -532,8 +599,17 @@ extern "C" kvm_status kvm_index_score(const kvm_index_desc* d, const void* X, co
     hipLaunchKernelGGL(query_kernel<uint16_t>, qgrid, dim3(256), qsmem, s, a);
   else
     hipLaunchKernelGGL(query_kernel<float>, qgrid, dim3(256), qsmem, s, a);
-  if (d->H_I == 32 && d->d_I == 64)
-    hipLaunchKernelGGL(score_mfma_kernel, dim3((d->L + 511) / 512, d->b), dim3(512), 0, s, a);
+  if (d->H_I == 32 && d->d_I == 64) {
+    static bool lds_set = false;   // a function attribute: setting it once per process suffices
+    if (!lds_set) {
+      st = check_hip(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_mfma_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kScoreLds),
+                     "score kernel LDS size");
+      if (st != KVM_OK) return st;
+      lds_set = true;
+    }
+    hipLaunchKernelGGL(score_mfma_kernel, dim3((d->L + 511) / 512, d->b), dim3(512), kScoreLds, s, a);
+  }
   else
     hipLaunchKernelGGL(score_valu_kernel, dim3((d->L + 255) / 256, d->b), dim3(256),
                        (size_t)d->H_I * d->d_I * sizeof(float), s, a);

@@ -35,6 +35,7 @@ CASES = [
     CONFIGS[2],
     CONFIGS[2].with_(b=2, L=1000, B=100, R=8, needles=4),
     CONFIGS[2].with_(L=777, W=1, B=77, R=0, needles=0),
+    CONFIGS[2].with_(L=1500, W=10, B=150, R=4, needles=2),   # staged query groups of 4, 4 and 2
     CONFIGS[2].with_(L=64, W=64, B=16, R=4, needles=0),
 ]
 
