@@ -293,10 +293,14 @@ kvm_status kvm_moment_readout(const kvm_mread_desc* desc, const void* q, const f
  * A8 + A9 / V3  Split-K decode attention with memory read-out          [IM 2.B; ASM; MKV 4]
  *
  * Per sequence bb and query head h (KV head g = h / G, G = H_q / H_kv):
- *   the new token (k_new, v_new) is first written to slot len[bb] (or append_slot[bb]);
- *   attention over the first n = len[bb] + 1 slots (len[bb] if append_slot is given, or
- *   if k_new is NULL) is computed as n_split partial states (a_c, lse_c) over disjoint
- *   slot ranges, merged by lse = log sum_c exp(lse_c), a = sum_c exp(lse_c - lse) a_c;
+ *   the new token (k_new, v_new) takes slot app = len[bb] (or append_slot[bb]); attention
+ *   is over the first n = len[bb] + 1 slots (len[bb] if append_slot is given, or if k_new
+ *   is NULL), n clamped to cap; when app < n the new token is attended and written into
+ *   both caches at slot app (the slot's old contents are never read), otherwise it is
+ *   neither.  The cached slots are reduced to n_split partial states (a_c, lse_c) over
+ *   disjoint slot sets (bf16 d = 128: 128-slot chunks dealt round robin; otherwise
+ *   contiguous ranges), the new token is one more state (v_new, scale q.k_new), and the
+ *   states merge in a fixed order by lse = log sum_c exp(lse_c), a = sum_c exp(lse_c - lse) a_c;
  *   mode KVM_READ_NONE:    o = a
  *   mode KVM_READ_MEMORY:  m = M_g phi(q) / (bvec_g . phi(q) + eps), o = a + sigmoid(w_g[h].q) m
  *   mode KVM_READ_MOMENTS: f_E = s_v/n_e + (S - s_v s_k^T/n_e) q / (n_e sqrt d),
@@ -308,7 +312,8 @@ kvm_status kvm_moment_readout(const kvm_mread_desc* desc, const void* q, const f
  * len [b] i32 (not modified), append_slot [b] i32 (nullable), o [b,H_q,d] f32,
  * lse [b,H_q] f32 (nullable: log-partition of the retained attention, scale applied).
  * The library never reads or writes a slot >= cap (n is clamped to cap).
- * Supported: d in {64, 128}, G in {1, 2, 4, 8}; n_split 0 chooses automatically.
+ * Supported: d in {64, 128}, G in {1, 2, 4, 8}, cap <= 8388607; n_split 0 chooses
+ * automatically (the most splits that keep the grid within one even round on the chip).
  * ------------------------------------------------------------------------------------ */
 #define KVM_READ_NONE 0
 #define KVM_READ_MEMORY 1

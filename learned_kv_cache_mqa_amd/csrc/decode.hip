@@ -756,12 +756,17 @@ __global__ void len_add_kernel(int32_t* len, int b, int delta) {
   if (i < b) len[i] += delta;
 }
 
+// Splits per (sequence, KV head): the most that keep the grid within one round of two
+// attention blocks per compute unit (256 on this part).  A grid that overfills the round
+// leaves a second, partial round; one that does not divide evenly leaves some units with
+// twice the work of others -- both measured 15-30% slower than a full, even round.
 static int auto_split(const kvm_decode_desc* d) {
   if (d->n_split > 0) return d->n_split;
+  constexpr int kBlockSlots = 2 * 256;
   const int pairs = d->b * d->H_kv;
-  int s = (512 + pairs - 1) / pairs;
-  s = std::min(s, std::max(1, d->cap / 128));
-  return std::max(1, std::min(s, 64));
+  int s = std::max(1, kBlockSlots / pairs);
+  s = std::min(s, std::max(1, d->cap / 128));   // at least one 128-slot chunk per block
+  return std::min(s, 64);
 }
 
 struct DecodeWs {

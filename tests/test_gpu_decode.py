@@ -118,3 +118,41 @@ def test_decode_deterministic_and_split_invariant():
     assert outs[0].tobytes() == outs[1].tobytes()
     for x in outs[2:]:
         np.testing.assert_allclose(x, outs[0], rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_decode_append_slot_and_full_cache(dtype, d):
+    """The new token is attended and written at its slot only when that slot is below the
+    attended length: append_slot inside the length replaces that slot's contents, one at
+    or past it leaves the cache and the attention alone, and a full cache (len == cap)
+    without an append slot drops the token."""
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, assert_output
+
+    cap = 304
+    f = lambda x: gen.from_storage(x, dtype)
+    for lens, slots in (([300, 200, cap], [100, 250, 5]), ([cap, cap - 1], None)):
+        b = len(lens)
+        c = _case(dtype, b, 16, 4, d, cap, lens, seed=31 + b)
+        Kc, Vc = to_dev(c["Kc"]), to_dev(np.ascontiguousarray(c["Vc"].transpose(0, 1, 3, 2)))
+        slot_t = to_dev(np.array(slots, np.int32)) if slots is not None else None
+        o = api.kvm_decode_attn_mem(to_dev(c["q"]), Kc, Vc, to_dev(c["lens"]), k_new=to_dev(c["kn"]),
+                                    v_new=to_dev(c["vn"]), append_slot=slot_t)
+        torch.cuda.synchronize()
+        got, gK, gV = to_np(o), to_np(Kc), to_np(Vc)
+        for bi in range(b):
+            K, V = f(c["Kc"][bi]).copy(), f(c["Vc"][bi]).copy()
+            n = min(lens[bi] + (0 if slots is not None else 1), cap)
+            app = slots[bi] if slots is not None else lens[bi]
+            taken = app < n
+            if taken:
+                K[:, app] = f(c["kn"])[bi]
+                V[:, app] = f(c["vn"])[bi]
+            ref, _ = im.decode_attention(f(c["q"])[bi], K, V, n, 1 / math.sqrt(d))
+            assert_output(got[bi], ref, dtype, f"o seq {bi}")
+            if app < cap:
+                want_k = c["kn"][bi] if taken else c["Kc"][bi, :, app]
+                want_v = c["vn"][bi] if taken else c["Vc"][bi, :, app]
+                assert gK[bi, :, app].tobytes() == np.ascontiguousarray(want_k).tobytes()
+                assert np.ascontiguousarray(gV[bi, :, :, app]).tobytes() == np.ascontiguousarray(want_v).tobytes()
