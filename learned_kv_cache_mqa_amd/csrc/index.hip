@@ -297,50 +297,53 @@ __global__ __launch_bounds__(256) void query_kernel(IndexArgs a) {
 }
 
 // ------------------------------------------------------------------ A2: queries, matrix cores
-// bf16, d = 128, d_I = 64, W % 32 == 0.  One wave per (sequence, indexer head h): the window
-// queries of model head c(h), Q [W x 128], times W_qI[h]^T [128 x 64] on
+// bf16, d = 128, d_I = 64, W % 32 == 0.  One wave per (sequence, indexer head h, 32 window
+// queries): Q [32 x 128] of model head c(h) times W_qI[h]^T [128 x 64] on
 // v_mfma_f32_32x32x16_bf16; then RMSNorm over d_I per query, the gate from the key kernel
-// and 1/sqrt(d_I).
-__global__ __launch_bounds__(256) void query_mfma_kernel(IndexArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.x * 4 + wave, bb = blockIdx.y;
-  if (h >= a.H_I) return;
+// and 1/sqrt(d_I).  A grid of one-wave blocks spreads this latency-bound step over the chip;
+// every load (operands and the 16 gates) goes out before the first wait.
+__global__ __launch_bounds__(64) void query_mfma_kernel(IndexArgs a) {
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x, mt = blockIdx.y, bb = blockIdx.z;
   const int m = lane & 31, kg = lane >> 5;
   const int c = (h * a.H_q) / a.H_I;
   const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.Qwin) + (size_t)bb * a.W * a.H_q * 128 + (size_t)c * 128;
   const uint16_t* Wq = reinterpret_cast<const uint16_t*>(a.W_qI) + (size_t)h * 64 * 128;
   const float isd = 0.125f;   // 1/sqrt(64)
+  uint4 qa[8], wb0[8], wb1[8];
+  const int s = mt * 32 + m;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    qa[j] = *reinterpret_cast<const uint4*>(Q + (size_t)s * a.H_q * 128 + j * 16 + kg * 8);
+    wb0[j] = *reinterpret_cast<const uint4*>(Wq + (size_t)m * 128 + j * 16 + kg * 8);
+    wb1[j] = *reinterpret_cast<const uint4*>(Wq + (size_t)(32 + m) * 128 + j * 16 + kg * 8);
+  }
+  float gt[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int sq = mt * 32 + 8 * (j / 4) + 4 * kg + (j % 4);
+    gt[j] = a.gate[((size_t)bb * a.W + sq) * a.H_I + h];
+  }
   const float gk0 = a.gamma_q[m], gk1 = a.gamma_q[32 + m];
-  for (int mt = 0; mt < a.W / 32; ++mt) {
-    f32x16_t acc0 = {}, acc1 = {};
-    uint4 qa[8], wb0[8], wb1[8];
-    const int s = mt * 32 + m;
+  f32x16_t acc0 = {}, acc1 = {};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qa[j] = *reinterpret_cast<const uint4*>(Q + (size_t)s * a.H_q * 128 + j * 16 + kg * 8);
-      wb0[j] = *reinterpret_cast<const uint4*>(Wq + (size_t)m * 128 + j * 16 + kg * 8);
-      wb1[j] = *reinterpret_cast<const uint4*>(Wq + (size_t)(32 + m) * 128 + j * 16 + kg * 8);
-    }
+  for (int j = 0; j < 8; ++j) {
+    bf16x8_t A, B0, B1;
+    __builtin_memcpy(&A, &qa[j], 16);
+    __builtin_memcpy(&B0, &wb0[j], 16);
+    __builtin_memcpy(&B1, &wb1[j], 16);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B0, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B1, acc1, 0, 0, 0);
+  }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      bf16x8_t A, B0, B1;
-      __builtin_memcpy(&A, &qa[j], 16);
-      __builtin_memcpy(&B0, &wb0[j], 16);
-      __builtin_memcpy(&B1, &wb1[j], 16);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B1, acc1, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int sq = mt * 32 + 8 * (j / 4) + 4 * kg + (j % 4);
-      float ss = acc0[j] * acc0[j] + acc1[j] * acc1[j];
-      ss = group_sum<32>(ss);
-      const float r = rsqrtf(ss * (1.f / 64.f) + a.eps);
-      const float gt = a.gate[((size_t)bb * a.W + sq) * a.H_I + h];
-      float* out = a.qt + (((size_t)bb * a.W + sq) * a.H_I + h) * 64;
-      out[m] = gt * gk0 * acc0[j] * r * isd;
-      out[32 + m] = gt * gk1 * acc1[j] * r * isd;
-    }
+  for (int j = 0; j < 16; ++j) {
+    const int sq = mt * 32 + 8 * (j / 4) + 4 * kg + (j % 4);
+    float ss = acc0[j] * acc0[j] + acc1[j] * acc1[j];
+    ss = group_sum<32>(ss);
+    const float r = rsqrtf(ss * (1.f / 64.f) + a.eps);
+    float* out = a.qt + (((size_t)bb * a.W + sq) * a.H_I + h) * 64;
+    out[m] = gt[j] * gk0 * acc0[j] * r * isd;
+    out[32 + m] = gt[j] * gk1 * acc1[j] * r * isd;
   }
 }
 
@@ -594,7 +597,7 @@ extern "C" kvm_status kvm_index_score(const kvm_index_desc* d, const void* X, co
     hipLaunchKernelGGL(keyproj_valu_kernel<float>, dim3((d->L + 15) / 16, d->b), dim3(256), 0, s, a);
   const dim3 qgrid((d->W + kQB - 1) / kQB, d->b);
   if (mfma)
-    hipLaunchKernelGGL(query_mfma_kernel, dim3((d->H_I + 3) / 4, d->b), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(query_mfma_kernel, dim3(d->H_I, d->W / 32, d->b), dim3(64), 0, s, a);
   else if (bf)
     hipLaunchKernelGGL(query_kernel<uint16_t>, qgrid, dim3(256), qsmem, s, a);
   else
