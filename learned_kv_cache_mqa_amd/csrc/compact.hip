@@ -81,10 +81,14 @@ __global__ __launch_bounds__(256) void compact_reduce_kernel(CompactArgs a) {
 }
 
 // ------------------------------------------------------------------ bf16: matrix cores
-// LDS tile: per dim row, 16 token pairs (32 tokens, bf16x2 per word) + 2 pad words; a pitch
-// of 18 words keeps the transposed stores and the 8-byte fragment loads conflict-light.
+// LDS tile: per dim row, 16 token pairs (32 tokens, bf16x2 per word) + 2 pad words.  The
+// pair words of a row sit in four groups of four (the 8 tokens an MFMA lane reads); the groups
+// are XOR-swizzled by the row's 32-dim tile index.  With the pitch of 18 words this keeps
+// both the transposed stores (a wave's 64 lanes: 16 dim blocks x 4 token pairs of one group)
+// and the 8-byte fragment loads (32 consecutive rows) free of bank conflicts.
 constexpr int kTok = 32;
 constexpr int kPitch = 18;
+__device__ __forceinline__ int pair_word(int row, int pr) { return row * kPitch + (pr ^ (((row >> 5) & 3) << 2)); }
 
 // Stages one tile of 32 tokens for the contraction: this thread holds tokens (2 pr, 2 pr + 1)
 // x dims db*8 .. db*8+8 of K and V.  Writes V^T (exact bf16) to sV and u = w phi(k) (memory)
@@ -118,7 +122,7 @@ __device__ __forceinline__ void stage_tile(const CompactArgs& a, int pr, int db,
   constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int at = (db * 8 + e) * kPitch + pr;
+    const int at = pair_word(db * 8 + e, pr);
     const bool odd = e & 1;
     const uint32_t vw = __builtin_amdgcn_perm(v1[e >> 1], v0[e >> 1], odd ? 0x07060302u : 0x05040100u) & vmask;
     sV[at] = vw;
@@ -194,10 +198,11 @@ void compact_mfma_kernel(CompactArgs a) {
   const __amdgpu_buffer_rsrc_t rS =
       make_rsrc(a.slot_map + (a.per_head ? pair : (size_t)bb) * a.L + p0, (p1 - p0) * 4);
 
-  // thread -> (token pair, 8-dim block); D = 64 leaves half the threads without a slot of
-  // their own (they load a duplicate and stage nothing)
-  const int pr = tid % PAIRS;
-  const int db = (tid / PAIRS) % DB;
+  // thread -> (token pair, 8-dim block), dim blocks fastest: 16 lanes read one token's whole
+  // 256-byte row.  D = 64 leaves half the threads without a slot of their own (they load a
+  // duplicate and stage nothing)
+  const int db = tid % DB;
+  const int pr = (tid / DB) % PAIRS;
   const bool loader = DB * PAIRS >= 256 || tid / PAIRS < DB;
   float vacc0[8], vacc1[8];
 #pragma unroll
@@ -245,19 +250,21 @@ void compact_mfma_kernel(CompactArgs a) {
       // All hi products are issued before the lo ones so that no MFMA waits on the previous.
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int woff = ks * 8 + (lane >> 5) * 4;
+        const int grp = ks * 2 + (lane >> 5);   // this lane's group of 4 pair words
         const int m = lane & 31;
         bf16x8_t A[NTI], Bh[NTJ], Bl[NTJ];
 #pragma unroll
         for (int x = 0; x < NTI; ++x) {
-          const uint32_t* pa = sV[cur] + ((wi * NTI + x) * 32 + m) * kPitch + woff;
+          const int ti = wi * NTI + x;
+          const uint32_t* pa = sV[cur] + (ti * 32 + m) * kPitch + ((grp ^ (ti & 3)) << 2);
           const uint2 a0 = *reinterpret_cast<const uint2*>(pa), a1 = *reinterpret_cast<const uint2*>(pa + 2);
           const uint4 av = {a0.x, a0.y, a1.x, a1.y};
           __builtin_memcpy(&A[x], &av, 16);
         }
 #pragma unroll
         for (int y = 0; y < NTJ; ++y) {
-          const int r = ((wj * NTJ + y) * 32 + m) * kPitch + woff;
+          const int tj = wj * NTJ + y;
+          const int r = (tj * 32 + m) * kPitch + ((grp ^ (tj & 3)) << 2);
           const uint2 h0 = *reinterpret_cast<const uint2*>(sH[cur] + r), h1 = *reinterpret_cast<const uint2*>(sH[cur] + r + 2);
           const uint4 hv = {h0.x, h0.y, h1.x, h1.y};
           __builtin_memcpy(&Bh[y], &hv, 16);
@@ -310,17 +317,26 @@ void compact_mfma_kernel(CompactArgs a) {
         pm[r * D + col] = acc[x * NTJ + y][j];
       }
     }
-  // vector sums: threads sharing db reduce over their token pairs
-  float* pv = a.partv + (pair * a.n_chunks + c) * (size_t)(2 * D);
+  // vector sums over the token pairs: in LDS (the tiles are free now), then thread i < 2D sums
+  // entry i over the pairs in order
+  __syncthreads();
+  float* sv = reinterpret_cast<float*>(sV[0]);   // [PAIRS][2D] floats
+  static_assert(PAIRS * 2 * D <= 2 * D * kPitch, "vector sums fit in one staged tile");
+  if (loader) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float x0 = vacc0[e], x1 = vacc1[e];
-    x0 = group_sum<PAIRS>(x0);
-    x1 = group_sum<PAIRS>(x1);
-    if (pr == 0 && loader) { pv[db * 8 + e] = x0; pv[D + db * 8 + e] = x1; }
+    for (int e = 0; e < 8; ++e) {
+      sv[pr * 2 * D + db * 8 + e] = vacc0[e];
+      sv[pr * 2 * D + D + db * 8 + e] = vacc1[e];
+    }
   }
   if (tid == 0) s_n = 0;
   __syncthreads();
+  float* pv = a.partv + (pair * a.n_chunks + c) * (size_t)(2 * D);
+  for (int i = tid; i < 2 * D; i += 256) {
+    float x = 0.f;
+    for (int q = 0; q < PAIRS; ++q) x += sv[q * 2 * D + i];
+    pv[i] = x;
+  }
   if (db == 0 && nloc) atomicAdd(&s_n, nloc);
   __syncthreads();
   if (tid == 0) a.partn[pair * a.n_chunks + c] = s_n;
