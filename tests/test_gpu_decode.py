@@ -156,3 +156,93 @@ def test_decode_append_slot_and_full_cache(dtype, d):
                 want_v = c["vn"][bi] if taken else c["Vc"][bi, :, app]
                 assert gK[bi, :, app].tobytes() == np.ascontiguousarray(want_k).tobytes()
                 assert np.ascontiguousarray(gV[bi, :, :, app]).tobytes() == np.ascontiguousarray(want_v).tobytes()
+
+
+def _sweep_cases(n=40):
+    """Seeded random decode configurations: group sizes, head dims, dtypes, caps that are
+    and are not multiples of 64, lengths from 1 to cap, every append mode, every read-out
+    and explicit split counts."""
+    r = np.random.default_rng(20261203)
+    out = []
+    for i in range(n):
+        dtype = ["bf16", "f32"][int(r.integers(0, 4) == 0)]
+        d = [64, 128][int(r.integers(0, 3) > 0)]
+        G = int(r.choice([1, 2, 4, 8]))
+        H_kv = int(r.choice([1, 2, 4, 8]))
+        b = int(r.integers(1, 4))
+        cap = 8 * int(r.integers(1, 90)) if r.random() < 0.6 else 64 * int(r.integers(1, 11))
+        mode = ["none", "append", "slot"][int(r.integers(0, 3))]
+        lens = [int(r.integers(1, cap + 1)) for _ in range(b)]
+        slots = [int(r.integers(0, cap)) for _ in range(b)]
+        readout = ["none", "memory", "moments"][int(r.integers(0, 3))]
+        n_split = int(r.choice([0, 0, 1, 2, 3, 5, 8, 13]))
+        out.append((i, dtype, d, G, H_kv, b, cap, mode, lens, slots, readout, n_split))
+    return out
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"sweep{c[0]}-{c[1]}-d{c[2]}-G{c[3]}-{c[7]}-{c[10]}")
+def test_decode_random_sweep(case):
+    import torch
+    from oracle import momentkv as mk
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, assert_output
+
+    i, dtype, d, G, H_kv, b, cap, mode, lens, slots, readout, n_split = case
+    H_q = G * H_kv
+    c = _case(dtype, b, H_q, H_kv, d, cap, lens, seed=1000 + i, n_ev=20)
+    f = lambda x: gen.from_storage(x, dtype)
+    mom = None
+    if readout == "moments":
+        rr = gen.rng(93, i, 0, 0)
+        moms = [[mk.empty(d) if (bi + g) % 3 == 0 else
+                 mk.add(mk.empty(d), f(gen.to_storage(rr.standard_normal((17, d)), dtype)),
+                        f(gen.to_storage(rr.standard_normal((17, d)), dtype)))
+                 for g in range(H_kv)] for bi in range(b)]
+        mom = dict(n_e=to_dev(np.array([[m["n"] for m in row] for row in moms], np.int32)),
+                   s_k=to_dev(np.array([[m["sk"] for m in row] for row in moms], np.float32)),
+                   s_v=to_dev(np.array([[m["sv"] for m in row] for row in moms], np.float32)),
+                   S=to_dev(np.array([[m["S"] for m in row] for row in moms], np.float32)))
+    Kc, Vc = to_dev(c["Kc"]), to_dev(np.ascontiguousarray(c["Vc"].transpose(0, 1, 3, 2)))
+    lse = torch.empty((b, H_q), dtype=torch.float32, device=Kc.device)
+    kw = {}
+    if mode != "none":
+        kw.update(k_new=to_dev(c["kn"]), v_new=to_dev(c["vn"]))
+    if mode == "slot":
+        kw.update(append_slot=to_dev(np.array(slots, np.int32)))
+    if readout == "memory":
+        kw.update(M=to_dev(c["M"]), bvec=to_dev(c["bv"]), w_g=to_dev(c["w_g"]))
+    if readout == "moments":
+        kw.update(moments=mom)
+    o = api.kvm_decode_attn_mem(to_dev(c["q"]), Kc, Vc, to_dev(c["lens"]), lse=lse, n_split=n_split, **kw)
+    torch.cuda.synchronize()
+    got, glse, gK, gV = to_np(o), to_np(lse), to_np(Kc), to_np(Vc)
+    scale = 1 / math.sqrt(d)
+    for bi in range(b):
+        K, V = f(c["Kc"][bi]).copy(), f(c["Vc"][bi]).copy()
+        wantK, wantV = c["Kc"][bi].copy(), c["Vc"][bi].copy()
+        if mode == "append":
+            n, app = min(lens[bi] + 1, cap), (lens[bi] if lens[bi] < cap else -1)
+        elif mode == "slot":
+            n = lens[bi]
+            app = slots[bi] if slots[bi] < n else -1
+        else:
+            n, app = lens[bi], -1
+        if app >= 0:
+            K[:, app], V[:, app] = f(c["kn"])[bi], f(c["vn"])[bi]
+            wantK[:, app], wantV[:, app] = c["kn"][bi], c["vn"][bi]
+        ref, ref_lse = im.decode_attention(f(c["q"])[bi], K, V, n, scale)
+        if readout == "memory":
+            m, g = im.memory_readout(f(c["q"])[bi], c["M"][bi].astype(np.float64), c["bv"][bi].astype(np.float64),
+                                     f(c["w_g"]), 1e-6)
+            ref = im.residual_output(ref, m, g)
+        elif readout == "moments":
+            qd = f(c["q"])[bi]
+            for h in range(H_q):
+                m32 = {k: (np.float32(v).astype(np.float64) if k != "n" else v) for k, v in moms[bi][h // G].items()}
+                ref[h] = mk.mix(qd[h], ref[h], float(ref_lse[h]), m32, d)[0]
+        assert_output(got[bi], ref, dtype, f"o seq {bi}")
+        np.testing.assert_allclose(got[bi], ref, rtol=1e-3, atol=1e-3 * np.abs(ref).max())
+        np.testing.assert_allclose(glse[bi], ref_lse, rtol=1e-4, atol=1e-4)
+        # the caches change at the new token's slot only
+        assert gK[bi].tobytes() == wantK.tobytes()
+        assert gV[bi].tobytes() == np.ascontiguousarray(wantV.transpose(0, 2, 1)).tobytes()
