@@ -200,3 +200,59 @@ def test_gather_rows_and_rank_r_update():
                                                  M0[i, g], b0[i, g])
             assert normwise(to_np(M)[i, g], rM) < 1e-5
             assert normwise(to_np(bv)[i, g], rb) < 1e-5
+
+
+def _compact_sweep(n=24):
+    """Seeded random shapes for the top-k + compaction + memory build chain."""
+    r = np.random.default_rng(777)
+    out = []
+    for i in range(n):
+        dtype = "bf16" if r.random() < 0.75 else "f32"
+        d = int(r.choice([64, 128]))
+        b, H = int(r.integers(1, 3)), int(r.integers(1, 5))
+        L = int(r.integers(33, 3000))
+        B = int(r.integers(1, L + 1))
+        R = int(r.integers(0, min(B, 40) + 1))
+        lam = float(r.choice([0.0, 0.5, 0.9, 0.99, 1.0]))
+        extra = int(r.integers(0, 100))
+        out.append((i, dtype, b, L, H, d, B, R, lam, extra))
+    return out
+
+
+@pytest.mark.parametrize("case", _compact_sweep(), ids=lambda c: f"sweep{c[0]}-{c[1]}-L{c[3]}-d{c[5]}")
+def test_select_compact_build_random_sweep(case):
+    """top-k (bit-exact), compaction (bit-exact) and the memory build (the bar) on random
+    shapes, each step fed by the GPU's previous one only where the oracle agrees exactly."""
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, assert_output
+    i, dtype, b, L, H, d, B, R, lam, extra = case
+    lam = float(np.float32(lam))
+    I = _scores(b, L, seed=5000 + i, ties=int(i % 3), specials=(i % 4 == 0))
+    idx, sm = api.kvm_topk_select(to_dev(I), B, R)
+    torch.cuda.synchronize()
+    gi, gs = to_np(idx), to_np(sm)
+    sel = [im.topk_select(I[r].astype(np.float64), B, R) for r in range(b)]
+    for r in range(b):
+        assert gi[r].tolist() == sel[r][0].tolist() and gs[r].tolist() == sel[r][1].tolist(), f"row {r}"
+    keep = gi.shape[1]
+    cap = keep + extra
+    Kt, Vt = _kv(dtype, b, L, H, d, seed=6000 + i)
+    rM = gen.rng(94, i, 0, 0)
+    M0 = rM.standard_normal((b, H, d, d)).astype(np.float32)
+    b0 = np.abs(rM.standard_normal((b, H, d))).astype(np.float32)
+    M, bv = to_dev(M0.copy()), to_dev(b0.copy())
+    Kc, Vc = api.kvm_compact_kv(to_dev(Kt), to_dev(Vt), sm, idx, keep, cap, M=M, bvec=bv, lam=lam)
+    torch.cuda.synchronize()
+    gK, gV, gM, gb = to_np(Kc), to_np(Vc), to_np(M), to_np(bv)
+    Kd, Vd = gen.from_storage(Kt, dtype), gen.from_storage(Vt, dtype)
+    for r in range(b):
+        rK, rV = im.compact(Kt[r], Vt[r], sel[r][1], cap)
+        assert gK[r][:, :keep].tobytes() == np.ascontiguousarray(rK[:, :keep]).tobytes()
+        assert np.ascontiguousarray(gV[r][:, :, :keep]).tobytes() == \
+            np.ascontiguousarray(rV[:, :keep].transpose(0, 2, 1)).tobytes()
+        ev = im.evicted_in_order(sel[r][1])
+        for g in range(H):
+            refM, refb = im.memory_build(Kd[r, ev, g], Vd[r, ev, g], lam, M0[r, g], b0[r, g])
+            assert_output(gM[r, g], refM, dtype, f"M seq {r} head {g}")
+            assert_output(gb[r, g], refb, dtype, f"b seq {r} head {g}")
