@@ -20,6 +20,8 @@ CASES = [
     (4, dict(L=1024, B=120, R=64), 48, 1),
     (4, dict(L=700, B=33, R=17, W=32, needles=0), 40, 2),
     (1, dict(streaming=True, B=40, R=8, recent_inclusive=False), 40, 1),
+    # the timed pool: 1024 + 64 slots (68 score blocks of 16 keys), shorter prefill
+    (4, dict(L=2048, B=1024, R=64), 16, 1),
 ]
 
 
