@@ -7,12 +7,14 @@ import numpy as np
 import pytest
 
 from oracle import indexmem as im
+from oracle import moment_stream as ms
 from oracle import momentkv as mk
 from tests import test_oracle_golden as gold
 from tests import test_oracle_pins as pins
 
 _orig = {name: getattr(im, name) for name in dir(im) if callable(getattr(im, name))}
 _orig_mk = {name: getattr(mk, name) for name in dir(mk) if callable(getattr(mk, name))}
+_orig_ms = {name: getattr(ms, name) for name in dir(ms) if callable(getattr(ms, name))}
 
 
 def _phi_no_plus_one(x):
@@ -106,6 +108,34 @@ def _residual_plus(k, v, mom, d):
     return np.asarray(v) - vbar + (np.asarray(k) @ St.T) / (mom["n"] * np.sqrt(d))
 
 
+def _stream_alpha_without_new(q_grp, Kpool, k_new, scale):
+    q_grp = np.asarray(q_grp, np.float64)
+    al = np.zeros(len(Kpool))
+    for q in q_grp:
+        lg = scale * (np.asarray(Kpool) @ q)
+        w = np.exp(lg - lg.max())
+        al += w / w.sum()
+    return al / len(q_grp)
+
+
+def _evict_highest(scores, pos, cand):
+    return _orig_ms["eviction_choice"]([-x for x in scores], pos, cand)
+
+
+def _evict_lower_on_ties(scores, pos, cand):
+    return min(cand, key=lambda j: (im.select_key(scores[j]), int(pos[j])))
+
+
+MUTATIONS_STREAM = [
+    ("stream alpha drops the new token", ms, "step_alpha", _stream_alpha_without_new,
+     [pins.test_stream_alpha_is_textbook_softmax_and_window_of_one]),
+    ("stream evicts the highest score", ms, "eviction_choice", _evict_highest,
+     [pins.test_stream_step_hand_example, pins.test_stream_steps_brute_force_choice_and_moments]),
+    ("stream ties evict the lower position", ms, "eviction_choice", _evict_lower_on_ties,
+     [pins.test_stream_step_hand_example]),
+]
+
+
 MUTATIONS = [
     ("phi drops +1", im, "phi", _phi_no_plus_one, [pins.test_phi_is_elu_plus_one, gold.test_memory_tiny]),
     ("M transposed", im, "memory_build", _memory_transposed, [pins.test_memory_special_cases, gold.test_memory_tiny]),
@@ -127,7 +157,8 @@ MUTATIONS = [
 ]
 
 
-@pytest.mark.parametrize("name,mod,attr,fn,tests", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+@pytest.mark.parametrize("name,mod,attr,fn,tests", MUTATIONS + MUTATIONS_STREAM,
+                         ids=[m[0] for m in MUTATIONS + MUTATIONS_STREAM])
 def test_mutation_is_caught(monkeypatch, name, mod, attr, fn, tests):
     monkeypatch.setattr(mod, attr, fn)
     for t in tests:

@@ -8,6 +8,7 @@ from hypothesis import given, settings, strategies as st
 from scipy.special import softmax as sp_softmax, logsumexp as sp_lse
 
 from oracle import indexmem as im
+from oracle import moment_stream as ms
 from oracle import momentkv as mk
 from oracle import streaming as sm
 
@@ -537,3 +538,96 @@ def test_moment_rounds():
         assert hd["mom"]["n"] == L - B == len(ev)
         np.testing.assert_allclose(hd["mom"]["S"], V[ev, g].T @ K[ev, g], rtol=1e-12)
         assert sorted(np.concatenate([ev, hd["kept"]]).tolist()) == list(range(L))
+
+
+# ============================================================================ MomentKV during decode
+
+def _mstate(P, H_kv, d, L, R, seed, n_ev=0):
+    """A pool of P tokens per KV head at distinct positions below L, with moments of n_ev
+    evicted rows, plus the evicted rows themselves."""
+    r = np.random.default_rng(seed)
+    pos = np.stack([np.sort(r.choice(L, P, replace=False)) for _ in range(H_kv)])
+    Kc, Vc = r.standard_normal((H_kv, P, d)), r.standard_normal((H_kv, P, d))
+    ev = [(r.standard_normal((n_ev, d)), r.standard_normal((n_ev, d))) for _ in range(H_kv)]
+    moms = [mk.add(mk.empty(d), k, v) if n_ev else mk.empty(d) for k, v in ev]
+    return ms.MomentStreamState(pos, Kc, Vc, moms, L, R), ev
+
+
+def test_stream_alpha_is_textbook_softmax_and_window_of_one():
+    # catches: the new token left out of the softmax, heads summed instead of averaged
+    r = np.random.default_rng(5)
+    G, d, P = 3, 8, 11
+    q, Kp, kn = r.standard_normal((G, d)), r.standard_normal((P, d)), r.standard_normal(d)
+    al = ms.step_alpha(q, Kp, kn, 0.3)
+    keys = np.vstack([Kp, kn])
+    want = np.mean([sp_softmax(0.3 * keys @ qh)[:-1] for qh in q], axis=0)
+    np.testing.assert_allclose(al, want, rtol=1e-13)
+    # the prefill's alpha with one window query at the new token's position
+    win = mk.alpha(q[None], keys[:, None, :], [P], 0.3, G)[0]
+    np.testing.assert_allclose(al, win[:-1], rtol=1e-12)
+    assert 0 < al.sum() < 1
+
+
+def test_stream_step_hand_example():
+    # zero keys: every logit is 0, alpha = 1/5; nothing evicted yet, so score = ||v|| / 5.
+    # ||v|| = 3, 1, 2, 1 at positions 0..3: positions 1 and 3 tie at the lowest score and
+    # the higher one (3) goes.  Output: uniform average of the pool (lse = log 4) mixed with
+    # the evicted row: w_R = sigmoid(log 4 - log 1) = 4/5.
+    # catches: evicting the highest score, ties evicting the lower position, folding the
+    # new token into the moments, mixing with the wrong weight
+    V = np.array([[3.0, 0.0], [0.0, 1.0], [0.0, 2.0], [1.0, 0.0]])
+    st_ = ms.MomentStreamState([[0, 1, 2, 3]], np.zeros((1, 4, 2)), V[None], [mk.empty(2)], 4, 0)
+    o, lse, slots, evp, sc = ms.step(st_, np.array([[1.0, -1.0]]), np.zeros((1, 2)), np.array([[4.0, 4.0]]))
+    np.testing.assert_allclose(sc[0], [0.6, 0.2, 0.4, 0.2], rtol=1e-14)
+    assert slots.tolist() == [3] and evp.tolist() == [3]
+    assert st_.slot_pos.tolist() == [[0, 1, 2, 4]] and st_.next_pos == 5
+    m = st_.moms[0]
+    assert m["n"] == 1 and np.array_equal(m["sv"], [1.0, 0.0]) and not m["sk"].any() and not m["S"].any()
+    assert lse[0] == pytest.approx(math.log(4))
+    np.testing.assert_allclose(o[0], [0.8 * 1.75 + 0.2, 0.8 * 1.75], rtol=1e-14)
+    # a recent window of 2 protects positions > 2: the lowest candidate is position 1
+    st2 = ms.MomentStreamState([[0, 1, 2, 3]], np.zeros((1, 4, 2)), V[None], [mk.empty(2)], 4, 2)
+    _, _, slots2, evp2, _ = ms.step(st2, np.array([[1.0, -1.0]]), np.zeros((1, 2)), np.array([[4.0, 4.0]]))
+    assert slots2.tolist() == [1] and evp2.tolist() == [1]
+
+
+def test_stream_steps_brute_force_choice_and_moments():
+    # every step's choice against a from-scratch score (alpha by softmax, the covariance
+    # as the centred sum over the evicted rows themselves), and the running moments
+    # against the plain sums of everything evicted
+    # catches: a wrong residual sign or scale, a stale moment, a candidate inside the window
+    H_q, H_kv, d, P, L, R, T = 4, 2, 6, 9, 40, 3, 12
+    st_, ev0 = _mstate(P, H_kv, d, L, R, seed=21, n_ev=5)
+    r = np.random.default_rng(22)
+    evicted = [[(k, v) for k, v in zip(*ev0[g])] for g in range(H_kv)]
+    for t in range(T):
+        q, kn, vn = r.standard_normal((H_q, d)), r.standard_normal((H_kv, d)), r.standard_normal((H_kv, d))
+        p = st_.next_pos
+        pos0, K0, V0 = st_.slot_pos.copy(), st_.Kc.copy(), st_.Vc.copy()
+        _, _, slots, evp, _ = ms.step(st_, q, kn, vn)
+        for g in range(H_kv):
+            Ke = np.array([k for k, _ in evicted[g]])
+            Ve = np.array([v for _, v in evicted[g]])
+            n = len(Ke)
+            kbar, vbar = Ke.mean(0), Ve.mean(0)
+            Sc = sum(np.outer(v - vbar, k - kbar) for k, v in zip(Ke, Ve))
+            sc = []
+            for j in range(P):
+                keys = np.vstack([K0[g], kn[g]])
+                al = np.mean([sp_softmax(keys @ q[h] / math.sqrt(d))[j] for h in (2 * g, 2 * g + 1)])
+                rj = V0[g, j] - vbar - Sc @ K0[g, j] / (n * math.sqrt(d))
+                sc.append(al * np.linalg.norm(rj))
+            cands = [j for j in range(P) if pos0[g, j] <= p - R]
+            best = min(cands, key=lambda j: (sc[j], -pos0[g, j]))
+            assert slots[g] == best and evp[g] == pos0[g, best]
+            evicted[g].append((K0[g, best], V0[g, best]))
+            Ke = np.array([k for k, _ in evicted[g]])
+            Ve = np.array([v for _, v in evicted[g]])
+            m = st_.moms[g]
+            assert m["n"] == len(Ke)
+            np.testing.assert_allclose(m["sk"], Ke.sum(0), rtol=1e-12)
+            np.testing.assert_allclose(m["sv"], Ve.sum(0), rtol=1e-12)
+            S_ref = sum(np.outer(v, k) for k, v in zip(Ke, Ve))
+            np.testing.assert_allclose(m["S"], S_ref, rtol=1e-12, atol=1e-13 * np.abs(S_ref).max())
+            assert sorted(st_.slot_pos[g].tolist()) == sorted(set(pos0[g].tolist()) - {evp[g]} | {p})
+            assert np.array_equal(st_.Kc[g, best], kn[g]) and np.array_equal(st_.Vc[g, best], vn[g])
