@@ -210,6 +210,37 @@ def time_rows(torch, api, KL, dev):
         rows[name] = round(e0.elapsed_time(e1) / reps, 4)
     rows["V_workload"] = (f"MomentKV, batch {c5.b}, {c5.L} tokens, {c5.H_q}/{c5.H_kv} heads, d {c5.d}, window {c5.W}: "
                           "alpha (two passes), first score round over all tokens, read-out")
+    # N1: MomentKV eviction step + decode over the pool, per token, at the budget and at 1024
+    for Pn in (c5.B, 1024):
+        capn = api.cache_cap(Pn)
+        Kn, Vn = rn(c5.b, c5.H_kv, capn, c5.d), rn(c5.b, c5.H_kv, c5.d, capn)
+        posn = (torch.arange(Pn, device=dev, dtype=torch.int32) * 4).expand(c5.b, c5.H_kv, Pn).contiguous()
+        nextn = torch.full((c5.b,), 4 * Pn, dtype=torch.int32, device=dev)
+        momn = {k: v.clone() for k, v in mom.items()}
+        lensn = torch.full((c5.b,), Pn, dtype=torch.int32, device=dev)
+        qn, kn, vn = rn(steps, c5.b, c5.H_q, c5.d), rn(steps, c5.b, c5.H_kv, c5.d), rn(steps, c5.b, c5.H_kv, c5.d)
+        esn = torch.empty((c5.b, c5.H_kv), dtype=torch.int32, device=dev)
+        on = torch.empty((c5.b, c5.H_q, c5.d), device=dev)
+
+        def mstream_steps():
+            for t in range(steps):
+                api.kvm_moment_stream_evict(qn[t], kn[t], vn[t], Kn, Vn, posn, nextn, momn, 0, evict_slot=esn)
+                api.kvm_decode_attn_mem(qn[t], Kn, Vn, lensn, moments=momn, o=on)
+        mstream_steps()
+        grn = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(grn, stream=st):
+                mstream_steps()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        with torch.cuda.stream(st):
+            e0.record(st)
+            grn.replay()
+            e1.record(st)
+        torch.cuda.synchronize()
+        rows[f"N1_moment_stream_step_us_P{Pn}"] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+    rows["N1_workload"] = (f"MomentKV, batch {c5.b}, {c5.H_q}/{c5.H_kv} heads, d {c5.d}, pool of P slots per KV head: "
+                           "eviction step + decode with the NC mix per token, HIP graph")
     return rows
 
 

@@ -290,6 +290,48 @@ kvm_status kvm_moment_readout(const kvm_mread_desc* desc, const void* q, const f
                               const float* s_v, const float* S, float* o, void* stream);
 
 /* ------------------------------------------------------------------------------------ *
+ * N1  MomentKV eviction during decode                               [MKV parts 1, 3]
+ *
+ * The moment sums are updated at every eviction [MKV part 1].  Each (sequence bb, KV
+ * head g) keeps a full pool of P slots (slot_pos[bb, g, j] = the position held by slot j,
+ * K/V in Kc / Vc as in kvm_decode_attn_mem).  For the new token at position
+ * p = next_pos[bb] (query heads h of the group, G = H_q / H_kv), per (bb, g):
+ *   1. alpha_j = (1/G) sum_h softmax over the pool and the new token of
+ *      (q_h . k / sqrt d), taken at pooled slot j;
+ *   2. score_j = alpha_j ||r_j||, r_j = v_j - s_v/n_e - S~ k_j / (n_e sqrt d),
+ *      S~ = S - s_v s_k^T / n_e, r_j = v_j while n_e = 0 [MKV part 3];
+ *   3. e = the slot with the lowest score among those with slot_pos <= p - R; among equal
+ *      scores the higher position is evicted (NaN orders as -inf, -0 as +0);
+ *   4. n_e += 1, s_k += k_e, s_v += v_e, S += v_e k_e^T (from the caches at slot e);
+ *   5. slot e takes the new token: its K/V are written into Kc / Vc at slot e and
+ *      slot_pos[bb, g, e] = p; evict_slot[bb, g] = e.
+ * next_pos[bb] += 1.  The pages give no per-step order; steps 1-5 are this library's
+ * reading (the prefill's alpha with a window of one query).  The new query's output then
+ * comes from kvm_decode_attn_mem (mode KVM_READ_MOMENTS, len = P, no k_new: the token is
+ * already in its slot).
+ * q [b, H_q, d], k_new, v_new [b, H_kv, d] bf16; Kc [b, H_kv, cap, d], Vc [b, H_kv, d, cap]
+ * bf16 (read-modify-write); slot_pos [b, H_kv, P] i32, next_pos [b] i32, n_e [b, H_kv] i32,
+ * s_k, s_v [b, H_kv, d] f32, S [b, H_kv, d, d] f32 (all read-modify-write);
+ * evict_slot [b, H_kv] i32 (output).  Requires P > R, cap >= P, d in {64, 128},
+ * G in {1, 2, 4, 8}.  Arithmetic: fp32; S~ / (n_e sqrt d) enters the matrix cores as three bf16
+ * terms against the exact bf16 keys.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t b, H_q, H_kv, d;
+  int32_t P;               /* pool slots per (sequence, KV head), all occupied           */
+  int32_t cap;             /* slot capacity of Kc / Vc                                    */
+  int32_t R;               /* recent window                                               */
+  int32_t dtype;           /* KVM_BF16                                                    */
+} kvm_mstream_desc;
+
+size_t kvm_moment_stream_workspace_size(const kvm_mstream_desc* desc);
+kvm_status kvm_moment_stream_evict(const kvm_mstream_desc* desc, const void* q, const void* k_new,
+                                   const void* v_new, void* Kc, void* Vc, int32_t* slot_pos,
+                                   int32_t* next_pos, int32_t* n_e, float* s_k, float* s_v,
+                                   float* S, int32_t* evict_slot, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------------------ *
  * A8 + A9 / V3  Split-K decode attention with memory read-out          [IM 2.B; ASM; MKV 4]
  *
  * Per sequence bb and query head h (KV head g = h / G, G = H_q / H_kv):

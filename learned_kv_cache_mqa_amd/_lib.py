@@ -59,6 +59,11 @@ class MReadDesc(C.Structure):
     _fields_ = [("b", i32), ("H_q", i32), ("H_kv", i32), ("d", i32), ("dtype", i32), ("scale", f32)]
 
 
+class MStreamDesc(C.Structure):
+    _fields_ = [("b", i32), ("H_q", i32), ("H_kv", i32), ("d", i32), ("P", i32), ("cap", i32), ("R", i32),
+                ("dtype", i32)]
+
+
 # name -> (restype, argtypes); symbols that the header declares
 SIGNATURES = {
     "kvm_abi_version": (C.c_int, []),
@@ -84,6 +89,8 @@ SIGNATURES = {
     "kvm_moment_alpha": (C.c_int, [C.POINTER(MomentDesc), vp, vp, vp, vp, sz, vp]),
     "kvm_moment_score": (C.c_int, [C.POINTER(MomentDesc)] + [vp] * 9),
     "kvm_moment_readout": (C.c_int, [C.POINTER(MReadDesc)] + [vp] * 9),
+    "kvm_moment_stream_workspace_size": (sz, [C.POINTER(MStreamDesc)]),
+    "kvm_moment_stream_evict": (C.c_int, [C.POINTER(MStreamDesc)] + [vp] * 13 + [sz, vp]),
 }
 
 

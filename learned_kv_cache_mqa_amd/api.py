@@ -274,3 +274,26 @@ def kvm_moment_readout(q, o_R, lse_R, moments, o=None, scale=None, stream=None):
     check(lib().kvm_moment_readout(C.byref(desc), _p(q), _p(o_R), _p(lse_R), _p(moments["n_e"]), _p(moments["s_k"]),
                                    _p(moments["s_v"]), _p(moments["S"]), _p(o), _stream(stream)))
     return o
+
+
+def kvm_moment_stream_evict(q, k_new, v_new, Kc, Vc, slot_pos, next_pos, moments, R, evict_slot=None,
+                            stream=None, ws=None):
+    """One MomentKV eviction step during decode, per (sequence, KV head): alpha of the new
+    query over the pool, score alpha*||r||, eviction of the lowest non-recent slot into the
+    moments dict(n_e, s_k, s_v, S), and the new token's K/V written into the freed slot.
+    Returns evict_slot [b, H_kv] i32.  Follow with kvm_decode_attn_mem(q, Kc, Vc, len=P,
+    moments=moments) for the step's output."""
+    _contig(q, k_new, v_new, Kc, Vc, slot_pos, next_pos, evict_slot, *moments.values())
+    b, H_q, d = q.shape
+    _, H_kv, cap, _ = Kc.shape
+    P = slot_pos.shape[-1]
+    desc = K.MStreamDesc(b=b, H_q=H_q, H_kv=H_kv, d=d, P=P, cap=cap, R=R, dtype=_dtype(q))
+    if evict_slot is None:
+        evict_slot = torch.empty((b, H_kv), dtype=torch.int32, device=q.device)
+    nb = lib().kvm_moment_stream_workspace_size(C.byref(desc))
+    if ws is None:
+        ws = workspace(nb, q.device, stream, "mstream")
+    check(lib().kvm_moment_stream_evict(C.byref(desc), _p(q), _p(k_new), _p(v_new), _p(Kc), _p(Vc), _p(slot_pos),
+                                        _p(next_pos), _p(moments["n_e"]), _p(moments["s_k"]), _p(moments["s_v"]),
+                                        _p(moments["S"]), _p(evict_slot), _p(ws), ws.numel(), _stream(stream)))
+    return evict_slot

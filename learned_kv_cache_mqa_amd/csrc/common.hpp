@@ -131,6 +131,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
+// x = h + m + l in bf16 (round to nearest even at each step; ~24 bits of x), 8 values with
+// the packed hardware conversion
+__device__ __forceinline__ void split3_bf16x8(const float (&x)[8], bf16x8_t& h, bf16x8_t& m, bf16x8_t& l) {
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const f32x2_t v = {x[j], x[j + 1]};
+    const bf16x2_t hh = __builtin_convertvector(v, bf16x2_t);
+    const f32x2_t r1 = {v[0] - (float)hh[0], v[1] - (float)hh[1]};
+    const bf16x2_t mm = __builtin_convertvector(r1, bf16x2_t);
+    const f32x2_t r2 = {r1[0] - (float)mm[0], r1[1] - (float)mm[1]};
+    const bf16x2_t ll = __builtin_convertvector(r2, bf16x2_t);
+    h[j] = hh[0]; h[j + 1] = hh[1];
+    m[j] = mm[0]; m[j + 1] = mm[1];
+    l[j] = ll[0]; l[j + 1] = ll[1];
+  }
+}
+
+// 16 bytes at byte offset `off` of a buffer (zeros past its end)
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ float phi_f(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 __device__ __forceinline__ float sigmoid_f(float x) {
   float e = __expf(-fabsf(x));

@@ -219,14 +219,6 @@ struct ScoreArgs {
 
 constexpr int kScoreKeys = 256;
 
-__device__ __forceinline__ void split3(float x, uint16_t& h, uint16_t& m, uint16_t& l) {
-  h = f32_to_bf16_bits(x);
-  const float r1 = x - __uint_as_float((uint32_t)h << 16);
-  m = f32_to_bf16_bits(r1);
-  const float r2 = r1 - __uint_as_float((uint32_t)m << 16);
-  l = f32_to_bf16_bits(r2);
-}
-
 template <int D>
 __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
   constexpr int KS = D / 16;
@@ -238,28 +230,36 @@ __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
   __shared__ float s_ss[NW][kScoreKeys];
 
   const int ne = a.n_e[pair];
-  const float inv_n = ne > 0 ? 1.f / (float)ne : 0.f;
+  const float inv_n = (ne > 0 ? 1.f : 0.f) / (float)max(ne, 1);   // no branch on the count
   const float* sk = a.s_k + (size_t)pair * D;
   const float* sv = a.s_v + (size_t)pair * D;
-  // A operands: row i = 32 wave + col of S' (zero while nothing is evicted)
+  // A operands: row i = 32 wave + col of S' (zero while nothing is evicted).  Every load is
+  // unconditional; the count only selects the result, so no load waits behind a branch.
   const int i_row = wave * 32 + col;
   bf16x8_t sh[KS], sm[KS], sl[KS];
   {
     const float* Sr = a.S + ((size_t)pair * D + i_row) * D;
     const float svi = sv[i_row];
     const float f = inv_n * a.inv_sqrt_d;
+    float4 s4[KS][2], k4[KS][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      uint16_t hv[8], mv[8], lv[8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        s4[ks][u] = *reinterpret_cast<const float4*>(Sr + ks * 16 + half * 8 + 4 * u);
+        k4[ks][u] = *reinterpret_cast<const float4*>(sk + ks * 16 + half * 8 + 4 * u);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int cc = ks * 16 + half * 8 + e;
-        const float x = ne > 0 ? (Sr[cc] - svi * sk[cc] * inv_n) * f : 0.f;
-        split3(x, hv[e], mv[e], lv[e]);
+        const float sr = e < 4 ? (&s4[ks][0].x)[e] : (&s4[ks][1].x)[e - 4];
+        const float kv = e < 4 ? (&k4[ks][0].x)[e] : (&k4[ks][1].x)[e - 4];
+        x[e] = ne > 0 ? (sr - svi * kv * inv_n) * f : 0.f;
       }
-      __builtin_memcpy(&sh[ks], hv, 16);
-      __builtin_memcpy(&sm[ks], mv, 16);
-      __builtin_memcpy(&sl[ks], lv, 16);
+      split3_bf16x8(x, sh[ks], sm[ks], sl[ks]);
     }
   }
   // v_bar of the 16 dims this lane holds in the C layout
@@ -267,23 +267,33 @@ __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) vbar[j] = sv[wave * 32 + 8 * (j / 4) + 4 * half + (j % 4)] * inv_n;
 
-  const uint16_t* Kb = a.K + bb * a.batch_stride + g * a.head_stride;
-  const uint16_t* Vb = a.V + bb * a.batch_stride + g * a.head_stride;
+  // K and V of this (sequence, KV head) through buffer resources that end after token L-1:
+  // keys past the end read zeros, so no load is conditional
+  const int tb = (int)sizeof(uint16_t);
+  const int span = (int)(((long long)(a.L - 1) * a.tok_stride + D) * tb);
+  const auto rK = make_rsrc(a.K + bb * a.batch_stride + g * a.head_stride, span);
+  const auto rV = make_rsrc(a.V + bb * a.batch_stride + g * a.head_stride, span);
   const int k0 = c * kScoreKeys;
   const int ntile = min(kScoreKeys, a.L - k0 + 31) / 32;
   for (int t = 0; t < ntile; ++t) {
     const int key = k0 + t * 32 + col;
-    const bool ok = key < a.L;
-    const uint16_t* kp = Kb + (size_t)(ok ? key : 0) * a.tok_stride + half * 8;
-    const uint16_t* vp = Vb + (size_t)(ok ? key : 0) * a.tok_stride + wave * 32 + 4 * half;
+    const int kbase = key * (int)a.tok_stride;
+    uint4 kt[KS];
+    uint2 vt[4];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kt[ks] = load16(rK, (kbase + half * 8 + ks * 16) * tb);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rV, (kbase + wave * 32 + 4 * half + 8 * q4) * tb, 0, 0);
+      vt[q4] = make_uint2(v[0], v[1]);
+    }
     f32x16_t acc;
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      uint4 kv = ok ? *reinterpret_cast<const uint4*>(kp + ks * 16) : make_uint4(0, 0, 0, 0);
       bf16x8_t B;
-      __builtin_memcpy(&B, &kv, 16);
+      __builtin_memcpy(&B, &kt[ks], 16);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh[ks], B, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sm[ks], B, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl[ks], B, acc, 0, 0, 0);
@@ -292,8 +302,7 @@ __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       // rows 8 q4 + 4 half + 0..3: four consecutive dims of this key's v
-      uint2 vv = ok ? *reinterpret_cast<const uint2*>(vp + 8 * q4) : make_uint2(0, 0);
-      const float v4[4] = {bf16_lo(vv.x), bf16_hi(vv.x), bf16_lo(vv.y), bf16_hi(vv.y)};
+      const float v4[4] = {bf16_lo(vt[q4].x), bf16_hi(vt[q4].x), bf16_lo(vt[q4].y), bf16_hi(vt[q4].y)};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float r = v4[e] - vbar[q4 * 4 + e] - acc[q4 * 4 + e];
@@ -443,6 +452,12 @@ extern "C" kvm_status kvm_moment_score(const kvm_moment_desc* d, const void* K, 
   if (st != KVM_OK) return st;
   KVM_PTR_ALIGNED(K); KVM_PTR_ALIGNED(V); KVM_PTR_ALIGNED(alpha); KVM_PTR_ALIGNED(n_e);
   KVM_PTR_ALIGNED(s_k); KVM_PTR_ALIGNED(s_v); KVM_PTR_ALIGNED(S); KVM_PTR_ALIGNED(score);
+  {
+    long long ts, hs, bs;
+    strides(d, ts, hs, bs);
+    KVM_REQUIRE(((long long)(d->L + kScoreKeys) * ts + d->d) * 2 < 0x7fffffffLL, KVM_ERR_RANGE,
+                "one (sequence, KV head) of K/V spans more than 2 GiB (L %d)", d->L);
+  }
   st = require_gfx950();
   if (st != KVM_OK) return st;
   ScoreArgs a{};

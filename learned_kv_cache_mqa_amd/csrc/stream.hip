@@ -43,10 +43,6 @@ constexpr int kThreadsPerKey = 256 / kStreamKeys;  // lanes sharing one key's he
 constexpr int kKeyDims = 64 / kThreadsPerKey;      // key dims each lane loads
 constexpr int kRowPitch = 68;     // LDS row pitch (floats) of queries and keys: 16-byte aligned rows
 
-__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
 __device__ __forceinline__ float loadf(__amdgpu_buffer_rsrc_t r, int off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }

@@ -63,3 +63,33 @@ def test_decode_validation(L):
     assert _decode(L, wsb=16) == 6
     assert b"workspace" in L.kvm_last_error()
     assert _decode(L, desc=dict(mode=2)) == 1            # moments mode needs the moments
+
+
+def _mstream(L, **kw):
+    from learned_kv_cache_mqa_amd import _lib as K
+    d = K.MStreamDesc(b=2, H_q=32, H_kv=8, d=128, P=1024, cap=1024, R=16, dtype=K.KVM_BF16)
+    for k, v in kw.pop("desc", {}).items():
+        setattr(d, k, v)
+    names = ["q", "kn", "vn", "Kc", "Vc", "pos", "next", "ne", "sk", "sv", "S", "ev", "ws"]
+    p = {n: FAKE for n in names}
+    p["wsb"] = 1 << 30
+    p.update(kw)
+    args = [None if p[n] is None else C.c_void_p(p[n]) for n in names] + [p["wsb"], None]
+    return L.kvm_moment_stream_evict(C.byref(d), *args)
+
+
+def test_moment_stream_validation(L):
+    from learned_kv_cache_mqa_amd import _lib as K
+    assert _mstream(L, desc=dict(d=96)) == 2
+    assert _mstream(L, desc=dict(H_q=36)) == 2          # not a multiple of H_kv
+    assert _mstream(L, desc=dict(H_q=8 * 16)) == 2      # group of 16
+    assert _mstream(L, desc=dict(H_q=8 * 3)) == 2       # group of 3
+    assert _mstream(L, desc=dict(dtype=K.KVM_F32)) == 3
+    assert _mstream(L, desc=dict(R=1024)) == 5          # no candidate could exist
+    assert _mstream(L, desc=dict(cap=512)) == 5
+    assert _mstream(L, S=None) == 1
+    assert _mstream(L, Vc=FAKE + 2) == 4
+    assert _mstream(L, wsb=64) == 6
+    d = K.MStreamDesc(b=2, H_q=32, H_kv=8, d=128, P=1024, cap=1024, R=16, dtype=K.KVM_BF16)
+    # logits [pairs, G, P] and norms [pairs, P], f32, each 256-byte aligned
+    assert L.kvm_moment_stream_workspace_size(C.byref(d)) == 16 * 4 * 1024 * 4 + 16 * 1024 * 4
