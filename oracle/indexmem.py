@@ -270,20 +270,30 @@ def decode_attention(q, Kc, Vc, n, scale):
 
 # ----------------------------------------------------------------------------- A9
 
-def memory_readout(q, M, b, w_g, eps=1e-6):
+def memory_query(q, W_m):
+    """Reading of the slow-weight projection layer [IM 2.B, mechanism: a trained projection
+    layer and the gate read from M]: the query that addresses M is W_m q, with one d x d
+    matrix per layer shared by every query head; the gate keeps the model's query.
+    q [H_q, d], W_m [d, d] -> [H_q, d].  W_m = I gives the read-out without projection."""
+    return np.asarray(q, np.float64) @ np.asarray(W_m, np.float64).T
+
+
+def memory_readout(q, M, b, w_g, eps=1e-6, q_mem=None):
     """Memory read-out and its gate, per query head [IM 2.B].
 
-    m(q) = M phi(q) / (b . phi(q) + eps) and g(q) = sigmoid(w_g . q) (this library's fixed
-    forms; the pages name M, b and g(q) only).  Query head h reads the state of its KV
-    head h // G.  q [H_q, d], M [H_kv, d, d], b [H_kv, d], w_g [H_q, d] -> m [H_q, d], g [H_q].
+    m(q) = M phi(q~) / (b . phi(q~) + eps) and g(q) = sigmoid(w_g . q) (this library's fixed
+    forms; the pages name M, b and g(q) only), with q~ = q_mem (the projected query, see
+    memory_query) if given, else q.  Query head h reads the state of its KV head h // G.
+    q, q_mem [H_q, d], M [H_kv, d, d], b [H_kv, d], w_g [H_q, d] -> m [H_q, d], g [H_q].
     """
     q = np.asarray(q, np.float64)
+    qm = q if q_mem is None else np.asarray(q_mem, np.float64)
     H_q = q.shape[0]
     G = H_q // M.shape[0]
     m = np.zeros_like(q)
     g = np.zeros(H_q)
     for h in range(H_q):
-        f = phi(q[h])
+        f = phi(qm[h])
         m[h] = (M[h // G] @ f) / (b[h // G] @ f + eps)
         g[h] = sigmoid(np.asarray(w_g, np.float64)[h] @ q[h])
     return m, g

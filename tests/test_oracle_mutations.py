@@ -126,6 +126,30 @@ def _evict_lower_on_ties(scores, pos, cand):
     return min(cand, key=lambda j: (im.select_key(scores[j]), int(pos[j])))
 
 
+def _mq_transposed(q, W_m):
+    return _orig["memory_query"](q, np.asarray(W_m).T)
+
+
+def _readout_gate_on_projection(q, M, b, w_g, eps=1e-6, q_mem=None):
+    return _orig["memory_readout"](q if q_mem is None else q_mem, M, b, w_g, eps, q_mem)
+
+
+def _readout_projection_after_phi(q, M, b, w_g, eps=1e-6, q_mem=None):
+    # W phi(q) instead of phi(W q); W is recovered from (q, q_mem) by least squares
+    if q_mem is None:
+        return _orig["memory_readout"](q, M, b, w_g, eps)
+    q = np.asarray(q, np.float64)
+    W = np.linalg.lstsq(q, np.asarray(q_mem, np.float64), rcond=None)[0].T
+    H_q, G = q.shape[0], q.shape[0] // M.shape[0]
+    m = np.zeros_like(q)
+    g = np.zeros(H_q)
+    for h in range(H_q):
+        f = W @ im.phi(q[h])
+        m[h] = (M[h // G] @ f) / (b[h // G] @ f + eps)
+        g[h] = im.sigmoid(np.asarray(w_g)[h] @ q[h])
+    return m, g
+
+
 MUTATIONS_STREAM = [
     ("stream alpha drops the new token", ms, "step_alpha", _stream_alpha_without_new,
      [pins.test_stream_alpha_is_textbook_softmax_and_window_of_one]),
@@ -133,6 +157,12 @@ MUTATIONS_STREAM = [
      [pins.test_stream_step_hand_example, pins.test_stream_steps_brute_force_choice_and_moments]),
     ("stream ties evict the lower position", ms, "eviction_choice", _evict_lower_on_ties,
      [pins.test_stream_step_hand_example]),
+    ("read-out projection transposed", im, "memory_query", _mq_transposed,
+     [pins.test_memory_query_projection_special_cases]),
+    ("gate reads the projected query", im, "memory_readout", _readout_gate_on_projection,
+     [pins.test_memory_query_projection_special_cases]),
+    ("projection applied after phi", im, "memory_readout", _readout_projection_after_phi,
+     [pins.test_memory_query_projection_special_cases]),
 ]
 
 

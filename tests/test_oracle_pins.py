@@ -631,3 +631,37 @@ def test_stream_steps_brute_force_choice_and_moments():
             np.testing.assert_allclose(m["S"], S_ref, rtol=1e-12, atol=1e-13 * np.abs(S_ref).max())
             assert sorted(st_.slot_pos[g].tolist()) == sorted(set(pos0[g].tolist()) - {evp[g]} | {p})
             assert np.array_equal(st_.Kc[g, best], kn[g]) and np.array_equal(st_.Vc[g, best], vn[g])
+
+
+# ============================================================================ read-out projection
+
+def test_memory_query_projection_special_cases():
+    # catches: the projection transposed, applied after phi, or fed to the gate
+    r = np.random.default_rng(31)
+    H_q, H_kv, d = 4, 2, 5
+    q, w_g = r.standard_normal((H_q, d)), r.standard_normal((H_q, d))
+    M, b = r.standard_normal((H_kv, d, d)), np.abs(r.standard_normal((H_kv, d))) + 0.5
+    base_m, base_g = im.memory_readout(q, M, b, w_g)
+    # identity: the plain read-out
+    m, g = im.memory_readout(q, M, b, w_g, q_mem=im.memory_query(q, np.eye(d)))
+    np.testing.assert_allclose(m, base_m, rtol=1e-14)
+    assert np.array_equal(g, base_g)
+    # permutation P: phi(Pq) = P phi(q), so reading with P equals reading M P and P^T b
+    perm = np.array([2, 0, 4, 1, 3])
+    P = np.eye(d)[perm]
+    assert not np.array_equal(P, P.T)
+    m, g = im.memory_readout(q, M, b, w_g, q_mem=im.memory_query(q, P))
+    m2, _ = im.memory_readout(q, M @ P, np.einsum("ij,gi->gj", P, b), w_g)
+    np.testing.assert_allclose(m, m2, rtol=1e-13)
+    assert np.array_equal(g, base_g)
+    # zero projection: phi(0) = 1, so m = M 1 / (b . 1 + eps) for every query; the gate
+    # still follows the model query
+    m, g = im.memory_readout(q, M, b, w_g, q_mem=im.memory_query(q, np.zeros((d, d))))
+    for h in range(H_q):
+        np.testing.assert_allclose(m[h], M[h // 2].sum(1) / (b[h // 2].sum() + 1e-6), rtol=1e-13)
+    assert np.array_equal(g, base_g)
+    # W = -I: phi acts on the projected query (phi(-q) differs from -phi(q))
+    m, _ = im.memory_readout(q, M, b, w_g, q_mem=im.memory_query(q, -np.eye(d)))
+    for h in range(H_q):
+        f = np.where(-q[h] > 0, -q[h] + 1.0, np.exp(-q[h]))
+        np.testing.assert_allclose(m[h], M[h // 2] @ f / (b[h // 2] @ f + 1e-6), rtol=1e-13)
