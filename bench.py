@@ -176,6 +176,7 @@ def time_rows(torch, api, KL, dev):
     torch.cuda.synchronize()
     e0, e1 = ev(), ev()
     with torch.cuda.stream(st):
+        gr.replay()   # warm replay; the state keeps evolving, as it would in decode
         e0.record(st)
         gr.replay()
         e1.record(st)
@@ -234,6 +235,7 @@ def time_rows(torch, api, KL, dev):
         torch.cuda.synchronize()
         e0, e1 = ev(), ev()
         with torch.cuda.stream(st):
+            grn.replay()
             e0.record(st)
             grn.replay()
             e1.record(st)
@@ -241,6 +243,42 @@ def time_rows(torch, api, KL, dev):
         rows[f"N1_moment_stream_step_us_P{Pn}"] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
     rows["N1_workload"] = (f"MomentKV, batch {c5.b}, {c5.H_q}/{c5.H_kv} heads, d {c5.d}, pool of P slots per KV head: "
                            "eviction step + decode with the NC mix per token, HIP graph")
+    # N2: the read-out projection: decode layer-steps at the 16K workload's shapes, with and
+    # without the projected query (kvm_mem_query + decode reading q_mem)
+    c3 = CONFIGS[3]
+    cap3, n3 = api.cache_cap(c3.keep + 512), c3.keep + 256
+    K3, V3 = rn(c3.b, c3.H_kv, cap3, c3.d), rn(c3.b, c3.H_kv, c3.d, cap3)
+    q3, kn3, vn3 = rn(steps, c3.b, c3.H_q, c3.d), rn(steps, c3.b, c3.H_kv, c3.d), rn(steps, c3.b, c3.H_kv, c3.d)
+    M3 = torch.randn((c3.b, c3.H_kv, c3.d, c3.d), generator=g, device=dev) * 0.01
+    b3 = torch.rand((c3.b, c3.H_kv, c3.d), generator=g, device=dev) + 1
+    wg3 = rn(c3.H_q, c3.d, std=c3.d ** -0.5)
+    Wm = rn(c3.d, c3.d, std=c3.d ** -0.5)
+    lens3 = torch.full((c3.b,), n3, dtype=torch.int32, device=dev)
+    qm3 = torch.empty((c3.b, c3.H_q, c3.d), dtype=bf, device=dev)
+    o3 = torch.empty((c3.b, c3.H_q, c3.d), device=dev)
+    for proj in (False, True):
+        def dsteps():
+            for t in range(steps):
+                if proj:
+                    api.kvm_mem_query(q3[t], Wm, q_mem=qm3)
+                api.kvm_decode_attn_mem(q3[t], K3, V3, lens3, k_new=kn3[t], v_new=vn3[t], M=M3, bvec=b3, w_g=wg3,
+                                        o=o3, q_mem=qm3 if proj else None)
+        dsteps()
+        gr3 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(gr3, stream=st):
+                dsteps()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        with torch.cuda.stream(st):
+            gr3.replay()
+            e0.record(st)
+            gr3.replay()
+            e1.record(st)
+        torch.cuda.synchronize()
+        rows["N2_decode_step_us_" + ("projected" if proj else "plain")] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
+    rows["N2_workload"] = (f"decode layer-step, batch {c3.b}, {c3.H_q}/{c3.H_kv} heads, d {c3.d}, {n3} cached slots: "
+                           "plain read-out vs read-out addressed with W_m q (one extra kernel), HIP graph")
     return rows
 
 

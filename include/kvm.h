@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KVM_ABI_VERSION 1
+#define KVM_ABI_VERSION 2
 
 typedef enum {
   KVM_OK = 0,
@@ -344,14 +344,17 @@ kvm_status kvm_moment_stream_evict(const kvm_mstream_desc* desc, const void* q, 
  *   contiguous ranges), the new token is one more state (v_new, scale q.k_new), and the
  *   states merge in a fixed order by lse = log sum_c exp(lse_c), a = sum_c exp(lse_c - lse) a_c;
  *   mode KVM_READ_NONE:    o = a
- *   mode KVM_READ_MEMORY:  m = M_g phi(q) / (bvec_g . phi(q) + eps), o = a + sigmoid(w_g[h].q) m
+ *   mode KVM_READ_MEMORY:  m = M_g phi(q~) / (bvec_g . phi(q~) + eps), o = a + sigmoid(w_g[h].q) m,
+ *                          q~ = q_mem[bb, h] if q_mem is given (the projected query, see
+ *                          kvm_mem_query), else q
  *   mode KVM_READ_MOMENTS: f_E = s_v/n_e + (S - s_v s_k^T/n_e) q / (n_e sqrt d),
  *                          log Z_E = log n_e + (q.s_k/n_e)/sqrt d,
  *                          w = sigmoid(lse - log Z_E), o = w a + (1 - w) f_E (o = a if n_e = 0)
  * q [b,H_q,d], k_new/v_new [b,H_kv,d] (dtype, nullable), Kc [b,H_kv,cap,d] slot-major and
  * Vc [b,H_kv,d,cap] dim-major (dtype; as written by kvm_compact_kv), cap % 8 == 0 (a
  * multiple of 64 keeps every V row on 128-byte lines, the bandwidth-friendly choice),
- * len [b] i32 (not modified), append_slot [b] i32 (nullable), o [b,H_q,d] f32,
+ * len [b] i32 (not modified), append_slot [b] i32 (nullable), q_mem [b,H_q,d] (dtype,
+ * nullable; only with KVM_READ_MEMORY, else KVM_ERR_RANGE), o [b,H_q,d] f32,
  * lse [b,H_q] f32 (nullable: log-partition of the retained attention, scale applied).
  * The library never reads or writes a slot >= cap (n is clamped to cap).
  * Supported: d in {64, 128}, G in {1, 2, 4, 8}, cap <= 8388607; n_split 0 chooses
@@ -374,9 +377,23 @@ size_t kvm_decode_workspace_size(const kvm_decode_desc* desc);
 kvm_status kvm_decode_attn_mem(const kvm_decode_desc* desc, const void* q, const void* k_new,
                                const void* v_new, const int32_t* append_slot, void* Kc, void* Vc,
                                const int32_t* len, const float* M, const float* bvec,
-                               const void* w_g, const int32_t* n_e, const float* s_k,
-                               const float* s_v, const float* S, float* o, float* lse,
-                               void* ws, size_t ws_bytes, void* stream);
+                               const void* w_g, const void* q_mem, const int32_t* n_e,
+                               const float* s_k, const float* s_v, const float* S, float* o,
+                               float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * N2  The read-out projection (slow weights)                                [IM 2.B]
+ *
+ * The pages name a trained projection layer that, with the gate, reads the memory.  This
+ * library's reading: one d x d matrix W_m per layer, shared by every query head, maps the
+ * query that addresses M:  q_mem[r] = W_m q[r]  for each row r of q [rows, d]
+ * (rows = b * H_q), fp32 accumulation, stored in dtype (bf16: round to nearest even).
+ * Pass q_mem to kvm_decode_attn_mem; the gate keeps the model query.  W_m = I gives the
+ * read-out without projection.  q, q_mem [rows, d] and W_m [d, d] (row i gives output
+ * dim i) in dtype; q_mem must not alias q.  Supported: d in {64, 128}.
+ * ------------------------------------------------------------------------------------ */
+kvm_status kvm_mem_query(int32_t rows, int32_t d, int32_t dtype, const void* q, const void* W_m,
+                         void* q_mem, void* stream);
 
 /* len[i] += delta for i < b (device i32): advances cache lengths between decode steps. */
 kvm_status kvm_len_add(int32_t* len, int32_t b, int32_t delta, void* stream);

@@ -81,7 +81,8 @@ SIGNATURES = {
     "kvm_mem_update": (C.c_int, [C.POINTER(MemDesc), vp, vp, vp, vp, vp, vp]),
     "kvm_decode_workspace_size": (sz, [C.POINTER(DecodeDesc)]),
     "kvm_decode_attn_mem": (C.c_int, [C.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                      vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+                                      vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+    "kvm_mem_query": (C.c_int, [i32, i32, i32, vp, vp, vp, vp]),
     "kvm_len_add": (C.c_int, [vp, i32, i32, vp]),
     "kvm_stream_workspace_size": (sz, [C.POINTER(StreamDesc)]),
     "kvm_stream_evict": (C.c_int, [C.POINTER(StreamDesc)] + [vp] * 17 + [sz, vp]),

@@ -61,11 +61,12 @@ def decode_desc(q, Kc, mode, n_split=0, scale=None, eps=1e-6):
 
 def kvm_decode_attn_mem(q, Kc, Vc, len_, k_new=None, v_new=None, append_slot=None, M=None, bvec=None,
                         w_g=None, moments=None, o=None, lse=None, n_split=0, scale=None, eps=1e-6,
-                        stream=None, ws=None):
+                        stream=None, ws=None, q_mem=None):
     """Decode attention over Kc [b,H_kv,cap,d] / Vc [b,H_kv,d,cap] (appending k_new/v_new), merged split-K
-    states, plus the memory read-out (M, bvec, w_g) or the MomentKV mix (moments =
-    dict(n_e, s_k, s_v, S)).  Returns o [b,H_q,d] f32 (and lse [b,H_q] if given)."""
-    _contig(q, Kc, Vc, len_, k_new, v_new, append_slot, M, bvec, w_g)
+    states, plus the memory read-out (M, bvec, w_g; addressed with q_mem if given, see
+    kvm_mem_query) or the MomentKV mix (moments = dict(n_e, s_k, s_v, S)).
+    Returns o [b,H_q,d] f32 (and lse [b,H_q] if given)."""
+    _contig(q, Kc, Vc, len_, k_new, v_new, append_slot, M, bvec, w_g, q_mem)
     mode = K.KVM_READ_MEMORY if M is not None else (K.KVM_READ_MOMENTS if moments is not None else K.KVM_READ_NONE)
     desc = decode_desc(q, Kc, mode, n_split, scale, eps)
     if o is None:
@@ -75,10 +76,21 @@ def kvm_decode_attn_mem(q, Kc, Vc, len_, k_new=None, v_new=None, append_slot=Non
         ws = workspace(nb, q.device, stream, "decode")
     mo = moments or {}
     check(lib().kvm_decode_attn_mem(C.byref(desc), _p(q), _p(k_new), _p(v_new), _p(append_slot), _p(Kc),
-                                    _p(Vc), _p(len_), _p(M), _p(bvec), _p(w_g), _p(mo.get("n_e")),
+                                    _p(Vc), _p(len_), _p(M), _p(bvec), _p(w_g), _p(q_mem), _p(mo.get("n_e")),
                                     _p(mo.get("s_k")), _p(mo.get("s_v")), _p(mo.get("S")), _p(o), _p(lse),
                                     _p(ws), ws.numel(), _stream(stream)))
     return o
+
+
+def kvm_mem_query(q, W_m, q_mem=None, stream=None):
+    """q_mem = W_m q per query row (q [..., d], W_m [d, d], same dtype): the projected query
+    that the memory read-out addresses M with."""
+    _contig(q, W_m, q_mem)
+    d = q.shape[-1]
+    if q_mem is None:
+        q_mem = torch.empty_like(q)
+    check(lib().kvm_mem_query(q.numel() // d, d, _dtype(q), _p(q), _p(W_m), _p(q_mem), _stream(stream)))
+    return q_mem
 
 
 def kvm_len_add(len_, delta=1, stream=None):

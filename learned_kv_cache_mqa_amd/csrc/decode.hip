@@ -61,6 +61,7 @@ struct DecodeArgs {
   float* num;       // [b, H_kv, G, D]   read-out numerator rows
   int b, H_q, H_kv, cap, n_split, mode;
   float scale, eps;
+  const void* q_mem;  // the query the memory read-out addresses M with (q unless projected)
 };
 
 static constexpr float kLog2e = 1.4426950408889634f;
@@ -291,7 +292,7 @@ __device__ __forceinline__ void readout_rest(const DecodeArgs& a, int c, size_t 
 // The 32 threads of a head also form the head's dot products (q . k_new, b . phi(q),
 // w_g . q or s_k . q) from D / 32 elements each.  Every load goes out in one round, before
 // anything waits: values are kept as raw bits until all loads are issued.
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool PROJ>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   constexpr int E = D / 32;
   const int rb = blockIdx.x, g = blockIdx.y, bb = blockIdx.z;
@@ -312,7 +313,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   // optional inputs through buffers of size 0 when absent (their loads read zeros), so no
   // load sits behind a branch
   constexpr int EB = E * (int)sizeof(T);   // bytes of a head's D / 32 elements
-  T qr[E], kr[E], wr[E];
+  T qr[E], kr[E], wr[E], qmr[PROJ ? E : 1];
   float xr[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) qr[e] = qh[e];
@@ -327,6 +328,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.s_v + pair * D, mom ? D * 4 : 0);
   const __amdgpu_buffer_rsrc_t re = make_rsrc(a.n_e + pair, mom ? 4 : 0);
   buffer_bytes<EB>(rk, l32 * EB, kr);
+  if constexpr (PROJ) {   // the projected query addresses the memory
+    const __amdgpu_buffer_rsrc_t rqm =
+        make_rsrc(reinterpret_cast<const T*>(a.q_mem) + ((size_t)bb * a.H_q + (size_t)g * G) * D, G * D * tb);
+    buffer_bytes<EB>(rqm, h * D * tb + l32 * EB, qmr);
+  }
   buffer_bytes<EB>(rw, h * D * tb + l32 * EB, wr);
   buffer_bytes<E * 4>(rx, l32 * E * 4, xr);
   const T vr = buffer_elem<T>(rv, dd * tb);
@@ -362,13 +368,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
       mx = nm;
     }
   }
-  // head dot products: q . k_new, b . phi(q) or s_k . q, w_g . q
+  // head dot products: q . k_new, b . phi(q_mem) or s_k . q, w_g . q
   float s_new = 0.f, x0 = 0.f, x1 = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const float qv = load_scalar<T>(&qr[e]);
+    float qm = qv;
+    if constexpr (PROJ) qm = load_scalar<T>(&qmr[e]);
     s_new = fmaf(qv, load_scalar<T>(&kr[e]), s_new);
-    x0 = fmaf(xr[e], mem ? phi_f(qv) : qv, x0);
+    x0 = fmaf(xr[e], mem ? phi_f(qm) : qm, x0);
     x1 = fmaf(load_scalar<T>(&wr[e]), qv, x1);
   }
   s_new = group_sum<32>(s_new);
@@ -404,7 +412,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ FMA path (any dtype, D)
-template <typename T, int D, int G, int NW>
+template <typename T, int D, int G, int NW, bool PROJ>
 __global__ __launch_bounds__(NW * 64) void decode_fma_kernel(DecodeArgs a) {
   constexpr int EPL = Vec16<T>::N;   // elements per lane (16 bytes)
   constexpr int LPT = D / EPL;       // lanes per token row
@@ -418,6 +426,7 @@ __global__ __launch_bounds__(NW * 64) void decode_fma_kernel(DecodeArgs a) {
 
   const Span sp = block_span(a, c, 1, uniform(seq_len(a, bb)));
   const T* qp = reinterpret_cast<const T*>(a.q) + ((size_t)bb * a.H_q + (size_t)g * G) * D;
+  const T* qmp = PROJ ? reinterpret_cast<const T*>(a.q_mem) + ((size_t)bb * a.H_q + (size_t)g * G) * D : qp;
   const size_t cache_off = ((size_t)bb * a.H_kv + g) * (size_t)a.cap * D;
   T* Kp = reinterpret_cast<T*>(a.Kc) + cache_off;
   T* Vt = reinterpret_cast<T*>(a.Vc) + cache_off;   // [D][cap]
@@ -425,7 +434,7 @@ __global__ __launch_bounds__(NW * 64) void decode_fma_kernel(DecodeArgs a) {
   const NewTok<T, D> nt = new_token_load<T, D>(a, c, pair);
   {
     ReadoutRegs<T, G> rr;
-    readout_load<T, D, G, NW * 64>(rr, a, c, pair, qp);
+    readout_load<T, D, G, NW * 64>(rr, a, c, pair, qmp);
     readout_first<T, D, G, NW * 64>(a, c, pair, rr);
   }
 
@@ -471,7 +480,7 @@ __global__ __launch_bounds__(NW * 64) void decode_fma_kernel(DecodeArgs a) {
       m[h] = mn;
     }
   }
-  readout_rest<T, D, G, NW * 64>(a, c, pair, qp);
+  readout_rest<T, D, G, NW * 64>(a, c, pair, qmp);
   new_token_store<T, D>(a, c, pair, sp, nt);
   // merge the TPI lane groups of the wave
 #pragma unroll
@@ -664,7 +673,7 @@ __device__ __forceinline__ void tile_pv(TileRegs& T, const f32x4_t (&sc)[2], int
 #define KVM_DECODE_WPE 2
 #endif
 constexpr int WPE = KVM_DECODE_WPE;
-template <int G>
+template <int G, bool PROJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = 128, NW = 4, TILE = 32, STEP = NW * TILE;
   static_assert(G <= 8, "G");
@@ -681,8 +690,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   // while the length is still being read
   const SeqLen sl = seq_len(a, bb);
   const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)bb * a.H_q + (size_t)g * G) * D;
+  const uint16_t* qmp =
+      PROJ ? reinterpret_cast<const uint16_t*>(a.q_mem) + ((size_t)bb * a.H_q + (size_t)g * G) * D : qp;
   ReadoutRegs<uint16_t, G> rr;
-  readout_load<uint16_t, D, G, NW * 64>(rr, a, c, pair, qp);
+  readout_load<uint16_t, D, G, NW * 64>(rr, a, c, pair, qmp);
   const NewTok<uint16_t, D> nt = new_token_load<uint16_t, D>(a, c, pair);
 
   // B operand of S^T = K q^T: lane (head m16, k group kg) holds q[m16][cc*32 + kg*8 .. +8]
@@ -732,7 +743,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     tile_pv<G>(ta, sc, t0, sp.n, sp.app, qs, m16, kg, m, l, acc);
     tile_load_v(ta, t0 + stride, sp.n, B, m16, kg);
   }
-  readout_rest<uint16_t, D, G, NW * 64>(a, c, pair, qp);
+  readout_rest<uint16_t, D, G, NW * 64>(a, c, pair, qmp);
   new_token_store<uint16_t, D>(a, c, pair, sp, nt);
   // wave state -> LDS: head h's max and sum (over its four lanes) from lane h, acc rows
   // 4*kg + i from the lanes of group kg
@@ -783,14 +794,21 @@ static DecodeWs decode_ws(const kvm_decode_desc* d, int ns) {
   return w;
 }
 
-template <typename T, int D, int G>
-static void launch_decode(const DecodeArgs& a, hipStream_t st) {
+template <typename T, int D, int G, bool PROJ>
+static void launch_decode_p(const DecodeArgs& a, hipStream_t st) {
   dim3 grid(a.n_split, a.H_kv, a.b);
   if constexpr (std::is_same<T, uint16_t>::value && D == 128)
-    hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<G, PROJ>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_fma_kernel<T, D, G, 4>), grid, dim3(256), 0, st, a);
-  hipLaunchKernelGGL((decode_merge_kernel<T, D, G>), dim3(D / 32, a.H_kv, a.b), dim3(32 * G), 0, st, a);
+    hipLaunchKernelGGL((decode_fma_kernel<T, D, G, 4, PROJ>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D, G, PROJ>), dim3(D / 32, a.H_kv, a.b), dim3(32 * G), 0, st, a);
+}
+
+// the read-out's projected query is a compile-time switch, so the plain path is unchanged
+template <typename T, int D, int G>
+static void launch_decode(const DecodeArgs& a, hipStream_t st) {
+  if (a.q_mem != a.q) launch_decode_p<T, D, G, true>(a, st);
+  else launch_decode_p<T, D, G, false>(a, st);
 }
 
 template <typename T, int D>
@@ -816,10 +834,10 @@ extern "C" size_t kvm_decode_workspace_size(const kvm_decode_desc* d) {
 extern "C" kvm_status kvm_decode_attn_mem(const kvm_decode_desc* d, const void* q, const void* k_new,
                                           const void* v_new, const int32_t* append_slot, void* Kc,
                                           void* Vc, const int32_t* len, const float* M,
-                                          const float* bvec, const void* w_g, const int32_t* n_e,
-                                          const float* s_k, const float* s_v, const float* S,
-                                          float* o, float* lse, void* ws, size_t ws_bytes,
-                                          void* stream) {
+                                          const float* bvec, const void* w_g, const void* q_mem,
+                                          const int32_t* n_e, const float* s_k, const float* s_v,
+                                          const float* S, float* o, float* lse, void* ws,
+                                          size_t ws_bytes, void* stream) {
   KVM_PTR(d);
   KVM_REQUIRE(d->b > 0 && d->H_q > 0 && d->H_kv > 0 && d->cap > 0, KVM_ERR_SHAPE,
               "b, H_q, H_kv and cap must be positive");
@@ -837,6 +855,9 @@ extern "C" kvm_status kvm_decode_attn_mem(const kvm_decode_desc* d, const void* 
   KVM_REQUIRE(append_slot == nullptr || k_new != nullptr, KVM_ERR_NULL, "append_slot needs k_new");
   KVM_OPT_ALIGNED(k_new); KVM_OPT_ALIGNED(v_new); KVM_OPT_ALIGNED(lse);
   if (d->mode == KVM_READ_MEMORY) { KVM_PTR_ALIGNED(M); KVM_PTR_ALIGNED(bvec); KVM_PTR_ALIGNED(w_g); }
+  KVM_REQUIRE(q_mem == nullptr || d->mode == KVM_READ_MEMORY, KVM_ERR_RANGE,
+              "q_mem is read only by the memory read-out (mode %d)", d->mode);
+  KVM_OPT_ALIGNED(q_mem);
   if (d->mode == KVM_READ_MOMENTS) {
     KVM_PTR_ALIGNED(n_e); KVM_PTR_ALIGNED(s_k); KVM_PTR_ALIGNED(s_v); KVM_PTR_ALIGNED(S);
   }
@@ -848,7 +869,7 @@ extern "C" kvm_status kvm_decode_attn_mem(const kvm_decode_desc* d, const void* 
   if (st != KVM_OK) return st;
 
   DecodeArgs a{};
-  a.q = q; a.k_new = k_new; a.v_new = v_new; a.append_slot = append_slot;
+  a.q = q; a.q_mem = q_mem ? q_mem : q; a.k_new = k_new; a.v_new = v_new; a.append_slot = append_slot;
   a.Kc = Kc; a.Vc = Vc; a.len = len; a.M = M; a.bvec = bvec; a.w_g = w_g;
   a.n_e = n_e; a.s_k = s_k; a.s_v = s_v; a.S = S; a.o = o; a.lse = lse;
   a.rmat = d->mode == KVM_READ_MEMORY ? M : S;
@@ -866,6 +887,68 @@ extern "C" kvm_status kvm_decode_attn_mem(const kvm_decode_desc* d, const void* 
     ok = d->d == 128 ? dispatch_g<float, 128>(G, a, s) : dispatch_g<float, 64>(G, a, s);
   if (!ok) return set_error(KVM_ERR_SHAPE, "unsupported group size");
   return check_hip(hipGetLastError(), "decode kernel launch");
+}
+
+// q_mem[r] = W_m q[r] for rows r of [rows, D]: 4 rows per block, thread i forms output dim i
+// from W_m's row i (fp32 accumulation, stored in the query's dtype).
+template <typename T, int D>
+__global__ __launch_bounds__(D) void mem_query_kernel(const T* q, const T* W, T* out, int rows) {
+  constexpr int N = Vec16<T>::N, RPB = 4;
+  const int r0 = blockIdx.x * RPB, i = threadIdx.x;
+  __shared__ float sq[RPB][D];
+#pragma unroll
+  for (int u = 0; u < RPB; ++u)
+    sq[u][i] = r0 + u < rows ? load_scalar<T>(q + (size_t)(r0 + u) * D + i) : 0.f;
+  float w[D];
+#pragma unroll
+  for (int c = 0; c < D; c += N) {
+    float t[N];
+    Vec16<T>::load(W + (size_t)i * D + c, t);
+#pragma unroll
+    for (int e = 0; e < N; ++e) w[c + e] = t[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < RPB; ++u) {
+    float x = 0.f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) x = fmaf(w[c], sq[u][c], x);
+    if (r0 + u < rows) {
+      if constexpr (sizeof(T) == 2) {
+        const __bf16 h = (__bf16)x;
+        __builtin_memcpy(out + (size_t)(r0 + u) * D + i, &h, 2);
+      } else {
+        out[(size_t)(r0 + u) * D + i] = x;
+      }
+    }
+  }
+}
+
+extern "C" kvm_status kvm_mem_query(int32_t rows, int32_t d, int32_t dtype, const void* q, const void* W_m,
+                                    void* q_mem, void* stream) {
+  KVM_REQUIRE(rows > 0, KVM_ERR_SHAPE, "rows must be positive");
+  KVM_REQUIRE(d == 64 || d == 128, KVM_ERR_SHAPE, "head dim %d not in {64, 128}", d);
+  KVM_REQUIRE(dtype == KVM_F32 || dtype == KVM_BF16, KVM_ERR_DTYPE, "dtype %d", dtype);
+  KVM_PTR_ALIGNED(q); KVM_PTR_ALIGNED(W_m); KVM_PTR_ALIGNED(q_mem);
+  KVM_REQUIRE(q_mem != q, KVM_ERR_RANGE, "q_mem must not alias q");
+  kvm_status st = require_gfx950();
+  if (st != KVM_OK) return st;
+  const dim3 grid((rows + 3) / 4);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == KVM_BF16) {
+    const auto* qb = static_cast<const uint16_t*>(q);
+    const auto* wb = static_cast<const uint16_t*>(W_m);
+    auto* ob = static_cast<uint16_t*>(q_mem);
+    if (d == 128) hipLaunchKernelGGL((mem_query_kernel<uint16_t, 128>), grid, dim3(128), 0, s, qb, wb, ob, rows);
+    else hipLaunchKernelGGL((mem_query_kernel<uint16_t, 64>), grid, dim3(64), 0, s, qb, wb, ob, rows);
+  } else {
+    const auto* qf = static_cast<const float*>(q);
+    const auto* wf = static_cast<const float*>(W_m);
+    auto* of = static_cast<float*>(q_mem);
+    if (d == 128) hipLaunchKernelGGL((mem_query_kernel<float, 128>), grid, dim3(128), 0, s, qf, wf, of, rows);
+    else hipLaunchKernelGGL((mem_query_kernel<float, 64>), grid, dim3(64), 0, s, qf, wf, of, rows);
+  }
+  return check_hip(hipGetLastError(), "mem_query launch");
 }
 
 extern "C" kvm_status kvm_len_add(int32_t* len, int32_t b, int32_t delta, void* stream) {

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.kvm_abi_version() == 1
+    assert L.kvm_abi_version() == 2
     assert L.kvm_status_string(6) == b"workspace too small"
 
 
@@ -44,12 +44,12 @@ def _decode(L, **kw):
                      mode=K.KVM_READ_MEMORY, scale=0.088, eps=1e-6)
     for k, v in kw.pop("desc", {}).items():
         setattr(d, k, v)
-    p = dict(q=FAKE, kn=FAKE, vn=FAKE, app=None, Kc=FAKE, Vc=FAKE, len=FAKE, M=FAKE, b=FAKE, wg=FAKE,
+    p = dict(q=FAKE, kn=FAKE, vn=FAKE, app=None, Kc=FAKE, Vc=FAKE, len=FAKE, M=FAKE, b=FAKE, wg=FAKE, qm=None,
              ne=None, sk=None, sv=None, S=None, o=FAKE, lse=None, ws=FAKE, wsb=1 << 30)
     p.update(kw)
     return L.kvm_decode_attn_mem(C.byref(d), *[None if p[k] is None else C.c_void_p(p[k]) if k != "wsb" else p[k]
                                                for k in ["q", "kn", "vn", "app", "Kc", "Vc", "len", "M", "b", "wg",
-                                                         "ne", "sk", "sv", "S", "o", "lse", "ws", "wsb"]], None)
+                                                         "qm", "ne", "sk", "sv", "S", "o", "lse", "ws", "wsb"]], None)
 
 
 def test_decode_validation(L):
@@ -63,6 +63,19 @@ def test_decode_validation(L):
     assert _decode(L, wsb=16) == 6
     assert b"workspace" in L.kvm_last_error()
     assert _decode(L, desc=dict(mode=2)) == 1            # moments mode needs the moments
+    assert _decode(L, qm=FAKE + 8) == 4                  # projected query misaligned
+    assert _decode(L, desc=dict(mode=0), M=None, qm=FAKE) == 5   # q_mem only with the memory read-out
+
+
+def test_mem_query_validation(L):
+    from learned_kv_cache_mqa_amd import _lib as K
+    f = lambda rows=4, d=128, dt=K.KVM_BF16, q=FAKE, w=FAKE, o=FAKE + 4096: L.kvm_mem_query(
+        rows, d, dt, None if q is None else C.c_void_p(q), C.c_void_p(w), C.c_void_p(o), None)
+    assert f(rows=0) == 2
+    assert f(d=96) == 2
+    assert f(dt=9) == 3
+    assert f(q=None) == 1
+    assert f(o=FAKE) == 5                                # q_mem aliases q
 
 
 def _mstream(L, **kw):

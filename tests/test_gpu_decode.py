@@ -246,3 +246,65 @@ def test_decode_random_sweep(case):
         # the caches change at the new token's slot only
         assert gK[bi].tobytes() == wantK.tobytes()
         assert gV[bi].tobytes() == np.ascontiguousarray(wantV.transpose(0, 2, 1)).tobytes()
+
+
+PROJ_CASES = [
+    # dtype, b, H_q, H_kv, d, cap, lens, n_split
+    ("bf16", 2, 32, 8, 128, 704, [410, 666], 0),     # matrix-core path
+    ("bf16", 1, 16, 2, 64, 200, [150], 3),           # d 64, group of 8
+    ("f32", 2, 8, 2, 128, 96, [33, 60], 2),          # FMA path
+]
+
+
+@pytest.mark.parametrize("dtype,b,H_q,H_kv,d,cap,lens,n_split", PROJ_CASES)
+def test_readout_projection_matches_oracle(dtype, b, H_q, H_kv, d, cap, lens, n_split):
+    """kvm_mem_query against the oracle's W_m q, and the decode read-out addressed with the
+    projected query.  The decode check feeds both sides the oracle's projected query
+    (rounded to the storage type), so only the read-out arithmetic is compared; the
+    pipeline check (the GPU's own projection into the decode) takes the output bar."""
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, assert_output
+
+    c = _case(dtype, b, H_q, H_kv, d, cap, lens, seed=cap + 7)
+    r = gen.rng(92, d, H_q, 0)
+    W_m = gen.to_storage(np.eye(d) + r.standard_normal((d, d)) / math.sqrt(d), dtype)
+    f = lambda x: gen.from_storage(x, dtype)
+    qd = f(c["q"])
+    qm_ref = np.stack([im.memory_query(qd[i], f(W_m)) for i in range(b)])
+    # the projection: fp32 accumulation, then one rounding to the storage type
+    got_qm = f(to_np(api.kvm_mem_query(to_dev(c["q"]), to_dev(W_m))))
+    ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -22
+    np.testing.assert_allclose(got_qm, qm_ref, rtol=ulp, atol=1e-6 * np.abs(qm_ref).max())
+
+    qm_st = gen.to_storage(qm_ref, dtype)
+    Kc, Vc = to_dev(c["Kc"]), to_dev(np.ascontiguousarray(c["Vc"].transpose(0, 1, 3, 2)))
+    o = to_np(api.kvm_decode_attn_mem(to_dev(c["q"]), Kc, Vc, to_dev(c["lens"]), k_new=to_dev(c["kn"]),
+                                      v_new=to_dev(c["vn"]), M=to_dev(c["M"]), bvec=to_dev(c["bv"]),
+                                      w_g=to_dev(c["w_g"]), n_split=n_split, q_mem=to_dev(qm_st)))
+    Kr, Vr = f(c["Kc"]).copy(), f(c["Vc"]).copy()
+    for i in range(b):
+        n = int(c["lens"][i])
+        Kr[i, :, n], Vr[i, :, n] = f(c["kn"])[i], f(c["vn"])[i]
+        oa, _ = im.decode_attention(qd[i], Kr[i], Vr[i], n + 1, 1 / math.sqrt(d))
+        m, g = im.memory_readout(qd[i], c["M"][i].astype(np.float64), c["bv"][i].astype(np.float64), f(c["w_g"]),
+                                 1e-6, q_mem=f(qm_st)[i])
+        ref = im.residual_output(oa, m, g)
+        assert_output(o[i], ref, dtype, f"seq {i}: o with the projected query")
+        np.testing.assert_allclose(o[i], ref, rtol=2e-4, atol=2e-4 * np.abs(ref).max())
+        # the projection changes the output: the unprojected read-out is far from it
+        m0, g0 = im.memory_readout(qd[i], c["M"][i].astype(np.float64), c["bv"][i].astype(np.float64), f(c["w_g"]))
+        assert np.abs(im.residual_output(oa, m0, g0) - ref).max() > 1e-3 * np.abs(ref).max()
+
+    # pipeline: the GPU's projection feeds the GPU decode (fresh caches: the call above
+    # wrote the new token)
+    Kc, Vc = to_dev(c["Kc"]), to_dev(np.ascontiguousarray(c["Vc"].transpose(0, 1, 3, 2)))
+    qm_dev = api.kvm_mem_query(to_dev(c["q"]), to_dev(W_m))
+    o2 = to_np(api.kvm_decode_attn_mem(to_dev(c["q"]), Kc, Vc, to_dev(c["lens"]), k_new=to_dev(c["kn"]),
+                                       v_new=to_dev(c["vn"]), M=to_dev(c["M"]), bvec=to_dev(c["bv"]),
+                                       w_g=to_dev(c["w_g"]), n_split=n_split, q_mem=qm_dev))
+    for i in range(b):
+        n = int(c["lens"][i])
+        oa, _ = im.decode_attention(qd[i], Kr[i], Vr[i], n + 1, 1 / math.sqrt(d))
+        m, g = im.memory_readout(qd[i], c["M"][i].astype(np.float64), c["bv"][i].astype(np.float64), f(c["w_g"]),
+                                 1e-6, q_mem=qm_ref[i])
+        assert_output(o2[i], im.residual_output(oa, m, g), dtype, f"seq {i}: projection pipeline")
