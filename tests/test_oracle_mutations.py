@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 
 from oracle import indexmem as im
+from oracle import asm
 from oracle import moment_stream as ms
 from oracle import momentkv as mk
 from tests import test_oracle_golden as gold
@@ -15,6 +16,7 @@ from tests import test_oracle_pins as pins
 _orig = {name: getattr(im, name) for name in dir(im) if callable(getattr(im, name))}
 _orig_mk = {name: getattr(mk, name) for name in dir(mk) if callable(getattr(mk, name))}
 _orig_ms = {name: getattr(ms, name) for name in dir(ms) if callable(getattr(ms, name))}
+_orig_asm = {name: getattr(asm, name) for name in dir(asm) if callable(getattr(asm, name))}
 
 
 def _phi_no_plus_one(x):
@@ -150,6 +152,33 @@ def _readout_projection_after_phi(q, M, b, w_g, eps=1e-6, q_mem=None):
     return m, g
 
 
+def _aggregate_plain_mean(a, lse, idx, K):
+    a = np.asarray(a, np.float64)
+    a_bar, lse_bar = _orig_asm["aggregate"](a, lse, idx, K)
+    for k in range(K):
+        if (idx == k).any():
+            a_bar[k] = a[idx == k].mean(0)
+    return a_bar, lse_bar
+
+
+def _aggregate_summed_partition(a, lse, idx, K):
+    a_bar, lse_bar = _orig_asm["aggregate"](a, lse, idx, K)
+    for k in range(K):
+        n = int((idx == k).sum())
+        if n:
+            lse_bar[k] += np.log(n)
+    return a_bar, lse_bar
+
+
+def _lookup_dot(q, C):
+    return int(np.argmax(np.asarray(C) @ np.asarray(q)))
+
+
+def _assign_farthest(X, C):
+    idx, d2 = _orig_asm["kmeans_assign"](X, C)
+    return np.argmax(d2, axis=1), d2
+
+
 MUTATIONS_STREAM = [
     ("stream alpha drops the new token", ms, "step_alpha", _stream_alpha_without_new,
      [pins.test_stream_alpha_is_textbook_softmax_and_window_of_one]),
@@ -163,6 +192,12 @@ MUTATIONS_STREAM = [
      [pins.test_memory_query_projection_special_cases]),
     ("projection applied after phi", im, "memory_readout", _readout_projection_after_phi,
      [pins.test_memory_query_projection_special_cases]),
+    ("ASM state: plain mean of outputs", asm, "aggregate", _aggregate_plain_mean,
+     [pins.test_asm_aggregate_is_partition_weighted_mean]),
+    ("ASM state: summed partition", asm, "aggregate", _aggregate_summed_partition,
+     [pins.test_asm_aggregate_is_partition_weighted_mean]),
+    ("ASM lookup by dot product", asm, "lookup", _lookup_dot, [pins.test_asm_lookup_is_cosine_argmax]),
+    ("K-means assigns the farthest", asm, "kmeans_assign", _assign_farthest, [pins.test_kmeans_lloyd_steps]),
 ]
 
 

@@ -7,6 +7,7 @@ import pytest
 from hypothesis import given, settings, strategies as st
 from scipy.special import softmax as sp_softmax, logsumexp as sp_lse
 
+from oracle import asm
 from oracle import indexmem as im
 from oracle import moment_stream as ms
 from oracle import momentkv as mk
@@ -665,3 +666,97 @@ def test_memory_query_projection_special_cases():
     for h in range(H_q):
         f = np.where(-q[h] > 0, -q[h] + 1.0, np.exp(-q[h]))
         np.testing.assert_allclose(m[h], M[h // 2] @ f / (b[h // 2] @ f + 1e-6), rtol=1e-13)
+
+
+# ============================================================================ attention-state memory
+
+def test_asm_own_state_restores_full_attention():
+    # a query whose retrieved state is its own prefix state recovers attention over the
+    # prefix and the local tokens together (the online-softmax identity); a one-member
+    # cluster keeps its member's state exactly
+    # catches: a wrong merge weight, a dropped partition, an unscaled logit
+    r = np.random.default_rng(41)
+    N, H_q, H_kv, d, L, Lloc = 5, 4, 2, 8, 30, 7
+    Q = r.standard_normal((N, H_q, d))
+    K, V = r.standard_normal((L, H_kv, d)), r.standard_normal((L, H_kv, d))
+    Kl, Vl = r.standard_normal((Lloc, H_kv, d)), r.standard_normal((Lloc, H_kv, d))
+    sc = 1 / math.sqrt(d)
+    a, lse = asm.prefix_states(Q, K, V, sc)
+    for h in range(H_q):
+        g = h // 2
+        C = Q[:, h]                       # every query its own centroid
+        a_bar, lse_bar = asm.aggregate(a[:, h], lse[:, h], np.arange(N), N)
+        np.testing.assert_array_equal(a_bar, a[:, h])
+        np.testing.assert_array_equal(lse_bar, lse[:, h])
+        for i in range(N):
+            a_loc, l_loc = im.attention_state(Q[i, h], Kl[:, g], Vl[:, g], sc)
+            (o, l), k = asm.output(Q[i, h], C, a_bar, lse_bar, a_loc, l_loc)
+            assert k == i
+            keys, vals = np.vstack([K[:, g], Kl[:, g]]), np.vstack([V[:, g], Vl[:, g]])
+            w = sp_softmax(sc * keys @ Q[i, h])
+            np.testing.assert_allclose(o, w @ vals, rtol=1e-12)
+            assert l == pytest.approx(sp_lse(sc * keys @ Q[i, h]), rel=1e-13)
+
+
+def test_asm_aggregate_is_partition_weighted_mean():
+    # catches: an unweighted mean of the outputs, the summed (not mean) partition
+    r = np.random.default_rng(42)
+    N, d, K = 12, 6, 4
+    a, lse = r.standard_normal((N, d)), r.standard_normal(N) * 3
+    idx = np.array([0, 1, 1, 2, 0, 0, 1, 2, 2, 2, 0, 1])     # cluster 3 stays empty
+    a_bar, lse_bar = asm.aggregate(a, lse, idx, K)
+    for k in range(3):
+        m = idx == k
+        Z = np.exp(lse[m])
+        np.testing.assert_allclose(a_bar[k], (Z[:, None] * a[m]).sum(0) / Z.sum(), rtol=1e-12)
+        assert lse_bar[k] == pytest.approx(math.log(Z.mean()), rel=1e-12)
+    assert lse_bar[3] == -np.inf and not a_bar[3].any()
+    # identical members: the cluster's state is the member's
+    a2, l2 = asm.aggregate(np.tile(a[:1], (5, 1)), np.full(5, lse[0]), np.zeros(5, int), 1)
+    np.testing.assert_allclose(a2[0], a[0], rtol=1e-14)
+    assert l2[0] == pytest.approx(lse[0], rel=1e-14)
+
+
+def test_kmeans_lloyd_steps():
+    # catches: argmax instead of argmin, ties to the higher index, an empty cluster moved
+    r = np.random.default_rng(43)
+    centers = np.array([[10.0, 0, 0], [0, 10.0, 0], [0, 0, 10.0]])
+    X = np.vstack([c + 0.1 * r.standard_normal((20, 3)) for c in centers])
+    C0 = np.vstack([X[0], X[20], X[40], [100.0, 100, 100]])   # the last seed draws nobody
+    C, idx = asm.kmeans(X, C0, 3)
+    assert np.array_equal(idx, np.repeat([0, 1, 2], 20))
+    for k in range(3):
+        np.testing.assert_allclose(C[k], X[20 * k:20 * (k + 1)].mean(0), rtol=1e-13)
+    assert np.array_equal(C[3], [100.0, 100, 100])
+    # brute-force assignment and a tie between two equal centroids
+    Y = r.standard_normal((15, 3))
+    Cb = r.standard_normal((5, 3))
+    Cb[3] = Cb[1]
+    got, d2 = asm.kmeans_assign(Y, Cb)
+    for i in range(15):
+        dist = [float(((Y[i] - c) ** 2).sum()) for c in Cb]
+        assert got[i] == min(range(5), key=lambda k: (dist[k], k))
+        assert got[i] != 3
+    # Lloyd never increases the within-cluster sum of squares
+    Cc, last = Cb.copy(), None
+    for _ in range(5):
+        idx = asm.kmeans_assign(Y, Cc)[0]
+        inertia = sum(((Y[i] - Cc[idx[i]]) ** 2).sum() for i in range(15))
+        assert last is None or inertia <= last + 1e-12
+        last = inertia
+        Cc = asm.kmeans_update(Y, idx, Cc)
+
+
+def test_asm_lookup_is_cosine_argmax():
+    # catches: a plain dot product (sensitive to the centroid's norm)
+    r = np.random.default_rng(44)
+    C = r.standard_normal((9, 5))
+    for _ in range(20):
+        q = r.standard_normal(5)
+        k = asm.lookup(q, C)
+        cos = [float(c @ q / np.linalg.norm(c) / np.linalg.norm(q)) for c in C]
+        assert k == max(range(9), key=lambda j: (cos[j], -j))
+        assert asm.lookup(3.7 * q, C) == k
+        C2 = C.copy()
+        C2[k] *= 0.01                     # a short centroid in the same direction still wins
+        assert asm.lookup(q, C2) == k
