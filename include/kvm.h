@@ -332,6 +332,60 @@ kvm_status kvm_moment_stream_evict(const kvm_mstream_desc* desc, const void* q, 
                                    void* stream);
 
 /* ------------------------------------------------------------------------------------ *
+ * N3  Attention-state memory (ASM)                                       [ASM Method]
+ *
+ * A prefix is replaced by a lookup memory of attention states.  Per query head h (KV head
+ * g = h / G), with N calibration queries Q[i, h] and the prefix K, V (L tokens):
+ *   kvm_asm_prefix_states:  a[i, h] = sum_t softmax_t(Q[i,h] . K[t,g] / sqrt d) V[t,g],
+ *                           lse[i, h] = log sum_t exp(Q[i,h] . K[t,g] / sqrt d);
+ *   kvm_asm_kmeans:         Lloyd's iteration on the queries of each head: `iters` rounds of
+ *                           (assign to the nearest centroid by squared Euclidean distance,
+ *                           ties to the lower index; centroid = mean of its members, a
+ *                           centroid without members stays), then a final assignment;
+ *                           C [H_q, K, d] f32 holds the initial centroids on entry and the
+ *                           final ones on return, idx [H_q, N] i32 the final assignment;
+ *   kvm_asm_cluster_states: per cluster k the members' states merged with the online-softmax
+ *                           rule and the mean partition:
+ *                           a_bar[h, k] = sum_i Z_i a_i / sum_i Z_i (Z_i = exp lse_i),
+ *                           lse_bar[h, k] = log(sum_i Z_i / n_k)  (-inf, a_bar = 0 if n_k = 0;
+ *                           entries of idx outside [0, K) join no cluster);
+ *   kvm_asm_lookup:         for decode queries q [b, H_q, d]: k = the centroid of head h with
+ *                           the largest cosine similarity (ties: the lower index; a centroid at
+ *                           the origin is never chosen), and the merge with the query's local
+ *                           state (o_loc, lse_loc, e.g. from kvm_decode_attn_mem over the tokens
+ *                           after the prefix): lse = log(e^lse_loc + e^lse_bar[h,k]),
+ *                           o = e^(lse_loc - lse) o_loc + e^(lse_bar - lse) a_bar[h, k].
+ * The mean partition, the distance used for clustering and the cosine retrieval without
+ * whitening are this library's readings of the section.
+ * Q [N, H_q, d], q [b, H_q, d] bf16; K, V [L, H_kv, d] bf16 (or [H_kv, L, d] if
+ * kv_head_major); a, o_loc, o [.., H_q, d] f32; lse, lse_loc, lse_out [.., H_q] f32;
+ * a_bar [H_q, K, d], lse_bar [H_q, K] f32; idx_out [b, H_q] i32.  Supported: d in
+ * {64, 128}, K <= 256, bf16.  Arithmetic: fp32 distances and sums; the prefix attention on
+ * the matrix cores with fp32 accumulation and P as bf16 hi + lo.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t N;               /* calibration queries per head                                */
+  int32_t H_q, H_kv, d;
+  int32_t L;               /* prefix tokens                                               */
+  int32_t K;               /* centroids per head                                          */
+  int32_t dtype;           /* KVM_BF16                                                    */
+  int32_t kv_head_major;   /* prefix K/V layout                                           */
+} kvm_asm_desc;
+
+size_t kvm_asm_workspace_size(const kvm_asm_desc* desc);
+kvm_status kvm_asm_prefix_states(const kvm_asm_desc* desc, const void* Q, const void* K, const void* V,
+                                 float* a, float* lse, void* stream);
+kvm_status kvm_asm_kmeans(const kvm_asm_desc* desc, const void* Q, float* C, int32_t* idx, int32_t iters,
+                          void* ws, size_t ws_bytes, void* stream);
+kvm_status kvm_asm_cluster_states(const kvm_asm_desc* desc, const float* a, const float* lse,
+                                  const int32_t* idx, float* a_bar, float* lse_bar, void* ws,
+                                  size_t ws_bytes, void* stream);
+kvm_status kvm_asm_lookup(const kvm_asm_desc* desc, int32_t b, const void* q, const float* C,
+                          const float* a_bar, const float* lse_bar, const float* o_loc,
+                          const float* lse_loc, float* o, float* lse_out, int32_t* idx_out,
+                          void* stream);
+
+/* ------------------------------------------------------------------------------------ *
  * A8 + A9 / V3  Split-K decode attention with memory read-out          [IM 2.B; ASM; MKV 4]
  *
  * Per sequence bb and query head h (KV head g = h / G, G = H_q / H_kv):

@@ -59,6 +59,11 @@ class MReadDesc(C.Structure):
     _fields_ = [("b", i32), ("H_q", i32), ("H_kv", i32), ("d", i32), ("dtype", i32), ("scale", f32)]
 
 
+class AsmDesc(C.Structure):
+    _fields_ = [("N", i32), ("H_q", i32), ("H_kv", i32), ("d", i32), ("L", i32), ("K", i32), ("dtype", i32),
+                ("kv_head_major", i32)]
+
+
 class MStreamDesc(C.Structure):
     _fields_ = [("b", i32), ("H_q", i32), ("H_kv", i32), ("d", i32), ("P", i32), ("cap", i32), ("R", i32),
                 ("dtype", i32)]
@@ -83,6 +88,11 @@ SIGNATURES = {
     "kvm_decode_attn_mem": (C.c_int, [C.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     "kvm_mem_query": (C.c_int, [i32, i32, i32, vp, vp, vp, vp]),
+    "kvm_asm_workspace_size": (sz, [C.POINTER(AsmDesc)]),
+    "kvm_asm_prefix_states": (C.c_int, [C.POINTER(AsmDesc), vp, vp, vp, vp, vp, vp]),
+    "kvm_asm_kmeans": (C.c_int, [C.POINTER(AsmDesc), vp, vp, vp, i32, vp, sz, vp]),
+    "kvm_asm_cluster_states": (C.c_int, [C.POINTER(AsmDesc), vp, vp, vp, vp, vp, vp, sz, vp]),
+    "kvm_asm_lookup": (C.c_int, [C.POINTER(AsmDesc), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
     "kvm_len_add": (C.c_int, [vp, i32, i32, vp]),
     "kvm_stream_workspace_size": (sz, [C.POINTER(StreamDesc)]),
     "kvm_stream_evict": (C.c_int, [C.POINTER(StreamDesc)] + [vp] * 17 + [sz, vp]),

@@ -309,3 +309,78 @@ def kvm_moment_stream_evict(q, k_new, v_new, Kc, Vc, slot_pos, next_pos, moments
                                         _p(next_pos), _p(moments["n_e"]), _p(moments["s_k"]), _p(moments["s_v"]),
                                         _p(moments["S"]), _p(evict_slot), _p(ws), ws.numel(), _stream(stream)))
     return evict_slot
+
+
+# ------------------------------------------------------------------------------- ASM
+
+def asm_desc(Q, K_, K_centroids, kv_head_major=False):
+    N, H_q, d = Q.shape
+    if kv_head_major:
+        H_kv, L, _ = K_.shape
+    else:
+        L, H_kv, _ = K_.shape
+    return K.AsmDesc(N=N, H_q=H_q, H_kv=H_kv, d=d, L=L, K=K_centroids, dtype=_dtype(Q),
+                     kv_head_major=int(kv_head_major))
+
+
+def kvm_asm_prefix_states(Q, K_, V, kv_head_major=False, a=None, lse=None, stream=None):
+    """Attention states (a [N, H_q, d] f32, lse [N, H_q] f32) of calibration queries
+    Q [N, H_q, d] over the prefix K, V ([L, H_kv, d], or [H_kv, L, d] if kv_head_major)."""
+    _contig(Q, K_, V, a, lse)
+    desc = asm_desc(Q, K_, 1, kv_head_major)
+    if a is None:
+        a = torch.empty(Q.shape, dtype=torch.float32, device=Q.device)
+    if lse is None:
+        lse = torch.empty(Q.shape[:2], dtype=torch.float32, device=Q.device)
+    check(lib().kvm_asm_prefix_states(C.byref(desc), _p(Q), _p(K_), _p(V), _p(a), _p(lse), _stream(stream)))
+    return a, lse
+
+
+def _asm_ws(desc, device, stream, ws):
+    nb = lib().kvm_asm_workspace_size(C.byref(desc))
+    return workspace(nb, device, stream, "asm") if ws is None else ws
+
+
+def kvm_asm_kmeans(Q, C_, iters, idx=None, stream=None, ws=None):
+    """Lloyd's K-means per head on Q [N, H_q, d] from centroids C_ [H_q, K, d] f32
+    (updated in place).  Returns idx [H_q, N] i32, the final assignment."""
+    _contig(Q, C_, idx)
+    N, H_q, d = Q.shape
+    desc = K.AsmDesc(N=N, H_q=H_q, H_kv=1, d=d, L=1, K=C_.shape[1], dtype=_dtype(Q), kv_head_major=0)
+    if idx is None:
+        idx = torch.empty((H_q, N), dtype=torch.int32, device=Q.device)
+    ws = _asm_ws(desc, Q.device, stream, ws)
+    check(lib().kvm_asm_kmeans(C.byref(desc), _p(Q), _p(C_), _p(idx), int(iters), _p(ws), ws.numel(),
+                               _stream(stream)))
+    return idx
+
+
+def kvm_asm_cluster_states(a, lse, idx, n_centroids, a_bar=None, lse_bar=None, stream=None, ws=None):
+    """Per-cluster attention states from the members' (a [N, H_q, d], lse [N, H_q]) and the
+    assignment idx [H_q, N]: a_bar [H_q, K, d], lse_bar [H_q, K] (f32)."""
+    _contig(a, lse, idx, a_bar, lse_bar)
+    N, H_q, d = a.shape
+    desc = K.AsmDesc(N=N, H_q=H_q, H_kv=1, d=d, L=1, K=n_centroids, dtype=K.KVM_BF16, kv_head_major=0)
+    if a_bar is None:
+        a_bar = torch.empty((H_q, n_centroids, d), dtype=torch.float32, device=a.device)
+    if lse_bar is None:
+        lse_bar = torch.empty((H_q, n_centroids), dtype=torch.float32, device=a.device)
+    ws = _asm_ws(desc, a.device, stream, ws)
+    check(lib().kvm_asm_cluster_states(C.byref(desc), _p(a), _p(lse), _p(idx), _p(a_bar), _p(lse_bar), _p(ws),
+                                       ws.numel(), _stream(stream)))
+    return a_bar, lse_bar
+
+
+def kvm_asm_lookup(q, C_, a_bar, lse_bar, o_loc, lse_loc, o=None, lse_out=None, idx_out=None, stream=None):
+    """Retrieval by cosine similarity and the merge with the local state: returns
+    (o [b, H_q, d] f32, idx_out [b, H_q] i32); lse_out [b, H_q] is filled if given."""
+    _contig(q, C_, a_bar, lse_bar, o_loc, lse_loc, o, lse_out, idx_out)
+    b, H_q, d = q.shape
+    desc = K.AsmDesc(N=1, H_q=H_q, H_kv=1, d=d, L=1, K=C_.shape[1], dtype=_dtype(q), kv_head_major=0)
+    if o is None:
+        o = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if idx_out is None:
+        idx_out = torch.empty((b, H_q), dtype=torch.int32, device=q.device)
+    check(lib().kvm_asm_lookup(C.byref(desc), b, _p(q), _p(C_), _p(a_bar), _p(lse_bar), _p(o_loc), _p(lse_loc),
+                               _p(o), _p(lse_out), _p(idx_out), _stream(stream)))
+    return o, idx_out

@@ -1,0 +1,543 @@
+// Attention-state memory (ASM) [ASM Method]: a prefix is replaced by a lookup memory of
+// precomputed attention states (a, Z).
+//
+// Offline (calibration):
+//   prefix_states_kernel   (a, lse) of every calibration query over the prefix: attention
+//                          on the matrix cores, 32 queries per wave against 32-key tiles
+//                          staged in LDS and shared by the block's 4 waves (heads of one
+//                          KV group), online softmax in the log2 domain, P as bf16 hi + lo
+//   kmeans_assign_kernel   nearest centroid per query, exact fp32 squared distances
+//   cluster_part_kernel    per chunk of queries: every cluster's running sum (K-means
+//                          update) or running online-softmax state (the cluster's
+//                          attention state), rows taken in index order, in LDS
+//   cluster_reduce_kernel  the chunks combined in order: centroid means, or the cluster
+//                          states (a, lse - log n)
+// Online (decode):
+//   lookup_merge_kernel    the largest cosine similarity among a head's centroids, and the
+//                          retrieved state merged with the query's local attention state
+#include "common.hpp"
+
+namespace kvm {
+
+// ------------------------------------------------------------------ prefix states
+struct PrefixArgs {
+  const uint16_t* Q;   // [N, H_q, D]
+  const uint16_t* K;   // prefix keys: element (t, g, c) at t * ts + g * hs + c
+  const uint16_t* V;
+  float* a;            // [N, H_q, D]
+  float* lse;          // [N, H_q]
+  int N, H_q, G, L, ts, hs;
+  float sl2;           // logit scale * log2(e)
+};
+
+constexpr int kPT = 32;   // keys per tile
+
+// grid (ceil(G * ceil(N / 32) / 4), H_kv), 256 threads.  Wave w of block x takes item
+// i = 4x + w: query tile i / G of head g G + i % G.  S^T = K Q^T puts keys on the rows of
+// the 32 x 32 accumulator, so each lane holds 16 keys of one query column: the row max and
+// sum need one exchange between the half-waves, and the lane's probabilities are already
+// the A operand of P V (with V's keys gathered in the same order from a dim-major tile).
+template <int D>
+__global__ __launch_bounds__(256) void prefix_states_kernel(PrefixArgs a) {
+  constexpr int KS = D / 16, NT = D / 32;
+  constexpr int KP = D + 8;                  // sK row pitch (bf16)
+  constexpr int VP = kPT + 8;                // sV row pitch (bf16)
+  constexpr int CH = kPT * D / 8;            // 16-byte chunks per tile
+  constexpr int CPT = (CH + 255) / 256;      // chunks per thread
+  __shared__ __align__(16) uint16_t sK[2][kPT * KP];
+  __shared__ __align__(16) uint16_t sV[2][D * VP];
+  __shared__ float sRow[4][kPT];
+
+  const int g = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int nqt = (a.N + 31) / 32;
+  const int item = blockIdx.x * 4 + wave;
+  const bool active = item < a.G * nqt;
+  const int h = g * a.G + (active ? item % a.G : 0);
+  const int q0 = (active ? item / a.G : 0) * 32;
+
+  // B operand: lane (query q0 + col) holds dims ks * 16 + half * 8 .. + 8 (zeros past N)
+  bf16x8_t qb[KS];
+  {
+    const auto rq = make_rsrc(a.Q + (size_t)h * D, ((a.N - 1) * a.H_q * D + D) * 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = load16(rq, ((q0 + col) * a.H_q * D + ks * 16 + half * 8) * 2);
+      __builtin_memcpy(&qb[ks], &v, 16);
+    }
+  }
+  // tiles: chunk c = tid + 256 u is key c / (D / 8), dims (c % (D / 8)) * 8 .. + 8; keys past
+  // the prefix read zeros
+  const int span = ((a.L - 1) * a.ts + D) * 2;
+  const auto rk = make_rsrc(a.K + (size_t)g * a.hs, span);
+  const auto rv = make_rsrc(a.V + (size_t)g * a.hs, span);
+  uint4 pk[CPT], pv[CPT];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + 256 * u, kk = c / (D / 8), dc = c % (D / 8);
+      const int off = c < CH ? ((k0 + kk) * a.ts + dc * 8) * 2 : span;
+      pk[u] = load16(rk, off);
+      pv[u] = load16(rv, off);
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + 256 * u, kk = c / (D / 8), dc = c % (D / 8);
+      if (c < CH) {
+        *reinterpret_cast<uint4*>(sK[buf] + kk * KP + dc * 8) = pk[u];
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(&pv[u]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sV[buf][(dc * 8 + i) * VP + kk] = e[i];
+      }
+    }
+  };
+
+  float m = -INFINITY, l = 0.f;   // per query column (both half-waves hold the same)
+  f32x16_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[nt][j] = 0.f;
+
+  const int ntile = (a.L + kPT - 1) / kPT;
+  fetch(0);
+  stage(0);
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < ntile) fetch((t + 1) * kPT);
+    if (active) {
+      f32x16_t s;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s[j] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(sK[cur] + col * KP + ks * 16 + half * 8);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qb[ks], s, 0, 0, 0);
+      }
+      // key of accumulator row j: 8 (j / 4) + 4 half + j % 4
+      float p[16], mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = t * kPT + 8 * (j / 4) + 4 * half + (j & 3);
+        p[j] = key < a.L ? s[j] * a.sl2 : -INFINITY;
+        mx = fmaxf(mx, p[j]);
+      }
+      mx = fmaxf(mx, shfl_xor32(mx));
+      const float mn = fmaxf(m, mx);   // finite: every tile holds a key of the prefix
+      const float corr = __builtin_amdgcn_exp2f(m - mn);
+      float ls = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(p[j] - mn);
+        ls += p[j];
+      }
+      ls += shfl_xor32(ls);
+      l = fmaf(l, corr, ls);
+      m = mn;
+      // the output rows are queries: their factors come through LDS (in order within a wave)
+      if (half == 0) sRow[wave][col] = corr;
+      float cr[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) cr[j] = sRow[wave][8 * (j / 4) + 4 * half + (j & 3)];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[nt][j] *= cr[j];
+      // P V: K-step kk takes this lane's p[8 kk .. 8 kk + 7], keys 16 kk + 8 (i / 4) + 4 half + i % 4
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float pp[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pp[i] = p[8 * kk + i];
+        bf16x8_t ph, pm, plo;
+        split3_bf16x8(pp, ph, pm, plo);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint16_t* vr = sV[cur] + (nt * 32 + col) * VP + 16 * kk + 4 * half;
+          const uint2 v0 = *reinterpret_cast<const uint2*>(vr), v1 = *reinterpret_cast<const uint2*>(vr + 8);
+          const uint4 bv = make_uint4(v0.x, v0.y, v1.x, v1.y);
+          bf16x8_t B;
+          __builtin_memcpy(&B, &bv, 16);
+          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph, B, acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pm, B, acc[nt], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < ntile) stage(cur ^ 1);
+    __syncthreads();
+  }
+  if (!active) return;
+  if (half == 0) sRow[wave][col] = 1.f / l;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 8 * (j / 4) + 4 * half + (j & 3);
+      if (q0 + r < a.N) a.a[((size_t)(q0 + r) * a.H_q + h) * D + nt * 32 + col] = acc[nt][j] * sRow[wave][r];
+    }
+  if (half == 0 && q0 + col < a.N)
+    a.lse[(size_t)(q0 + col) * a.H_q + h] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+}
+
+// ------------------------------------------------------------------ K-means assignment
+// grid (ceil(N / 64), H), 256 threads: 4 lanes per query (D / 4 dims each), centroids in
+// LDS tiles of 32.  Squared distances are summed in fp32; ties keep the lower index.
+template <int D>
+__global__ __launch_bounds__(256) void kmeans_assign_kernel(const uint16_t* X, const float* C, int32_t* idx,
+                                                            int N, int H, int K) {
+  constexpr int DL = D / 4;
+  __shared__ __align__(16) float sC[32][D + 4];
+  const int hh = blockIdx.y, tid = threadIdx.x;
+  const int row = blockIdx.x * 64 + tid / 4, part = tid % 4;
+  float x[DL];
+  {
+    const auto rx = make_rsrc(X + (size_t)hh * D, ((N - 1) * H * D + D) * 2);
+#pragma unroll
+    for (int c = 0; c < DL; c += 8) {
+      const uint4 v = load16(rx, (row * H * D + part * DL + c) * 2);
+      float f[8];
+      Vec16<uint16_t>::unpack(v, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[c + e] = f[e];
+    }
+  }
+  const float* Ch = C + (size_t)hh * K * D;
+  float best = INFINITY;
+  int bi = 0;
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    __syncthreads();
+    for (int i = tid; i < 32 * D / 4; i += 256) {
+      const int kk = i / (D / 4), c4 = i % (D / 4);
+      const float4 v = k0 + kk < K ? *reinterpret_cast<const float4*>(Ch + (size_t)(k0 + kk) * D + c4 * 4)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(&sC[kk][c4 * 4]) = v;
+    }
+    __syncthreads();
+    const int nk = min(32, K - k0);
+    for (int kk = 0; kk < nk; ++kk) {
+      float d2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < DL; ++c) {
+        const float t = x[c] - sC[kk][part * DL + c];
+        d2 = fmaf(t, t, d2);
+      }
+      d2 = group_sum<4>(d2);
+      if (d2 < best) { best = d2; bi = k0 + kk; }
+    }
+  }
+  if (part == 0 && row < N) idx[(size_t)hh * N + row] = bi;
+}
+
+// ------------------------------------------------------------------ cluster sums / states
+// MODE 0: every cluster's sum of its member queries (bf16 X) and its member count.
+// MODE 1: every cluster's running online-softmax state of its members' (a, lse).
+struct ClusterArgs {
+  const uint16_t* X;    // MODE 0: [N, H, D] bf16
+  const float* A;       // MODE 1: [N, H, D] f32
+  const float* lse;     // MODE 1: [N, H]
+  const int32_t* idx;   // [H, N]
+  float* part;          // [H, nchunk, K, D + 4]: sums (or scaled a), count (or Z), max lse, count
+  int N, H, K, rows;    // rows per chunk
+};
+
+// grid (nchunk, H), D threads: thread = one dim; rows of the chunk in index order, each
+// folded into its cluster's LDS row (one writer per element: deterministic).  The rows'
+// operands are fetched 8 at a time ahead of their use.
+constexpr int kRowExtra = 4;   // per cluster row: D values, then count (or Z), max lse, count
+
+template <int D, int MODE>
+__global__ __launch_bounds__(D) void cluster_part_kernel(ClusterArgs a) {
+  extern __shared__ float sAcc[];   // [K][D + kRowExtra]
+  constexpr int RW = D + kRowExtra;
+  const int ch = blockIdx.x, hh = blockIdx.y, tid = threadIdx.x;
+  for (int i = tid; i < a.K * RW; i += D) sAcc[i] = i % RW == D + 1 ? -INFINITY : 0.f;
+  __syncthreads();
+  const int r0 = ch * a.rows, r1 = min(a.N, r0 + a.rows);
+  const int32_t* ix = a.idx + (size_t)hh * a.N;
+  for (int b0 = r0; b0 < r1; b0 += 8) {
+    int k[8];
+    float v[8], ls[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = min(b0 + u, r1 - 1);
+      k[u] = ix[r];
+      if (MODE == 0) v[u] = bf16_to_f32(a.X[((size_t)r * a.H + hh) * D + tid]);
+      else {
+        v[u] = a.A[((size_t)r * a.H + hh) * D + tid];
+        ls[u] = a.lse[(size_t)r * a.H + hh];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (b0 + u >= r1) break;
+      if (k[u] < 0 || k[u] >= a.K) continue;   // an assignment outside [0, K) joins no cluster
+      float* acc = sAcc + k[u] * RW;
+      if (MODE == 0) {   // each thread owns its element: no barrier between rows
+        acc[tid] += v[u];
+        if (tid == 0) acc[D] += 1.f;
+      } else {
+        // running state: acc[D + 1] = max lse, acc[D] = sum exp(lse - max), acc[dim] = sum exp(lse - max) a
+        const float mo = acc[D + 1], mn = fmaxf(mo, ls[u]);
+        const float f = __expf(mo - mn), w = __expf(ls[u] - mn);
+        acc[tid] = fmaf(acc[tid], f, w * v[u]);
+        __syncthreads();   // every dim has read the old max
+        if (tid == 0) { acc[D] = fmaf(acc[D], f, w); acc[D + 1] = mn; acc[D + 2] += 1.f; }
+        __syncthreads();
+      }
+    }
+  }
+  __syncthreads();   // the copy below reads elements that other threads updated
+  float* out = a.part + ((size_t)hh * gridDim.x + ch) * a.K * RW;
+  for (int i = tid; i < a.K * RW; i += D) out[i] = sAcc[i];
+}
+
+// grid (K, H), D threads: chunk partials combined in chunk order.
+// MODE 0: centroid = sum / count (a cluster without members keeps C).
+// MODE 1: a_bar = sum_c e^(m_c - m) S_c / sum_c e^(m_c - m) Z_c, lse_bar = m + log Z - log n
+//         (a cluster without members: a_bar = 0, lse_bar = -inf).
+template <int D, int MODE>
+__global__ __launch_bounds__(D) void cluster_reduce_kernel(const float* part, int nchunk, int K, float* C,
+                                                          float* a_bar, float* lse_bar) {
+  constexpr int RW = D + kRowExtra;
+  const int k = blockIdx.x, hh = blockIdx.y, tid = threadIdx.x;
+  const float* p0 = part + ((size_t)hh * nchunk * K + k) * RW;
+  const size_t cs = (size_t)K * RW;   // chunk stride
+  if (MODE == 0) {
+    float s = 0.f, n = 0.f;
+    for (int c = 0; c < nchunk; ++c) {
+      s += p0[c * cs + tid];
+      n += p0[c * cs + D];
+    }
+    float* cr = C + ((size_t)hh * K + k) * D;
+    if (n > 0.f) cr[tid] = s / n;
+  } else {
+    float m = -INFINITY, z = 0.f, s = 0.f, n = 0.f;
+    for (int c = 0; c < nchunk; ++c) {
+      const float mc = p0[c * cs + D + 1];
+      if (mc == -INFINITY) continue;
+      const float mn = fmaxf(m, mc);
+      const float f = __expf(m - mn), fc = __expf(mc - mn);
+      s = fmaf(s, f, fc * p0[c * cs + tid]);
+      z = fmaf(z, f, fc * p0[c * cs + D]);
+      n += p0[c * cs + D + 2];
+      m = mn;
+    }
+    a_bar[((size_t)hh * K + k) * D + tid] = z > 0.f ? s / z : 0.f;
+    if (tid == 0) lse_bar[(size_t)hh * K + k] = z > 0.f ? m + __logf(z) - __logf(n) : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------ lookup + merge
+// grid (H, b), 256 threads: cosine similarity of the query against the head's K centroids
+// (q . c / ||c||; ||q|| does not change the argmax), the largest (ties: the lower index),
+// then the retrieved state merged with the local one:
+//   lse = log(e^lse_loc + e^lse_bar), o = e^(lse_loc - lse) o_loc + e^(lse_bar - lse) a_bar.
+template <int D>
+__global__ __launch_bounds__(256) void lookup_merge_kernel(const uint16_t* q, const float* C,
+                                                          const float* a_bar, const float* lse_bar,
+                                                          const float* o_loc, const float* lse_loc, float* o,
+                                                          float* lse_out, int32_t* idx_out, int H, int K) {
+  const int hh = blockIdx.x, bb = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float sq[D];
+  __shared__ float s_best[4];
+  __shared__ int s_bi[4];
+  const size_t row = (size_t)bb * H + hh;
+  if (tid < D) sq[tid] = bf16_to_f32(q[row * D + tid]);
+  __syncthreads();
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int k = tid; k < K; k += 256) {
+    const float* c = C + ((size_t)hh * K + k) * D;
+    float dot = 0.f, n2 = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < D; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(c + i);
+      dot = fmaf(v.x, sq[i], dot);
+      dot = fmaf(v.y, sq[i + 1], dot);
+      dot = fmaf(v.z, sq[i + 2], dot);
+      dot = fmaf(v.w, sq[i + 3], dot);
+      n2 = fmaf(v.x, v.x, n2);
+      n2 = fmaf(v.y, v.y, n2);
+      n2 = fmaf(v.z, v.z, n2);
+      n2 = fmaf(v.w, v.w, n2);
+    }
+    const float cs = n2 > 0.f ? dot * rsqrtf(n2) : -INFINITY;   // a centroid at the origin is never retrieved
+    if (cs > best) { best = cs; bi = k; }
+  }
+  for (int off = 1; off < 64; off <<= 1) {
+    const float ob = __shfl_xor(best, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+  }
+  if (lane == 0) { s_best[wave] = best; s_bi[wave] = bi; }
+  __syncthreads();
+  float b = s_best[0];
+  int k = s_bi[0];
+  for (int w = 1; w < 4; ++w)
+    if (s_best[w] > b || (s_best[w] == b && s_bi[w] < k)) { b = s_best[w]; k = s_bi[w]; }
+  if (k >= K) k = 0;   // every centroid at the origin: the first one (its state merges as is)
+  const float l1 = lse_loc[row], l2 = lse_bar[(size_t)hh * K + k];
+  const float mx = fmaxf(l1, l2);
+  const float w1 = l1 == -INFINITY ? 0.f : __expf(l1 - mx), w2 = l2 == -INFINITY ? 0.f : __expf(l2 - mx);
+  const float z = w1 + w2;
+  if (tid < D) {
+    const float v = z > 0.f ? (w1 * o_loc[row * D + tid] + w2 * a_bar[((size_t)hh * K + k) * D + tid]) / z : 0.f;
+    o[row * D + tid] = v;
+  }
+  if (tid == 0) {
+    idx_out[row] = k;
+    if (lse_out) lse_out[row] = z > 0.f ? mx + __logf(z) : -INFINITY;
+  }
+}
+
+}  // namespace kvm
+
+using namespace kvm;
+
+// ------------------------------------------------------------------ host side
+
+static kvm_status check_asm_desc(const kvm_asm_desc* d) {
+  KVM_PTR(d);
+  KVM_REQUIRE(d->N > 0 && d->H_q > 0 && d->H_kv > 0 && d->L > 0, KVM_ERR_SHAPE, "N, H_q, H_kv, L must be positive");
+  KVM_REQUIRE(d->d == 64 || d->d == 128, KVM_ERR_SHAPE, "head dim %d not in {64, 128}", d->d);
+  KVM_REQUIRE(d->H_q % d->H_kv == 0, KVM_ERR_SHAPE, "H_q %d not a multiple of H_kv %d", d->H_q, d->H_kv);
+  KVM_REQUIRE(d->dtype == KVM_BF16, KVM_ERR_DTYPE, "ASM takes bf16 queries and prefix (dtype %d)", d->dtype);
+  KVM_REQUIRE(d->K >= 1 && d->K <= 256, KVM_ERR_RANGE, "K %d not in [1, 256]", d->K);
+  KVM_REQUIRE((long long)d->N * d->H_q * d->d * 2 < 0x7fffffffLL, KVM_ERR_RANGE, "N x H_q x d too large");
+  const long long ts = d->kv_head_major ? d->d : (long long)d->H_kv * d->d;
+  KVM_REQUIRE(((long long)d->L * ts + d->d) * 2 < 0x7fffffffLL, KVM_ERR_RANGE, "prefix of %d tokens too long", d->L);
+  return KVM_OK;
+}
+
+static int asm_chunk_rows(const kvm_asm_desc* d) { return 512; }
+static int asm_chunks(const kvm_asm_desc* d) { return (d->N + asm_chunk_rows(d) - 1) / asm_chunk_rows(d); }
+
+struct AsmWs { size_t part, total; };
+static AsmWs asm_ws(const kvm_asm_desc* d) {
+  AsmWs w;
+  w.part = 0;
+  w.total = align_up((size_t)d->H_q * asm_chunks(d) * d->K * (d->d + kRowExtra) * sizeof(float), 256);
+  return w;
+}
+
+static kvm_status set_lds(const void* fn, int bytes) {
+  if (bytes <= 65536) return KVM_OK;
+  return check_hip(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes), "LDS size");
+}
+
+template <int D, int MODE>
+static kvm_status cluster_pass(const ClusterArgs& a, int nchunk, float* C, float* a_bar, float* lse_bar,
+                               hipStream_t s) {
+  const int lds = a.K * (D + kRowExtra) * (int)sizeof(float);
+  kvm_status st = set_lds(reinterpret_cast<const void*>(&cluster_part_kernel<D, MODE>), lds);
+  if (st != KVM_OK) return st;
+  hipLaunchKernelGGL((cluster_part_kernel<D, MODE>), dim3(nchunk, a.H), dim3(D), lds, s, a);
+  hipLaunchKernelGGL((cluster_reduce_kernel<D, MODE>), dim3(a.K, a.H), dim3(D), 0, s, a.part, nchunk, a.K, C, a_bar,
+                     lse_bar);
+  return check_hip(hipGetLastError(), "cluster pass launch");
+}
+
+extern "C" size_t kvm_asm_workspace_size(const kvm_asm_desc* d) {
+  if (check_asm_desc(d) != KVM_OK) return 0;
+  return asm_ws(d).total;
+}
+
+extern "C" kvm_status kvm_asm_prefix_states(const kvm_asm_desc* d, const void* Q, const void* K, const void* V,
+                                            float* a_out, float* lse_out, void* stream) {
+  kvm_status st = check_asm_desc(d);
+  if (st != KVM_OK) return st;
+  KVM_PTR_ALIGNED(Q); KVM_PTR_ALIGNED(K); KVM_PTR_ALIGNED(V); KVM_PTR_ALIGNED(a_out); KVM_PTR_ALIGNED(lse_out);
+  st = require_gfx950();
+  if (st != KVM_OK) return st;
+  PrefixArgs a{};
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.a = a_out; a.lse = lse_out;
+  a.N = d->N; a.H_q = d->H_q; a.G = d->H_q / d->H_kv; a.L = d->L;
+  a.ts = d->kv_head_major ? d->d : d->H_kv * d->d;
+  a.hs = d->kv_head_major ? d->L * d->d : d->d;
+  a.sl2 = 1.4426950408889634f / sqrtf((float)d->d);
+  const int items = a.G * ((d->N + 31) / 32);
+  const dim3 grid((items + 3) / 4, d->H_kv);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->d == 128) hipLaunchKernelGGL(prefix_states_kernel<128>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(prefix_states_kernel<64>, grid, dim3(256), 0, s, a);
+  return check_hip(hipGetLastError(), "prefix states launch");
+}
+
+extern "C" kvm_status kvm_asm_kmeans(const kvm_asm_desc* d, const void* Q, float* C, int32_t* idx, int32_t iters,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  kvm_status st = check_asm_desc(d);
+  if (st != KVM_OK) return st;
+  KVM_REQUIRE(iters >= 0, KVM_ERR_RANGE, "iters %d < 0", iters);
+  KVM_PTR_ALIGNED(Q); KVM_PTR_ALIGNED(C); KVM_PTR_ALIGNED(idx);
+  const AsmWs w = asm_ws(d);
+  KVM_REQUIRE(ws != nullptr && ws_bytes >= w.total, KVM_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+  KVM_ALIGNED(ws);
+  st = require_gfx950();
+  if (st != KVM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto* Xb = static_cast<const uint16_t*>(Q);
+  const int H = d->H_q, N = d->N, K = d->K, nchunk = asm_chunks(d);
+  ClusterArgs ca{};
+  ca.X = Xb; ca.idx = idx; ca.part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.part);
+  ca.N = N; ca.H = H; ca.K = K; ca.rows = asm_chunk_rows(d);
+  const dim3 agrid((N + 63) / 64, H);
+  for (int it = 0; it <= iters; ++it) {
+    if (d->d == 128) hipLaunchKernelGGL(kmeans_assign_kernel<128>, agrid, dim3(256), 0, s, Xb, C, idx, N, H, K);
+    else hipLaunchKernelGGL(kmeans_assign_kernel<64>, agrid, dim3(256), 0, s, Xb, C, idx, N, H, K);
+    st = check_hip(hipGetLastError(), "kmeans assign launch");
+    if (st != KVM_OK || it == iters) return st;
+    st = d->d == 128 ? cluster_pass<128, 0>(ca, nchunk, C, nullptr, nullptr, s)
+                     : cluster_pass<64, 0>(ca, nchunk, C, nullptr, nullptr, s);
+    if (st != KVM_OK) return st;
+  }
+  return KVM_OK;
+}
+
+extern "C" kvm_status kvm_asm_cluster_states(const kvm_asm_desc* d, const float* a_in, const float* lse_in,
+                                             const int32_t* idx, float* a_bar, float* lse_bar, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  kvm_status st = check_asm_desc(d);
+  if (st != KVM_OK) return st;
+  KVM_PTR_ALIGNED(a_in); KVM_PTR_ALIGNED(lse_in); KVM_PTR_ALIGNED(idx); KVM_PTR_ALIGNED(a_bar);
+  KVM_PTR_ALIGNED(lse_bar);
+  const AsmWs w = asm_ws(d);
+  KVM_REQUIRE(ws != nullptr && ws_bytes >= w.total, KVM_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+  KVM_ALIGNED(ws);
+  st = require_gfx950();
+  if (st != KVM_OK) return st;
+  ClusterArgs ca{};
+  ca.A = a_in; ca.lse = lse_in; ca.idx = idx; ca.part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.part);
+  ca.N = d->N; ca.H = d->H_q; ca.K = d->K; ca.rows = asm_chunk_rows(d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return d->d == 128 ? cluster_pass<128, 1>(ca, asm_chunks(d), nullptr, a_bar, lse_bar, s)
+                     : cluster_pass<64, 1>(ca, asm_chunks(d), nullptr, a_bar, lse_bar, s);
+}
+
+extern "C" kvm_status kvm_asm_lookup(const kvm_asm_desc* d, int32_t b, const void* q, const float* C,
+                                     const float* a_bar, const float* lse_bar, const float* o_loc,
+                                     const float* lse_loc, float* o, float* lse_out, int32_t* idx_out,
+                                     void* stream) {
+  kvm_status st = check_asm_desc(d);
+  if (st != KVM_OK) return st;
+  KVM_REQUIRE(b > 0, KVM_ERR_SHAPE, "b must be positive");
+  KVM_PTR_ALIGNED(q); KVM_PTR_ALIGNED(C); KVM_PTR_ALIGNED(a_bar); KVM_PTR_ALIGNED(lse_bar); KVM_PTR_ALIGNED(o_loc);
+  KVM_PTR_ALIGNED(lse_loc); KVM_PTR_ALIGNED(o); KVM_PTR_ALIGNED(idx_out); KVM_OPT_ALIGNED(lse_out);
+  st = require_gfx950();
+  if (st != KVM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(d->H_q, b);
+  const auto* qb = static_cast<const uint16_t*>(q);
+  if (d->d == 128)
+    hipLaunchKernelGGL(lookup_merge_kernel<128>, grid, dim3(256), 0, s, qb, C, a_bar, lse_bar, o_loc, lse_loc, o,
+                       lse_out, idx_out, d->H_q, d->K);
+  else
+    hipLaunchKernelGGL(lookup_merge_kernel<64>, grid, dim3(256), 0, s, qb, C, a_bar, lse_bar, o_loc, lse_loc, o,
+                       lse_out, idx_out, d->H_q, d->K);
+  return check_hip(hipGetLastError(), "asm lookup launch");
+}

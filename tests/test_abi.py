@@ -106,3 +106,25 @@ def test_moment_stream_validation(L):
     d = K.MStreamDesc(b=2, H_q=32, H_kv=8, d=128, P=1024, cap=1024, R=16, dtype=K.KVM_BF16)
     # logits [pairs, G, P] and norms [pairs, P], f32, each 256-byte aligned
     assert L.kvm_moment_stream_workspace_size(C.byref(d)) == 16 * 4 * 1024 * 4 + 16 * 1024 * 4
+
+
+def test_asm_validation(L):
+    from learned_kv_cache_mqa_amd import _lib as K
+
+    def desc(**kw):
+        d = K.AsmDesc(N=4096, H_q=32, H_kv=8, d=128, L=16384, K=256, dtype=K.KVM_BF16, kv_head_major=0)
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return d
+    P = lambda *xs: [C.c_void_p(FAKE + 1024 * i) for i in range(len(xs))]
+    f = lambda d, **kw: L.kvm_asm_prefix_states(C.byref(d), *P(1, 2, 3, 4, 5), None)
+    assert f(desc(d=96)) == 2
+    assert f(desc(H_q=36)) == 2
+    assert f(desc(dtype=K.KVM_F32)) == 3
+    assert f(desc(K=257)) == 5
+    assert f(desc(L=0)) == 2
+    assert L.kvm_asm_kmeans(C.byref(desc()), *P(1, 2, 3), -1, C.c_void_p(FAKE), 1 << 30, None) == 5
+    assert L.kvm_asm_kmeans(C.byref(desc()), *P(1, 2, 3), 3, C.c_void_p(FAKE), 16, None) == 6
+    assert L.kvm_asm_lookup(C.byref(desc()), 0, *P(1, 2, 3, 4, 5, 6, 7, 8, 9), None) == 2
+    # partial rows [H, chunks of 512 queries, K, d + 4] f32
+    assert L.kvm_asm_workspace_size(C.byref(desc())) == 32 * 8 * 256 * 132 * 4
