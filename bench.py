@@ -279,6 +279,43 @@ def time_rows(torch, api, KL, dev):
         rows["N2_decode_step_us_" + ("projected" if proj else "plain")] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
     rows["N2_workload"] = (f"decode layer-step, batch {c3.b}, {c3.H_q}/{c3.H_kv} heads, d {c3.d}, {n3} cached slots: "
                            "plain read-out vs read-out addressed with W_m q (one extra kernel), HIP graph")
+    # N3: the attention-state memory at the 8B shapes, a 16K-token prefix
+    Nc, Lp, Kc, iters = 4096, 16384, 256, 10
+    Qc = rn(Nc, c3.H_q, c3.d)
+    Kp, Vp = rn(Lp, c3.H_kv, c3.d), rn(Lp, c3.H_kv, c3.d)
+    a_c, l_c = api.kvm_asm_prefix_states(Qc, Kp, Vp)
+    C0 = Qc[:Kc].float().transpose(0, 1).contiguous()
+    torch.cuda.synchronize()
+
+    def timed(fn, reps):
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    t_ps = timed(lambda: api.kvm_asm_prefix_states(Qc, Kp, Vp, a=a_c, lse=l_c), 3)
+    flops = 4.0 * Nc * Lp * c3.d * c3.H_q
+    rows["N3_prefix_states_ms"] = round(t_ps, 3)
+    rows["N3_prefix_states_tflops"] = round(flops / t_ps / 1e9, 1)
+    Cw = C0.clone()
+    idx_c = api.kvm_asm_kmeans(Qc, Cw, iters)
+    t_km = timed(lambda: api.kvm_asm_kmeans(Qc, C0.clone(), iters, idx=idx_c), 3)
+    rows["N3_kmeans_ms"] = round(t_km, 3)
+    ab_c, lb_c = api.kvm_asm_cluster_states(a_c, l_c, idx_c, Kc)
+    rows["N3_cluster_states_ms"] = round(timed(lambda: api.kvm_asm_cluster_states(a_c, l_c, idx_c, Kc, a_bar=ab_c,
+                                                                                     lse_bar=lb_c), 5), 4)
+    qd = rn(c3.b, c3.H_q, c3.d)
+    o_l = torch.randn((c3.b, c3.H_q, c3.d), generator=g, device=dev)
+    l_l = torch.randn((c3.b, c3.H_q), generator=g, device=dev)
+    o_m = torch.empty_like(o_l)
+    i_m = torch.empty((c3.b, c3.H_q), dtype=torch.int32, device=dev)
+    rows["N3_lookup_merge_us"] = round(1e3 * timed(lambda: api.kvm_asm_lookup(qd, Cw, ab_c, lb_c, o_l, l_l, o=o_m,
+                                                                             idx_out=i_m), 20), 2)
+    rows["N3_workload"] = (f"ASM, {c3.H_q}/{c3.H_kv} heads, d {c3.d}: {Nc} calibration queries per head over a "
+                           f"{Lp}-token prefix (4 N L d H_q flops), K-means with {Kc} centroids x {iters} iterations "
+                           f"(+ the cluster states), retrieval + merge for {c3.b} decode queries")
     return rows
 
 
