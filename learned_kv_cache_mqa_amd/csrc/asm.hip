@@ -4,14 +4,16 @@
 // Offline (calibration):
 //   prefix_states_kernel   (a, lse) of every calibration query over the prefix: attention
 //                          on the matrix cores, 32 queries per wave against 32-key tiles
-//                          staged in LDS and shared by the block's 4 waves (heads of one
+//                          staged in LDS and shared by the block's 8 waves (heads of one
 //                          KV group), online softmax in the log2 domain, P as bf16 hi + lo
-//   kmeans_assign_kernel   nearest centroid per query, exact fp32 squared distances
-//   cluster_part_kernel    per chunk of queries: every cluster's running sum (K-means
-//                          update) or running online-softmax state (the cluster's
-//                          attention state), rows taken in index order, in LDS
-//   cluster_reduce_kernel  the chunks combined in order: centroid means, or the cluster
-//                          states (a, lse - log n)
+//   kmeans_assign_kernel   nearest centroid per query on the matrix cores:
+//                          ||c||^2 - 2 x . c with the centroids as bf16 hi + mid + lo
+//   kmeans_part_kernel     per chunk of queries, every centroid's sum of its members as a
+//                          one-hot contraction on the matrix cores (exact products)
+//   kmeans_reduce_kernel   the chunks summed in order: the means, their planes and norms
+//   state_part_kernel      per chunk of queries, every cluster's running online-softmax
+//                          state of its members, rows taken in index order, in LDS
+//   state_reduce_kernel    the chunk states merged in order: (a, lse - log n)
 // Online (decode):
 //   lookup_merge_kernel    the largest cosine similarity among a head's centroids, and the
 //                          retrieved state merged with the query's local attention state
@@ -32,26 +34,29 @@ struct PrefixArgs {
 
 constexpr int kPT = 32;   // keys per tile
 
-// grid (ceil(G * ceil(N / 32) / 4), H_kv), 256 threads.  Wave w of block x takes item
-// i = 4x + w: query tile i / G of head g G + i % G.  S^T = K Q^T puts keys on the rows of
+constexpr int kPW = 8;    // waves per block (items sharing the block's K/V tiles)
+
+// grid (ceil(G * ceil(N / 32) / kPW), H_kv), 64 kPW threads.  Wave w of block x takes item
+// i = kPW x + w: query tile i / G of head g G + i % G.  Tiles reach LDS two ahead of use
+// (a ring of two register stages), so a tile's load latency spans two tiles of compute.  S^T = K Q^T puts keys on the rows of
 // the 32 x 32 accumulator, so each lane holds 16 keys of one query column: the row max and
 // sum need one exchange between the half-waves, and the lane's probabilities are already
 // the A operand of P V (with V's keys gathered in the same order from a dim-major tile).
 template <int D>
-__global__ __launch_bounds__(256) void prefix_states_kernel(PrefixArgs a) {
-  constexpr int KS = D / 16, NT = D / 32;
+__global__ __launch_bounds__(64 * kPW) void prefix_states_kernel(PrefixArgs a) {
+  constexpr int KS = D / 16, NT = D / 32, NTH = 64 * kPW;
   constexpr int KP = D + 8;                  // sK row pitch (bf16)
   constexpr int VP = kPT + 8;                // sV row pitch (bf16)
   constexpr int CH = kPT * D / 8;            // 16-byte chunks per tile
-  constexpr int CPT = (CH + 255) / 256;      // chunks per thread
+  constexpr int CPT = (CH + NTH - 1) / NTH;  // chunks per thread
   __shared__ __align__(16) uint16_t sK[2][kPT * KP];
   __shared__ __align__(16) uint16_t sV[2][D * VP];
-  __shared__ float sRow[4][kPT];
+  __shared__ float sRow[kPW][kPT];
 
   const int g = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int nqt = (a.N + 31) / 32;
-  const int item = blockIdx.x * 4 + wave;
+  const int item = blockIdx.x * kPW + wave;
   const bool active = item < a.G * nqt;
   const int h = g * a.G + (active ? item % a.G : 0);
   const int q0 = (active ? item / a.G : 0) * 32;
@@ -71,23 +76,23 @@ __global__ __launch_bounds__(256) void prefix_states_kernel(PrefixArgs a) {
   const int span = ((a.L - 1) * a.ts + D) * 2;
   const auto rk = make_rsrc(a.K + (size_t)g * a.hs, span);
   const auto rv = make_rsrc(a.V + (size_t)g * a.hs, span);
-  uint4 pk[CPT], pv[CPT];
-  auto fetch = [&](int k0) {
+  uint4 pk[2][CPT], pv[2][CPT];   // register ring: tile t sits in slot t % 2 until staged
+  auto fetch = [&](int slot, int k0) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = tid + 256 * u, kk = c / (D / 8), dc = c % (D / 8);
+      const int c = tid + NTH * u, kk = c / (D / 8), dc = c % (D / 8);
       const int off = c < CH ? ((k0 + kk) * a.ts + dc * 8) * 2 : span;
-      pk[u] = load16(rk, off);
-      pv[u] = load16(rv, off);
+      pk[slot][u] = load16(rk, off);
+      pv[slot][u] = load16(rv, off);
     }
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](int slot, int buf) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = tid + 256 * u, kk = c / (D / 8), dc = c % (D / 8);
+      const int c = tid + NTH * u, kk = c / (D / 8), dc = c % (D / 8);
       if (c < CH) {
-        *reinterpret_cast<uint4*>(sK[buf] + kk * KP + dc * 8) = pk[u];
-        const uint16_t* e = reinterpret_cast<const uint16_t*>(&pv[u]);
+        *reinterpret_cast<uint4*>(sK[buf] + kk * KP + dc * 8) = pk[slot][u];
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(&pv[slot][u]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) sV[buf][(dc * 8 + i) * VP + kk] = e[i];
       }
@@ -102,12 +107,17 @@ __global__ __launch_bounds__(256) void prefix_states_kernel(PrefixArgs a) {
     for (int j = 0; j < 16; ++j) acc[nt][j] = 0.f;
 
   const int ntile = (a.L + kPT - 1) / kPT;
-  fetch(0);
-  stage(0);
+  fetch(0, 0);
+  if (ntile > 1) fetch(1, kPT);
+  stage(0, 0);
   __syncthreads();
   for (int t = 0; t < ntile; ++t) {
     const int cur = t & 1;
-    if (t + 1 < ntile) fetch((t + 1) * kPT);
+    // slot t % 2 was staged before this tile: it takes tile t + 2
+    if (t + 2 < ntile) {
+      if (cur == 0) fetch(0, (t + 2) * kPT);
+      else fetch(1, (t + 2) * kPT);
+    }
     if (active) {
       f32x16_t s;
 #pragma unroll
@@ -166,7 +176,10 @@ __global__ __launch_bounds__(256) void prefix_states_kernel(PrefixArgs a) {
         }
       }
     }
-    if (t + 1 < ntile) stage(cur ^ 1);
+    if (t + 1 < ntile) {   // tile t + 1 (fetched a tile ago) into the other LDS buffer
+      if (cur == 0) stage(1, 1);
+      else stage(0, 0);
+    }
     __syncthreads();
   }
   if (!active) return;
@@ -182,74 +195,229 @@ __global__ __launch_bounds__(256) void prefix_states_kernel(PrefixArgs a) {
     a.lse[(size_t)(q0 + col) * a.H_q + h] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
 }
 
-// ------------------------------------------------------------------ K-means assignment
-// grid (ceil(N / 64), H), 256 threads: 4 lanes per query (D / 4 dims each), centroids in
-// LDS tiles of 32.  Squared distances are summed in fp32; ties keep the lower index.
+// ------------------------------------------------------------------ K-means
+// The centroids live in fp32 (C) and, for the matrix cores, as three bf16 planes
+// (hi + mid + lo, ~24 bits) beside their squared norms; score(x, c) = ||c||^2 - 2 x . c
+// orders a query's centroids as its squared distances do.
+struct KmArgs {
+  const uint16_t* X;   // [N, H, D] bf16
+  float* C;            // [H, K, D]
+  uint16_t* Cs;        // [H, 3, Kp, D] (Kp = K rounded up to 32; padding rows zero)
+  float* cn2;          // [H, Kp] (padding rows +inf)
+  int32_t* idx;        // [H, N]
+  float* part;         // [H, nchunk, Kp, D + kRowExtra]: partial sums, count
+  int N, H, K, Kp, rows;
+};
+
+constexpr int kRowExtra = 4;   // per partial row: D values, then the count (or Z), max lse, count
+
+// A 32-centroid tile in LDS (fp32, rows past K zero) -> C (optionally), the split planes and
+// the squared norms, each norm summed over the dims in order.
 template <int D>
-__global__ __launch_bounds__(256) void kmeans_assign_kernel(const uint16_t* X, const float* C, int32_t* idx,
-                                                            int N, int H, int K) {
-  constexpr int DL = D / 4;
-  __shared__ __align__(16) float sC[32][D + 4];
-  const int hh = blockIdx.y, tid = threadIdx.x;
-  const int row = blockIdx.x * 64 + tid / 4, part = tid % 4;
-  float x[DL];
-  {
-    const auto rx = make_rsrc(X + (size_t)hh * D, ((N - 1) * H * D + D) * 2);
-#pragma unroll
-    for (int c = 0; c < DL; c += 8) {
-      const uint4 v = load16(rx, (row * H * D + part * DL + c) * 2);
-      float f[8];
-      Vec16<uint16_t>::unpack(v, f);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[c + e] = f[e];
-    }
+__device__ void write_centroid_tile(const KmArgs& a, int hh, int k0, float (*sC)[D + 4], bool write_c) {
+  uint16_t* cs = a.Cs + (size_t)hh * 3 * a.Kp * D;
+  for (int i = threadIdx.x; i < 32 * D; i += blockDim.x) {
+    const int kk = i / D, c = i % D, k = k0 + kk;
+    const float x = sC[kk][c];
+    if (write_c && k < a.K) a.C[((size_t)hh * a.K + k) * D + c] = x;
+    const __bf16 h = (__bf16)x;
+    const float r1 = x - (float)h;
+    const __bf16 m = (__bf16)r1;
+    const __bf16 l = (__bf16)(r1 - (float)m);
+    __builtin_memcpy(cs + (size_t)k * D + c, &h, 2);
+    __builtin_memcpy(cs + ((size_t)a.Kp + k) * D + c, &m, 2);
+    __builtin_memcpy(cs + ((size_t)2 * a.Kp + k) * D + c, &l, 2);
   }
-  const float* Ch = C + (size_t)hh * K * D;
-  float best = INFINITY;
-  int bi = 0;
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    __syncthreads();
-    for (int i = tid; i < 32 * D / 4; i += 256) {
-      const int kk = i / (D / 4), c4 = i % (D / 4);
-      const float4 v = k0 + kk < K ? *reinterpret_cast<const float4*>(Ch + (size_t)(k0 + kk) * D + c4 * 4)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-      *reinterpret_cast<float4*>(&sC[kk][c4 * 4]) = v;
-    }
-    __syncthreads();
-    const int nk = min(32, K - k0);
-    for (int kk = 0; kk < nk; ++kk) {
-      float d2 = 0.f;
-#pragma unroll
-      for (int c = 0; c < DL; ++c) {
-        const float t = x[c] - sC[kk][part * DL + c];
-        d2 = fmaf(t, t, d2);
-      }
-      d2 = group_sum<4>(d2);
-      if (d2 < best) { best = d2; bi = k0 + kk; }
-    }
+  if (threadIdx.x < 32) {
+    const int k = k0 + threadIdx.x;
+    float s = 0.f;
+    for (int c = 0; c < D; ++c) s = fmaf(sC[threadIdx.x][c], sC[threadIdx.x][c], s);
+    a.cn2[(size_t)hh * a.Kp + k] = k < a.K ? s : INFINITY;
   }
-  if (part == 0 && row < N) idx[(size_t)hh * N + row] = bi;
 }
 
-// ------------------------------------------------------------------ cluster sums / states
-// MODE 0: every cluster's sum of its member queries (bf16 X) and its member count.
-// MODE 1: every cluster's running online-softmax state of its members' (a, lse).
+// grid (Kp / 32, H), 256 threads: the initial centroids' planes and norms.
+template <int D>
+__global__ __launch_bounds__(256) void kmeans_prep_kernel(KmArgs a) {
+  __shared__ float sC[32][D + 4];
+  const int k0 = blockIdx.x * 32, hh = blockIdx.y;
+  for (int i = threadIdx.x; i < 32 * D; i += 256) {
+    const int kk = i / D, c = i % D;
+    sC[kk][c] = k0 + kk < a.K ? a.C[((size_t)hh * a.K + k0 + kk) * D + c] : 0.f;
+  }
+  __syncthreads();
+  write_centroid_tile<D>(a, hh, k0, sC, false);
+}
+
+// grid (ceil(N / 128), H), 256 threads: wave w scores queries 128 x + 32 w .. + 31 against
+// 32-centroid tiles, S^T = C' X^T (centroids as rows), so each lane holds 16 centroids of
+// one query; the lower score wins, ties keep the lower index.
+template <int D>
+__global__ __launch_bounds__(256) void kmeans_assign_kernel(KmArgs a) {
+  constexpr int KS = D / 16;
+  const int hh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int q0 = blockIdx.x * 128 + wave * 32;
+  bf16x8_t xb[KS];
+  {
+    const auto rx = make_rsrc(a.X + (size_t)hh * D, ((a.N - 1) * a.H * D + D) * 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 v = load16(rx, ((q0 + col) * a.H * D + ks * 16 + half * 8) * 2);
+      __builtin_memcpy(&xb[ks], &v, 16);
+    }
+  }
+  const uint16_t* cs = a.Cs + (size_t)hh * 3 * a.Kp * D;
+  const float* n2 = a.cn2 + (size_t)hh * a.Kp;
+  float best = INFINITY;
+  int bi = 0;
+  for (int k0 = 0; k0 < a.Kp; k0 += 32) {
+    f32x16_t acc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const size_t off = (size_t)(k0 + col) * D + ks * 16 + half * 8;
+      const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(cs + off);
+      const bf16x8_t am = *reinterpret_cast<const bf16x8_t*>(cs + (size_t)a.Kp * D + off);
+      const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(cs + (size_t)2 * a.Kp * D + off);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, xb[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[ks], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {   // centroid of row j: k0 + 8 (j / 4) + 4 half + j % 4 (increasing)
+      const int k = k0 + 8 * (j / 4) + 4 * half + (j & 3);
+      const float sc = fmaf(-2.f, acc[j], n2[k]);
+      if (sc < best) { best = sc; bi = k; }
+    }
+  }
+  const float ob = shfl_xor32(best);
+  const int oi = __shfl_xor(bi, 32);
+  if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+  if (half == 0 && q0 + col < a.N) a.idx[(size_t)hh * a.N + q0 + col] = bi;
+}
+
+// grid (nchunk, H), 512 threads: the partial sums of every centroid over one chunk of
+// queries as one-hot contractions on the matrix cores: wave w owns centroids 32 w .. 32 w + 31
+// (the one-hot A rows, from the assignment) and all D / 32 dim tiles (B = X^T of a 64-query
+// stage in LDS).  The products are exact; the counts come from the same comparisons.
+template <int D>
+__global__ __launch_bounds__(512) void kmeans_part_kernel(KmArgs a) {
+  constexpr int NT = D / 32, RS = 64, XP = RS + 8;
+  constexpr int CPT = (RS * D / 8 + 511) / 512;   // 16-byte chunks per thread and stage
+  __shared__ __align__(16) uint16_t sXT[D * XP];
+  __shared__ int sIdx[RS];
+  const int ch = blockIdx.x, hh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int kc = wave * 32 + col;   // this lane's centroid (one-hot row)
+  const bool on = wave * 32 < a.Kp;
+  f32x16_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[nt][j] = 0.f;
+  int cnt = 0;
+  const int r0 = ch * a.rows, r1 = min(a.N, r0 + a.rows);
+  const auto rx = make_rsrc(a.X + (size_t)hh * D, ((a.N - 1) * a.H * D + D) * 2);
+  const int32_t* ix = a.idx + (size_t)hh * a.N;
+  uint4 px[CPT];
+  int pid = -1;
+  auto fetch = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + 512 * u, rr = c / (D / 8), dc = c % (D / 8);
+      const int r = s0 + rr;
+      px[u] = load16(rx, (r < r1 && c < RS * D / 8) ? (r * a.H * D + dc * 8) * 2 : 0x7ffffff0);
+    }
+    pid = (tid < RS && s0 + tid < r1) ? ix[s0 + tid] : -1;
+  };
+  fetch(r0);
+  for (int s0 = r0; s0 < r1; s0 += RS) {
+    __syncthreads();   // the previous stage is consumed
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + 512 * u, rr = c / (D / 8), dc = c % (D / 8);
+      if (c < RS * D / 8) {
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(&px[u]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) sXT[(dc * 8 + t) * XP + rr] = e[t];
+      }
+    }
+    if (tid < RS) sIdx[tid] = pid;
+    __syncthreads();
+    if (s0 + RS < r1) fetch(s0 + RS);
+    if (on) {
+#pragma unroll
+      for (int st = 0; st < RS / 16; ++st) {
+        uint16_t oh[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool hit = sIdx[16 * st + 8 * half + e] == kc;
+          oh[e] = hit ? 0x3F80 : 0;   // bf16 1.0
+          cnt += hit;
+        }
+        bf16x8_t A;
+        __builtin_memcpy(&A, oh, 16);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(sXT + (nt * 32 + col) * XP + 16 * st + 8 * half);
+          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[nt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (!on) return;
+  cnt += __shfl_xor(cnt, 32);
+  constexpr int RW = D + kRowExtra;
+  float* out = a.part + ((size_t)hh * gridDim.x + ch) * a.Kp * RW;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int k = wave * 32 + 8 * (j / 4) + 4 * half + (j & 3);
+      out[(size_t)k * RW + nt * 32 + col] = acc[nt][j];
+    }
+  if (half == 0) out[(size_t)kc * RW + D] = (float)cnt;
+}
+
+// grid (Kp / 32, H), 256 threads: chunk partials summed in chunk order; a centroid with
+// members becomes their mean, one without stays; then its planes and norm.
+template <int D>
+__global__ __launch_bounds__(256) void kmeans_reduce_kernel(KmArgs a, int nchunk) {
+  constexpr int RW = D + kRowExtra;
+  __shared__ float sC[32][D + 4];
+  const int k0 = blockIdx.x * 32, hh = blockIdx.y;
+  for (int i = threadIdx.x; i < 32 * D; i += 256) {
+    const int kk = i / D, c = i % D, k = k0 + kk;
+    float s = 0.f, n = 0.f;
+    for (int chn = 0; chn < nchunk; ++chn) {
+      const float* p = a.part + (((size_t)hh * nchunk + chn) * a.Kp + k) * RW;
+      s += p[c];
+      n += p[D];
+    }
+    float v = 0.f;
+    if (k < a.K) v = n > 0.f ? s / n : a.C[((size_t)hh * a.K + k) * D + c];
+    sC[kk][c] = v;
+  }
+  __syncthreads();
+  write_centroid_tile<D>(a, hh, k0, sC, true);
+}
+
+// ------------------------------------------------------------------ cluster states
+// Every cluster's running online-softmax state of its members' (a, lse).
 struct ClusterArgs {
-  const uint16_t* X;    // MODE 0: [N, H, D] bf16
-  const float* A;       // MODE 1: [N, H, D] f32
-  const float* lse;     // MODE 1: [N, H]
+  const float* A;       // [N, H, D] f32
+  const float* lse;     // [N, H]
   const int32_t* idx;   // [H, N]
-  float* part;          // [H, nchunk, K, D + 4]: sums (or scaled a), count (or Z), max lse, count
+  float* part;          // [H, nchunk, K, D + kRowExtra]: e^(lse - max) weighted a, Z, max lse, count
   int N, H, K, rows;    // rows per chunk
 };
 
-// grid (nchunk, H), D threads: thread = one dim; rows of the chunk in index order, each
-// folded into its cluster's LDS row (one writer per element: deterministic).  The rows'
-// operands are fetched 8 at a time ahead of their use.
-constexpr int kRowExtra = 4;   // per cluster row: D values, then count (or Z), max lse, count
-
-template <int D, int MODE>
-__global__ __launch_bounds__(D) void cluster_part_kernel(ClusterArgs a) {
+// grid (nchunk, H), D threads: thread = one dim; the chunk's rows in index order, each folded
+// into its cluster's LDS row (fixed order: deterministic).  Operands are fetched 8 rows ahead.
+template <int D>
+__global__ __launch_bounds__(D) void state_part_kernel(ClusterArgs a) {
   extern __shared__ float sAcc[];   // [K][D + kRowExtra]
   constexpr int RW = D + kRowExtra;
   const int ch = blockIdx.x, hh = blockIdx.y, tid = threadIdx.x;
@@ -264,70 +432,51 @@ __global__ __launch_bounds__(D) void cluster_part_kernel(ClusterArgs a) {
     for (int u = 0; u < 8; ++u) {
       const int r = min(b0 + u, r1 - 1);
       k[u] = ix[r];
-      if (MODE == 0) v[u] = bf16_to_f32(a.X[((size_t)r * a.H + hh) * D + tid]);
-      else {
-        v[u] = a.A[((size_t)r * a.H + hh) * D + tid];
-        ls[u] = a.lse[(size_t)r * a.H + hh];
-      }
+      v[u] = a.A[((size_t)r * a.H + hh) * D + tid];
+      ls[u] = a.lse[(size_t)r * a.H + hh];
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (b0 + u >= r1) break;
       if (k[u] < 0 || k[u] >= a.K) continue;   // an assignment outside [0, K) joins no cluster
       float* acc = sAcc + k[u] * RW;
-      if (MODE == 0) {   // each thread owns its element: no barrier between rows
-        acc[tid] += v[u];
-        if (tid == 0) acc[D] += 1.f;
-      } else {
-        // running state: acc[D + 1] = max lse, acc[D] = sum exp(lse - max), acc[dim] = sum exp(lse - max) a
-        const float mo = acc[D + 1], mn = fmaxf(mo, ls[u]);
-        const float f = __expf(mo - mn), w = __expf(ls[u] - mn);
-        acc[tid] = fmaf(acc[tid], f, w * v[u]);
-        __syncthreads();   // every dim has read the old max
-        if (tid == 0) { acc[D] = fmaf(acc[D], f, w); acc[D + 1] = mn; acc[D + 2] += 1.f; }
-        __syncthreads();
-      }
+      // acc[D + 1] = max lse, acc[D] = sum e^(lse - max), acc[dim] = sum e^(lse - max) a
+      const float mo = acc[D + 1], mn = fmaxf(mo, ls[u]);
+      const float f = __expf(mo - mn), w = __expf(ls[u] - mn);
+      acc[tid] = fmaf(acc[tid], f, w * v[u]);
+      __syncthreads();   // every dim has read the old max
+      if (tid == 0) { acc[D] = fmaf(acc[D], f, w); acc[D + 1] = mn; acc[D + 2] += 1.f; }
+      __syncthreads();
     }
   }
-  __syncthreads();   // the copy below reads elements that other threads updated
+  __syncthreads();
   float* out = a.part + ((size_t)hh * gridDim.x + ch) * a.K * RW;
   for (int i = tid; i < a.K * RW; i += D) out[i] = sAcc[i];
 }
 
-// grid (K, H), D threads: chunk partials combined in chunk order.
-// MODE 0: centroid = sum / count (a cluster without members keeps C).
-// MODE 1: a_bar = sum_c e^(m_c - m) S_c / sum_c e^(m_c - m) Z_c, lse_bar = m + log Z - log n
-//         (a cluster without members: a_bar = 0, lse_bar = -inf).
-template <int D, int MODE>
-__global__ __launch_bounds__(D) void cluster_reduce_kernel(const float* part, int nchunk, int K, float* C,
-                                                          float* a_bar, float* lse_bar) {
+// grid (K, H), D threads: chunk states merged in chunk order:
+// a_bar = sum_c e^(m_c - m) S_c / sum_c e^(m_c - m) Z_c, lse_bar = m + log Z - log n
+// (a cluster without members: a_bar = 0, lse_bar = -inf).
+template <int D>
+__global__ __launch_bounds__(D) void state_reduce_kernel(const float* part, int nchunk, int K, float* a_bar,
+                                                        float* lse_bar) {
   constexpr int RW = D + kRowExtra;
   const int k = blockIdx.x, hh = blockIdx.y, tid = threadIdx.x;
   const float* p0 = part + ((size_t)hh * nchunk * K + k) * RW;
   const size_t cs = (size_t)K * RW;   // chunk stride
-  if (MODE == 0) {
-    float s = 0.f, n = 0.f;
-    for (int c = 0; c < nchunk; ++c) {
-      s += p0[c * cs + tid];
-      n += p0[c * cs + D];
-    }
-    float* cr = C + ((size_t)hh * K + k) * D;
-    if (n > 0.f) cr[tid] = s / n;
-  } else {
-    float m = -INFINITY, z = 0.f, s = 0.f, n = 0.f;
-    for (int c = 0; c < nchunk; ++c) {
-      const float mc = p0[c * cs + D + 1];
-      if (mc == -INFINITY) continue;
-      const float mn = fmaxf(m, mc);
-      const float f = __expf(m - mn), fc = __expf(mc - mn);
-      s = fmaf(s, f, fc * p0[c * cs + tid]);
-      z = fmaf(z, f, fc * p0[c * cs + D]);
-      n += p0[c * cs + D + 2];
-      m = mn;
-    }
-    a_bar[((size_t)hh * K + k) * D + tid] = z > 0.f ? s / z : 0.f;
-    if (tid == 0) lse_bar[(size_t)hh * K + k] = z > 0.f ? m + __logf(z) - __logf(n) : -INFINITY;
+  float m = -INFINITY, z = 0.f, s = 0.f, n = 0.f;
+  for (int c = 0; c < nchunk; ++c) {
+    const float mc = p0[c * cs + D + 1];
+    if (mc == -INFINITY) continue;
+    const float mn = fmaxf(m, mc);
+    const float f = __expf(m - mn), fc = __expf(mc - mn);
+    s = fmaf(s, f, fc * p0[c * cs + tid]);
+    z = fmaf(z, f, fc * p0[c * cs + D]);
+    n += p0[c * cs + D + 2];
+    m = mn;
   }
+  a_bar[((size_t)hh * K + k) * D + tid] = z > 0.f ? s / z : 0.f;
+  if (tid == 0) lse_bar[(size_t)hh * K + k] = z > 0.f ? m + __logf(z) - __logf(n) : -INFINITY;
 }
 
 // ------------------------------------------------------------------ lookup + merge
@@ -406,38 +555,31 @@ static kvm_status check_asm_desc(const kvm_asm_desc* d) {
   KVM_REQUIRE(d->H_q % d->H_kv == 0, KVM_ERR_SHAPE, "H_q %d not a multiple of H_kv %d", d->H_q, d->H_kv);
   KVM_REQUIRE(d->dtype == KVM_BF16, KVM_ERR_DTYPE, "ASM takes bf16 queries and prefix (dtype %d)", d->dtype);
   KVM_REQUIRE(d->K >= 1 && d->K <= 256, KVM_ERR_RANGE, "K %d not in [1, 256]", d->K);
-  KVM_REQUIRE((long long)d->N * d->H_q * d->d * 2 < 0x7fffffffLL, KVM_ERR_RANGE, "N x H_q x d too large");
+  // buffer offsets are 32-bit, and past-the-end offsets (reading zeros) must stay out of range
+  KVM_REQUIRE((long long)d->N * d->H_q * d->d * 2 < 0x70000000LL, KVM_ERR_RANGE, "N x H_q x d too large");
   const long long ts = d->kv_head_major ? d->d : (long long)d->H_kv * d->d;
-  KVM_REQUIRE(((long long)d->L * ts + d->d) * 2 < 0x7fffffffLL, KVM_ERR_RANGE, "prefix of %d tokens too long", d->L);
+  KVM_REQUIRE(((long long)d->L * ts + d->d) * 2 < 0x70000000LL, KVM_ERR_RANGE, "prefix of %d tokens too long", d->L);
   return KVM_OK;
 }
 
 static int asm_chunk_rows(const kvm_asm_desc* d) { return 512; }
 static int asm_chunks(const kvm_asm_desc* d) { return (d->N + asm_chunk_rows(d) - 1) / asm_chunk_rows(d); }
 
-struct AsmWs { size_t part, total; };
+struct AsmWs { size_t cs, cn2, part, total; };
+static int asm_kp(const kvm_asm_desc* d) { return (d->K + 31) / 32 * 32; }
 static AsmWs asm_ws(const kvm_asm_desc* d) {
+  const size_t H = d->H_q, Kp = asm_kp(d);
   AsmWs w;
-  w.part = 0;
-  w.total = align_up((size_t)d->H_q * asm_chunks(d) * d->K * (d->d + kRowExtra) * sizeof(float), 256);
+  w.cs = 0;
+  w.cn2 = align_up(H * 3 * Kp * d->d * sizeof(uint16_t), 256);
+  w.part = align_up(w.cn2 + H * Kp * sizeof(float), 256);
+  w.total = align_up(w.part + H * asm_chunks(d) * Kp * (d->d + kRowExtra) * sizeof(float), 256);
   return w;
 }
 
 static kvm_status set_lds(const void* fn, int bytes) {
   if (bytes <= 65536) return KVM_OK;
   return check_hip(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes), "LDS size");
-}
-
-template <int D, int MODE>
-static kvm_status cluster_pass(const ClusterArgs& a, int nchunk, float* C, float* a_bar, float* lse_bar,
-                               hipStream_t s) {
-  const int lds = a.K * (D + kRowExtra) * (int)sizeof(float);
-  kvm_status st = set_lds(reinterpret_cast<const void*>(&cluster_part_kernel<D, MODE>), lds);
-  if (st != KVM_OK) return st;
-  hipLaunchKernelGGL((cluster_part_kernel<D, MODE>), dim3(nchunk, a.H), dim3(D), lds, s, a);
-  hipLaunchKernelGGL((cluster_reduce_kernel<D, MODE>), dim3(a.K, a.H), dim3(D), 0, s, a.part, nchunk, a.K, C, a_bar,
-                     lse_bar);
-  return check_hip(hipGetLastError(), "cluster pass launch");
 }
 
 extern "C" size_t kvm_asm_workspace_size(const kvm_asm_desc* d) {
@@ -462,11 +604,23 @@ extern "C" kvm_status kvm_asm_prefix_states(const kvm_asm_desc* d, const void* Q
   a.hs = d->kv_head_major ? d->L * d->d : d->d;
   a.sl2 = 1.4426950408889634f / sqrtf((float)d->d);
   const int items = a.G * ((d->N + 31) / 32);
-  const dim3 grid((items + 3) / 4, d->H_kv);
+  const dim3 grid((items + kPW - 1) / kPW, d->H_kv);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d->d == 128) hipLaunchKernelGGL(prefix_states_kernel<128>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(prefix_states_kernel<64>, grid, dim3(256), 0, s, a);
+  if (d->d == 128) hipLaunchKernelGGL(prefix_states_kernel<128>, grid, dim3(64 * kPW), 0, s, a);
+  else hipLaunchKernelGGL(prefix_states_kernel<64>, grid, dim3(64 * kPW), 0, s, a);
   return check_hip(hipGetLastError(), "prefix states launch");
+}
+
+template <int D>
+static void kmeans_run(const KmArgs& a, int iters, int nchunk, hipStream_t s) {
+  const dim3 tgrid(a.Kp / 32, a.H), agrid((a.N + 127) / 128, a.H), pgrid(nchunk, a.H);
+  hipLaunchKernelGGL(kmeans_prep_kernel<D>, tgrid, dim3(256), 0, s, a);
+  for (int it = 0; it <= iters; ++it) {
+    hipLaunchKernelGGL(kmeans_assign_kernel<D>, agrid, dim3(256), 0, s, a);
+    if (it == iters) break;
+    hipLaunchKernelGGL(kmeans_part_kernel<D>, pgrid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(kmeans_reduce_kernel<D>, tgrid, dim3(256), 0, s, a, nchunk);
+  }
 }
 
 extern "C" kvm_status kvm_asm_kmeans(const kvm_asm_desc* d, const void* Q, float* C, int32_t* idx, int32_t iters,
@@ -480,23 +634,19 @@ extern "C" kvm_status kvm_asm_kmeans(const kvm_asm_desc* d, const void* Q, float
   KVM_ALIGNED(ws);
   st = require_gfx950();
   if (st != KVM_OK) return st;
+  char* base = static_cast<char*>(ws);
+  KmArgs a{};
+  a.X = static_cast<const uint16_t*>(Q);
+  a.C = C;
+  a.Cs = reinterpret_cast<uint16_t*>(base + w.cs);
+  a.cn2 = reinterpret_cast<float*>(base + w.cn2);
+  a.idx = idx;
+  a.part = reinterpret_cast<float*>(base + w.part);
+  a.N = d->N; a.H = d->H_q; a.K = d->K; a.Kp = asm_kp(d); a.rows = asm_chunk_rows(d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const auto* Xb = static_cast<const uint16_t*>(Q);
-  const int H = d->H_q, N = d->N, K = d->K, nchunk = asm_chunks(d);
-  ClusterArgs ca{};
-  ca.X = Xb; ca.idx = idx; ca.part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.part);
-  ca.N = N; ca.H = H; ca.K = K; ca.rows = asm_chunk_rows(d);
-  const dim3 agrid((N + 63) / 64, H);
-  for (int it = 0; it <= iters; ++it) {
-    if (d->d == 128) hipLaunchKernelGGL(kmeans_assign_kernel<128>, agrid, dim3(256), 0, s, Xb, C, idx, N, H, K);
-    else hipLaunchKernelGGL(kmeans_assign_kernel<64>, agrid, dim3(256), 0, s, Xb, C, idx, N, H, K);
-    st = check_hip(hipGetLastError(), "kmeans assign launch");
-    if (st != KVM_OK || it == iters) return st;
-    st = d->d == 128 ? cluster_pass<128, 0>(ca, nchunk, C, nullptr, nullptr, s)
-                     : cluster_pass<64, 0>(ca, nchunk, C, nullptr, nullptr, s);
-    if (st != KVM_OK) return st;
-  }
-  return KVM_OK;
+  if (d->d == 128) kmeans_run<128>(a, iters, asm_chunks(d), s);
+  else kmeans_run<64>(a, iters, asm_chunks(d), s);
+  return check_hip(hipGetLastError(), "kmeans launch");
 }
 
 extern "C" kvm_status kvm_asm_cluster_states(const kvm_asm_desc* d, const float* a_in, const float* lse_in,
@@ -514,9 +664,23 @@ extern "C" kvm_status kvm_asm_cluster_states(const kvm_asm_desc* d, const float*
   ClusterArgs ca{};
   ca.A = a_in; ca.lse = lse_in; ca.idx = idx; ca.part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.part);
   ca.N = d->N; ca.H = d->H_q; ca.K = d->K; ca.rows = asm_chunk_rows(d);
+  const int nchunk = asm_chunks(d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return d->d == 128 ? cluster_pass<128, 1>(ca, asm_chunks(d), nullptr, a_bar, lse_bar, s)
-                     : cluster_pass<64, 1>(ca, asm_chunks(d), nullptr, a_bar, lse_bar, s);
+  const int lds = d->K * (d->d + kRowExtra) * (int)sizeof(float);
+  if (d->d == 128) {
+    st = set_lds(reinterpret_cast<const void*>(&state_part_kernel<128>), lds);
+    if (st != KVM_OK) return st;
+    hipLaunchKernelGGL(state_part_kernel<128>, dim3(nchunk, ca.H), dim3(128), lds, s, ca);
+    hipLaunchKernelGGL(state_reduce_kernel<128>, dim3(ca.K, ca.H), dim3(128), 0, s, ca.part, nchunk, ca.K, a_bar,
+                       lse_bar);
+  } else {
+    st = set_lds(reinterpret_cast<const void*>(&state_part_kernel<64>), lds);
+    if (st != KVM_OK) return st;
+    hipLaunchKernelGGL(state_part_kernel<64>, dim3(nchunk, ca.H), dim3(64), lds, s, ca);
+    hipLaunchKernelGGL(state_reduce_kernel<64>, dim3(ca.K, ca.H), dim3(64), 0, s, ca.part, nchunk, ca.K, a_bar,
+                       lse_bar);
+  }
+  return check_hip(hipGetLastError(), "cluster states launch");
 }
 
 extern "C" kvm_status kvm_asm_lookup(const kvm_asm_desc* d, int32_t b, const void* q, const float* C,

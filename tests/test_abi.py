@@ -126,5 +126,6 @@ def test_asm_validation(L):
     assert L.kvm_asm_kmeans(C.byref(desc()), *P(1, 2, 3), -1, C.c_void_p(FAKE), 1 << 30, None) == 5
     assert L.kvm_asm_kmeans(C.byref(desc()), *P(1, 2, 3), 3, C.c_void_p(FAKE), 16, None) == 6
     assert L.kvm_asm_lookup(C.byref(desc()), 0, *P(1, 2, 3, 4, 5, 6, 7, 8, 9), None) == 2
-    # partial rows [H, chunks of 512 queries, K, d + 4] f32
-    assert L.kvm_asm_workspace_size(C.byref(desc())) == 32 * 8 * 256 * 132 * 4
+    # split centroid planes [H, 3, K, d] bf16, norms [H, K] f32, partial rows
+    # [H, chunks of 512 queries, K, d + 4] f32, each 256-byte aligned
+    assert L.kvm_asm_workspace_size(C.byref(desc())) == 32 * 3 * 256 * 128 * 2 + 32 * 256 * 4 + 32 * 8 * 256 * 132 * 4
