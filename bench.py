@@ -467,8 +467,8 @@ def main():
     pbytes = prefill_bytes(cfg, keep) * layers
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                "kernel": "kvm_decode_attn_mem layer-step: decode_mfma_kernel<4> (split-K attention + memory "
-                          "read-out rows) then decode_merge_kernel<bf16,128,4>; launch_us = decode phase time / "
+                "kernel": "kvm_decode_attn_mem layer-step: decode_mfma_kernel<4,false> (split-K attention + "
+                          "memory read-out rows) then decode_merge_kernel<bf16,128,4,false>; launch_us = decode phase time / "
                           "(steps x layers), HIP events on the launch stream",
                 "bytes_per_launch": round(avg_bytes), "launch_us": round(launch_us, 3)}
     out = {
