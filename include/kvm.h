@@ -337,7 +337,10 @@ kvm_status kvm_moment_stream_evict(const kvm_mstream_desc* desc, const void* q, 
  * A prefix is replaced by a lookup memory of attention states.  Per query head h (KV head
  * g = h / G), with N calibration queries Q[i, h] and the prefix K, V (L tokens):
  *   kvm_asm_prefix_states:  a[i, h] = sum_t softmax_t(Q[i,h] . K[t,g] / sqrt d) V[t,g],
- *                           lse[i, h] = log sum_t exp(Q[i,h] . K[t,g] / sqrt d);
+ *                           lse[i, h] = log sum_t exp(Q[i,h] . K[t,g] / sqrt d); with
+ *                           accumulate != 0 the call covers one more chunk of the prefix and
+ *                           merges into the states in a, lse by the online-softmax identity
+ *                           (a long prefix encoded chunk by chunk, one chunk's K/V resident);
  *   kvm_asm_kmeans:         Lloyd's iteration on the queries of each head: `iters` rounds of
  *                           (assign to the nearest centroid by squared Euclidean distance,
  *                           ties to the lower index; centroid = mean of its members, a
@@ -374,7 +377,7 @@ typedef struct {
 
 size_t kvm_asm_workspace_size(const kvm_asm_desc* desc);
 kvm_status kvm_asm_prefix_states(const kvm_asm_desc* desc, const void* Q, const void* K, const void* V,
-                                 float* a, float* lse, void* stream);
+                                 float* a, float* lse, int32_t accumulate, void* stream);
 kvm_status kvm_asm_kmeans(const kvm_asm_desc* desc, const void* Q, float* C, int32_t* idx, int32_t iters,
                           void* ws, size_t ws_bytes, void* stream);
 kvm_status kvm_asm_cluster_states(const kvm_asm_desc* desc, const float* a, const float* lse,

@@ -89,7 +89,7 @@ SIGNATURES = {
                                       vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     "kvm_mem_query": (C.c_int, [i32, i32, i32, vp, vp, vp, vp]),
     "kvm_asm_workspace_size": (sz, [C.POINTER(AsmDesc)]),
-    "kvm_asm_prefix_states": (C.c_int, [C.POINTER(AsmDesc), vp, vp, vp, vp, vp, vp]),
+    "kvm_asm_prefix_states": (C.c_int, [C.POINTER(AsmDesc), vp, vp, vp, vp, vp, i32, vp]),
     "kvm_asm_kmeans": (C.c_int, [C.POINTER(AsmDesc), vp, vp, vp, i32, vp, sz, vp]),
     "kvm_asm_cluster_states": (C.c_int, [C.POINTER(AsmDesc), vp, vp, vp, vp, vp, vp, sz, vp]),
     "kvm_asm_lookup": (C.c_int, [C.POINTER(AsmDesc), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),

@@ -323,16 +323,20 @@ def asm_desc(Q, K_, K_centroids, kv_head_major=False):
                      kv_head_major=int(kv_head_major))
 
 
-def kvm_asm_prefix_states(Q, K_, V, kv_head_major=False, a=None, lse=None, stream=None):
+def kvm_asm_prefix_states(Q, K_, V, kv_head_major=False, a=None, lse=None, accumulate=False, stream=None):
     """Attention states (a [N, H_q, d] f32, lse [N, H_q] f32) of calibration queries
-    Q [N, H_q, d] over the prefix K, V ([L, H_kv, d], or [H_kv, L, d] if kv_head_major)."""
+    Q [N, H_q, d] over the prefix K, V ([L, H_kv, d], or [H_kv, L, d] if kv_head_major).
+    accumulate=True merges this chunk of the prefix into the states already in a, lse."""
     _contig(Q, K_, V, a, lse)
+    if accumulate and (a is None or lse is None):
+        raise ValueError("accumulate needs the states of the earlier chunks in a and lse")
     desc = asm_desc(Q, K_, 1, kv_head_major)
     if a is None:
         a = torch.empty(Q.shape, dtype=torch.float32, device=Q.device)
     if lse is None:
         lse = torch.empty(Q.shape[:2], dtype=torch.float32, device=Q.device)
-    check(lib().kvm_asm_prefix_states(C.byref(desc), _p(Q), _p(K_), _p(V), _p(a), _p(lse), _stream(stream)))
+    check(lib().kvm_asm_prefix_states(C.byref(desc), _p(Q), _p(K_), _p(V), _p(a), _p(lse), int(bool(accumulate)),
+                                      _stream(stream)))
     return a, lse
 
 

@@ -29,6 +29,7 @@ struct PrefixArgs {
   float* a;            // [N, H_q, D]
   float* lse;          // [N, H_q]
   int N, H_q, G, L, ts, hs;
+  int acc;             // merge into the states already in a, lse (a later chunk of the prefix)
   float sl2;           // logit scale * log2(e)
 };
 
@@ -52,6 +53,7 @@ __global__ __launch_bounds__(64 * kPW) void prefix_states_kernel(PrefixArgs a) {
   __shared__ __align__(16) uint16_t sK[2][kPT * KP];
   __shared__ __align__(16) uint16_t sV[2][D * VP];
   __shared__ float sRow[kPW][kPT];
+  __shared__ float sLse[kPW][kPT];
 
   const int g = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -183,16 +185,39 @@ __global__ __launch_bounds__(64 * kPW) void prefix_states_kernel(PrefixArgs a) {
     __syncthreads();
   }
   if (!active) return;
-  if (half == 0) sRow[wave][col] = 1.f / l;
+  const float lse_c = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;   // this chunk's
+  if (half == 0) {
+    sRow[wave][col] = 1.f / l;
+    sLse[wave][col] = lse_c;
+  }
+  // a later chunk merges with the state in memory by the online-softmax identity:
+  // lse = log(e^lse_old + e^lse_c), a = e^(lse_old - lse) a_old + e^(lse_c - lse) a_c
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int r = 8 * (j / 4) + 4 * half + (j & 3);
-      if (q0 + r < a.N) a.a[((size_t)(q0 + r) * a.H_q + h) * D + nt * 32 + col] = acc[nt][j] * sRow[wave][r];
+      if (q0 + r < a.N) {
+        float* ap = a.a + ((size_t)(q0 + r) * a.H_q + h) * D + nt * 32 + col;
+        float v = acc[nt][j] * sRow[wave][r];
+        if (a.acc) {
+          const float lo = a.lse[(size_t)(q0 + r) * a.H_q + h], lc = sLse[wave][r];
+          const float mx = fmaxf(lo, lc);
+          const float wo = __expf(lo - mx), wc = __expf(lc - mx);
+          v = (wo * *ap + wc * v) / (wo + wc);
+        }
+        *ap = v;
+      }
     }
-  if (half == 0 && q0 + col < a.N)
-    a.lse[(size_t)(q0 + col) * a.H_q + h] = (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f;
+  if (half == 0 && q0 + col < a.N) {
+    float* lp = a.lse + (size_t)(q0 + col) * a.H_q + h;
+    float out = lse_c;
+    if (a.acc) {
+      const float lo = *lp, mx = fmaxf(lo, lse_c);
+      out = mx + __logf(__expf(lo - mx) + __expf(lse_c - mx));
+    }
+    *lp = out;
+  }
 }
 
 // ------------------------------------------------------------------ K-means
@@ -588,7 +613,7 @@ extern "C" size_t kvm_asm_workspace_size(const kvm_asm_desc* d) {
 }
 
 extern "C" kvm_status kvm_asm_prefix_states(const kvm_asm_desc* d, const void* Q, const void* K, const void* V,
-                                            float* a_out, float* lse_out, void* stream) {
+                                            float* a_out, float* lse_out, int32_t accumulate, void* stream) {
   kvm_status st = check_asm_desc(d);
   if (st != KVM_OK) return st;
   KVM_PTR_ALIGNED(Q); KVM_PTR_ALIGNED(K); KVM_PTR_ALIGNED(V); KVM_PTR_ALIGNED(a_out); KVM_PTR_ALIGNED(lse_out);
@@ -598,7 +623,7 @@ extern "C" kvm_status kvm_asm_prefix_states(const kvm_asm_desc* d, const void* Q
   a.Q = static_cast<const uint16_t*>(Q);
   a.K = static_cast<const uint16_t*>(K);
   a.V = static_cast<const uint16_t*>(V);
-  a.a = a_out; a.lse = lse_out;
+  a.a = a_out; a.lse = lse_out; a.acc = accumulate != 0;
   a.N = d->N; a.H_q = d->H_q; a.G = d->H_q / d->H_kv; a.L = d->L;
   a.ts = d->kv_head_major ? d->d : d->H_kv * d->d;
   a.hs = d->kv_head_major ? d->L * d->d : d->d;

@@ -117,7 +117,7 @@ def test_asm_validation(L):
             setattr(d, k, v)
         return d
     P = lambda *xs: [C.c_void_p(FAKE + 1024 * i) for i in range(len(xs))]
-    f = lambda d, **kw: L.kvm_asm_prefix_states(C.byref(d), *P(1, 2, 3, 4, 5), None)
+    f = lambda d, **kw: L.kvm_asm_prefix_states(C.byref(d), *P(1, 2, 3, 4, 5), 0, None)
     assert f(desc(d=96)) == 2
     assert f(desc(H_q=36)) == 2
     assert f(desc(dtype=K.KVM_F32)) == 3

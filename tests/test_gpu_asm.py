@@ -70,6 +70,26 @@ def test_prefix_states_match_oracle(N, H_q, H_kv, d, L, hm):
     np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-4 * np.abs(rl).max())
 
 
+def test_prefix_states_in_chunks_match_oracle():
+    """A prefix encoded in three uneven chunks, each merged into the states of the earlier
+    ones, against the oracle's states over the whole prefix."""
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np
+    r = gen.rng(205, 0, 0, 0)
+    N, H_q, H_kv, d, cuts = 70, 8, 2, 128, [0, 130, 131, 500]
+    Q = _bf(r.standard_normal((N, H_q, d)))
+    K = _bf(r.standard_normal((cuts[-1], H_kv, d)))
+    V = _bf(r.standard_normal((cuts[-1], H_kv, d)))
+    a = lse = None
+    for c0, c1 in zip(cuts, cuts[1:]):
+        a, lse = api.kvm_asm_prefix_states(to_dev(Q), to_dev(np.ascontiguousarray(K[c0:c1])),
+                                           to_dev(np.ascontiguousarray(V[c0:c1])), a=a, lse=lse,
+                                           accumulate=c0 > 0)
+    ra, rl = asm.prefix_states(_f(Q), _f(K), _f(V), 1 / math.sqrt(d))
+    np.testing.assert_allclose(to_np(a), ra, rtol=2e-4, atol=2e-4 * np.abs(ra).max())
+    np.testing.assert_allclose(to_np(lse), rl, rtol=0, atol=1e-4 * np.abs(rl).max())
+
+
 KMEANS_CASES = [
     # N, H, d, K, iters, true centres
     (600, 4, 128, 16, 5, 16),
