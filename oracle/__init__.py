@@ -23,4 +23,4 @@ Parity status: every public function is pinned by tests/test_oracle_pins.py and
 tests/test_oracle_golden.py against closed forms, textbook special cases, brute
 force on tiny inputs or hand-computed fixtures; none is "parity unpinned".
 """
-from . import asm, indexmem, moment_stream, momentkv, streaming  # noqa: F401
+from . import asm, chunked, indexmem, moment_stream, momentkv, streaming  # noqa: F401

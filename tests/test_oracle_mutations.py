@@ -8,6 +8,7 @@ import pytest
 
 from oracle import indexmem as im
 from oracle import asm
+from oracle import chunked as ck
 from oracle import moment_stream as ms
 from oracle import momentkv as mk
 from tests import test_oracle_golden as gold
@@ -17,6 +18,7 @@ _orig = {name: getattr(im, name) for name in dir(im) if callable(getattr(im, nam
 _orig_mk = {name: getattr(mk, name) for name in dir(mk) if callable(getattr(mk, name))}
 _orig_ms = {name: getattr(ms, name) for name in dir(ms) if callable(getattr(ms, name))}
 _orig_asm = {name: getattr(asm, name) for name in dir(asm) if callable(getattr(asm, name))}
+_orig_ck = {name: getattr(ck, name) for name in dir(ck) if callable(getattr(ck, name))}
 
 
 def _phi_no_plus_one(x):
@@ -179,6 +181,19 @@ def _assign_farthest(X, C):
     return np.argmax(d2, axis=1), d2
 
 
+def _chunked_window_at_start(X, Q, K, V, W_kI, gamma_k, W_qI, gamma_q, W_g, B, R, lam, C, W,
+                             recent_inclusive=True, act="relu", eps=1e-6):
+    # the window read at each chunk's first W positions instead of its last W
+    Qs = np.array(Q, np.float64)
+    Xs = np.array(X, np.float64)
+    L = Xs.shape[0]
+    for s0 in range(0, L, C):
+        e = min(L, s0 + C)
+        Qs[e - W:e], Xs[e - W:e] = np.array(Q[s0:s0 + W]), np.array(X[s0:s0 + W])
+    return _orig_ck["prefill_chunked"](Xs, Qs, K, V, W_kI, gamma_k, W_qI, gamma_q, W_g, B, R, lam, C, W,
+                                       recent_inclusive, act, eps)
+
+
 MUTATIONS_STREAM = [
     ("stream alpha drops the new token", ms, "step_alpha", _stream_alpha_without_new,
      [pins.test_stream_alpha_is_textbook_softmax_and_window_of_one]),
@@ -198,6 +213,8 @@ MUTATIONS_STREAM = [
      [pins.test_asm_aggregate_is_partition_weighted_mean]),
     ("ASM lookup by dot product", asm, "lookup", _lookup_dot, [pins.test_asm_lookup_is_cosine_argmax]),
     ("K-means assigns the farthest", asm, "kmeans_assign", _assign_farthest, [pins.test_kmeans_lloyd_steps]),
+    ("chunk window at the chunk's start", ck, "prefill_chunked", _chunked_window_at_start,
+     [pins.test_chunked_single_chunk_is_one_shot_prefill, pins.test_chunked_running_max_budget_and_fold_composition]),
 ]
 
 

@@ -8,6 +8,7 @@ from hypothesis import given, settings, strategies as st
 from scipy.special import softmax as sp_softmax, logsumexp as sp_lse
 
 from oracle import asm
+from oracle import chunked as ck
 from oracle import indexmem as im
 from oracle import moment_stream as ms
 from oracle import momentkv as mk
@@ -760,3 +761,73 @@ def test_asm_lookup_is_cosine_argmax():
         C2 = C.copy()
         C2[k] *= 0.01                     # a short centroid in the same direction still wins
         assert asm.lookup(q, C2) == k
+
+
+# ============================================================================ chunked pre-eviction
+
+def _chunk_setup(L, seed, D=24, H_q=4, H_kv=2, d=8, H_I=3, d_I=6):
+    r = np.random.default_rng(seed)
+    return dict(X=r.standard_normal((L, D)), Q=r.standard_normal((L, H_q, d)),
+                K=r.standard_normal((L, H_kv, d)), V=r.standard_normal((L, H_kv, d)),
+                W_kI=r.standard_normal((d_I, D)) / math.sqrt(D), gamma_k=1 + 0.1 * r.standard_normal(d_I),
+                W_qI=r.standard_normal((H_I, d_I, d)) / math.sqrt(d), gamma_q=1 + 0.1 * r.standard_normal(d_I),
+                W_g=r.standard_normal((H_I, D)) / math.sqrt(D))
+
+
+def _chunked(c, B, R, lam, C, W):
+    return ck.prefill_chunked(c["X"], c["Q"], c["K"], c["V"], c["W_kI"], c["gamma_k"], c["W_qI"], c["gamma_q"],
+                              c["W_g"], B, R, lam, C, W)
+
+
+def test_chunked_single_chunk_is_one_shot_prefill():
+    # catches: a chunk schedule that changes the one-shot selection, a wrong window
+    L, W, B, R, lam = 40, 6, 12, 3, 0.9
+    c = _chunk_setup(L, 51)
+    out = _chunked(c, B, R, lam, L, W)
+    pre = im.prefill(c["X"], c["Q"][L - W:], c["K"], c["V"], c["W_kI"], c["gamma_k"], c["W_qI"], c["gamma_q"],
+                     c["W_g"], B, R, lam)
+    assert np.array_equal(out["pos"], pre["idx"])
+    np.testing.assert_allclose(out["I"], pre["I"][pre["idx"]], rtol=1e-13)
+    np.testing.assert_allclose(out["k_hat"], pre["k_hat"][pre["idx"]], rtol=1e-13)
+    np.testing.assert_allclose(out["M"], pre["M"], rtol=1e-12)
+    np.testing.assert_allclose(out["b"], pre["b"], rtol=1e-12)
+    np.testing.assert_array_equal(out["K"], c["K"][pre["idx"]])
+
+
+def test_chunked_running_max_budget_and_fold_composition():
+    # catches: a pooled key losing its earlier importance, the window taken at the chunk's
+    # start, a candidate from the recent window evicted, a fold in the wrong order
+    L, C, W, B, R, lam = 53, 12, 5, 10, 3, 0.8
+    c = _chunk_setup(L, 52)
+    out = _chunked(c, B, R, lam, C, W)
+    ends = [min(L, s + C) for s in range(0, L, C)]
+    kh = im.indexer_keys(c["X"], c["W_kI"], c["gamma_k"])
+    windows = []
+    for e in ends:
+        qh, gt = im.indexer_queries(c["Q"][e - W:e], c["X"][e - W:e], c["W_qI"], c["gamma_q"], c["W_g"])
+        windows.append((e, qh, gt))
+    seen, evicted_all = 0, []
+    prev = np.zeros(0, np.int64)
+    for (e, _, _), st in zip(windows, out["steps"]):
+        assert len(st["kept"]) == min(B, e) and np.all(np.diff(st["kept"]) > 0)
+        assert set(range(e - R, e)) <= set(st["kept"].tolist())
+        assert sorted(st["kept"].tolist() + st["evicted"].tolist()) == sorted(prev.tolist() + list(range(seen, e)))
+        evicted_all += st["evicted"].tolist()
+        prev, seen = st["kept"], e
+    # every pooled key's importance: the max over each later window (the one of its own
+    # chunk only from queries at or after it)
+    for t, It in zip(out["pos"], out["I"]):
+        best = -np.inf
+        for e, qh, gt in windows:
+            if e <= t:
+                continue
+            for i in range(W):
+                if e - W + i >= t:
+                    best = max(best, sum(gt[i, h] * max(qh[i, h] @ kh[t] / math.sqrt(kh.shape[1]), 0.0)
+                                         for h in range(qh.shape[1])))
+        assert It == pytest.approx(best, rel=1e-12)
+    # the per-chunk folds compose into one fold over all evictions in eviction order
+    for g in range(2):
+        Mr, br = im.memory_build(c["K"][evicted_all, g], c["V"][evicted_all, g], lam)
+        np.testing.assert_allclose(out["M"][g], Mr, rtol=1e-12)
+        np.testing.assert_allclose(out["b"][g], br, rtol=1e-12)
