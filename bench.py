@@ -316,6 +316,52 @@ def time_rows(torch, api, KL, dev):
     rows["N3_workload"] = (f"ASM, {c3.H_q}/{c3.H_kv} heads, d {c3.d}: {Nc} calibration queries per head over a "
                            f"{Lp}-token prefix (4 N L d H_q flops), K-means with {Kc} centroids x {iters} iterations "
                            f"(+ the cluster states), retrieval + merge for {c3.b} decode queries")
+    # N4: one layer's 16K prefill pre-evicted in chunks of 4096 tokens (the pool never holds
+    # more than keep + 4096 rows) against the one-shot index + evict of the same tokens
+    Cn = 4096
+    nck = c3.L // Cn
+    Xs = [rn(c3.b, Cn, c3.D) for _ in range(nck)]
+    Qs = [rn(c3.b, c3.W, c3.H_q, c3.d) for _ in range(nck)]
+    Ks = [rn(c3.b, Cn, c3.H_kv, c3.d) for _ in range(nck)]
+    Vs = [rn(c3.b, Cn, c3.H_kv, c3.d) for _ in range(nck)]
+    Wt = [rn(c3.d_I, c3.D, std=c3.D ** -0.5), torch.ones(c3.d_I, device=dev),
+          rn(c3.H_I, c3.d_I, c3.d, std=c3.d ** -0.5), torch.ones(c3.d_I, device=dev),
+          rn(c3.H_I, c3.D, std=c3.D ** -0.5)]
+    Mn = torch.zeros((c3.b, c3.H_kv, c3.d, c3.d), device=dev)
+    bn = torch.zeros((c3.b, c3.H_kv, c3.d), device=dev)
+    cap_f = api.cache_cap(c3.keep + c3.T)
+    lam3 = float(c3.lam)
+
+    def chunked():
+        P, pool = 0, dict(K=Ks[0].new_empty((c3.b, c3.H_kv, Cn, c3.d)), V=Vs[0].new_empty((c3.b, c3.H_kv, Cn, c3.d)),
+                          khat=torch.empty((c3.b, Cn, c3.d_I), device=dev), I=torch.empty((c3.b, Cn), device=dev),
+                          pos=torch.empty((c3.b, Cn), dtype=torch.int32, device=dev))
+        for c in range(nck):
+            last = c == nck - 1
+            cap_out = cap_f if last else min(P + Cn, c3.B) + Cn
+            pool, P = api.kvm_index_evict_chunk(Xs[c], Qs[c], Ks[c], Vs[c], *Wt, pool, P, c * Cn, c3.B, c3.R, lam3,
+                                                cap_out, last, Mn, bn, eps=c3.eps_rms)
+        return P
+    assert chunked() == c3.keep
+    Xf, Kf, Vf = torch.cat(Xs, 1), torch.cat(Ks, 1), torch.cat(Vs, 1)
+    If = torch.empty((c3.b, c3.L), device=dev)
+    idf = torch.empty((c3.b, c3.keep), dtype=torch.int32, device=dev)
+    smf = torch.empty((c3.b, c3.L), dtype=torch.int32, device=dev)
+    Kcf = torch.empty((c3.b, c3.H_kv, cap_f, c3.d), dtype=bf, device=dev)
+    Vcf = torch.empty((c3.b, c3.H_kv, c3.d, cap_f), dtype=bf, device=dev)
+
+    def one_shot():
+        api.kvm_index_score(Xf, Qs[-1], *Wt, I=If, eps=c3.eps_rms)
+        api.kvm_topk_select(If, c3.B, c3.R, True, idx=idf, slot_map=smf)
+        api.kvm_compact_kv(Kf, Vf, smf, idf, c3.keep, cap_f, Kc=Kcf, Vc=Vcf, M=Mn, bvec=bn, lam=lam3)
+    one_shot()
+    torch.cuda.synchronize()
+    rows["N4_chunked_index_evict_ms"] = round(timed(chunked, 5), 3)
+    rows["N4_one_shot_index_evict_ms"] = round(timed(one_shot, 5), 3)
+    rows["N4_pool_rows_peak"] = c3.keep + Cn
+    rows["N4_workload"] = (f"one layer at the 16K workload's shapes (batch {c3.b}, {c3.L} tokens, budget {c3.B}, "
+                           f"recent {c3.R}): {nck} chunks of {Cn} tokens, each scored by its own {c3.W}-query window "
+                           f"against pool + chunk, vs the one-shot index + evict holding all {c3.L} rows")
     return rows
 
 

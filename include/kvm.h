@@ -193,6 +193,54 @@ kvm_status kvm_mem_update(const kvm_mem_desc* desc, const void* K_rows, const vo
                           const int32_t* row_slot, float* M, float* bvec, void* stream);
 
 /* ------------------------------------------------------------------------------------ *
+ * N4  Chunked pre-eviction during prefill                                   [IM 2.A]
+ *
+ * The indexer predicts the entries to keep before the whole prefill is held: the prefill
+ * arrives in chunks, and after each the retained pool returns to the budget, so at most
+ * P + C <= B + C tokens are ever held.  One call is one chunk of C tokens starting at
+ * position `start`, with P tokens pooled before it:
+ *   1. the chunk's K, V (token-major [b, C, H_kv, d]) and positions join the pool after its
+ *      P rows;
+ *   2. the chunk's indexer keys; the queries of its last W positions (Qwin [b, W, H_q, d],
+ *      X rows C-W .. C-1); their scores against pool and chunk keys in position order
+ *      (each window query sees every key at or before it);
+ *   3. a pooled key's importance becomes the running max of its importance and the new
+ *      score, a chunk key's is its max over this window (kvm_index_score's form);
+ *   4. kvm_topk_select over pool and chunk (L = P + C, budget B, recent R = the chunk's
+ *      last R positions), kvm_compact_kv with KVM_FUSE_MEM (evictions folded into M, bvec
+ *      in ascending position order) and kvm_gather_rows of keys, importances, positions.
+ * The per-chunk schedule is this library's reading of the section; one chunk covering the
+ * prefill is the one-shot pre-eviction.  Pool buffers hold P + C rows per sequence (the
+ * stride of every pool array is P + C): Kp, Vp [b, H_kv, P+C, d] row-major (dtype),
+ * khat_p [b, P+C, d_I] f32, I_p [b, P+C] f32, pos_p [b, P+C] i32, rows 0 .. P-1 holding
+ * the pool; rows P .. P+C-1 are written (I_p and khat_p in full).  The next pool has
+ * stride cap_out (>= keep = kvm_chunk_keep): Kn [b, H_kv, cap_out, d]; Vn the same, or
+ * dim-major [b, H_kv, d, cap_out] when `final` (the decode caches); khat_n, I_n, pos_n
+ * (nullable) [b, cap_out, ..]; slots >= keep are not written.  M, bvec as in
+ * kvm_compact_kv.  Requires W <= C, R <= C and the index and compaction shapes.
+ * ------------------------------------------------------------------------------------ */
+typedef struct {
+  int32_t b, D, H_q, H_kv, d, H_I, d_I, W;
+  int32_t B, R, recent_inclusive;
+  int32_t P;               /* tokens pooled before this chunk                             */
+  int32_t C;               /* tokens in this chunk                                        */
+  int32_t start;           /* position of the chunk's first token                         */
+  int32_t cap_out;         /* row capacity of the next pool's buffers                     */
+  int32_t final;           /* 1: Vn in the dim-major decode layout                        */
+  int32_t dtype;
+  float lam, eps_rms;
+} kvm_chunk_desc;
+
+int32_t kvm_chunk_keep(const kvm_chunk_desc* desc);
+size_t kvm_chunk_workspace_size(const kvm_chunk_desc* desc);
+kvm_status kvm_index_evict_chunk(const kvm_chunk_desc* desc, const void* X, const void* Qwin,
+                                 const void* K, const void* V, const void* W_kI, const float* gamma_k,
+                                 const void* W_qI, const float* gamma_q, const void* W_g, void* Kp,
+                                 void* Vp, float* khat_p, float* I_p, int32_t* pos_p, void* Kn,
+                                 void* Vn, float* khat_n, float* I_n, int32_t* pos_n, float* M,
+                                 float* bvec, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
  * A7  Streaming eviction step during decode                    [IM 2.A; IM 2.B]
  *
  * Each sequence keeps a full pool of P tokens in slots 0..P-1 of the compact caches, with

@@ -59,6 +59,12 @@ class MReadDesc(C.Structure):
     _fields_ = [("b", i32), ("H_q", i32), ("H_kv", i32), ("d", i32), ("dtype", i32), ("scale", f32)]
 
 
+class ChunkDesc(C.Structure):
+    _fields_ = [("b", i32), ("D", i32), ("H_q", i32), ("H_kv", i32), ("d", i32), ("H_I", i32), ("d_I", i32),
+                ("W", i32), ("B", i32), ("R", i32), ("recent_inclusive", i32), ("P", i32), ("C", i32),
+                ("start", i32), ("cap_out", i32), ("final", i32), ("dtype", i32), ("lam", f32), ("eps_rms", f32)]
+
+
 class AsmDesc(C.Structure):
     _fields_ = [("N", i32), ("H_q", i32), ("H_kv", i32), ("d", i32), ("L", i32), ("K", i32), ("dtype", i32),
                 ("kv_head_major", i32)]
@@ -88,6 +94,9 @@ SIGNATURES = {
     "kvm_decode_attn_mem": (C.c_int, [C.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     "kvm_mem_query": (C.c_int, [i32, i32, i32, vp, vp, vp, vp]),
+    "kvm_chunk_keep": (i32, [C.POINTER(ChunkDesc)]),
+    "kvm_chunk_workspace_size": (sz, [C.POINTER(ChunkDesc)]),
+    "kvm_index_evict_chunk": (C.c_int, [C.POINTER(ChunkDesc)] + [vp] * 22 + [sz, vp]),
     "kvm_asm_workspace_size": (sz, [C.POINTER(AsmDesc)]),
     "kvm_asm_prefix_states": (C.c_int, [C.POINTER(AsmDesc), vp, vp, vp, vp, vp, i32, vp]),
     "kvm_asm_kmeans": (C.c_int, [C.POINTER(AsmDesc), vp, vp, vp, i32, vp, sz, vp]),

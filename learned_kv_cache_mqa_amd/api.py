@@ -388,3 +388,70 @@ def kvm_asm_lookup(q, C_, a_bar, lse_bar, o_loc, lse_loc, o=None, lse_out=None, 
     check(lib().kvm_asm_lookup(C.byref(desc), b, _p(q), _p(C_), _p(a_bar), _p(lse_bar), _p(o_loc), _p(lse_loc),
                                _p(o), _p(lse_out), _p(idx_out), _stream(stream)))
     return o, idx_out
+
+
+# ------------------------------------------------------------------------------- chunked prefill
+
+def kvm_index_evict_chunk(X, Qwin, K_, V, W_kI, gamma_k, W_qI, gamma_q, W_g, pool, P, start, B, R, lam, cap_out,
+                          final, M, bvec, recent_inclusive=True, eps=1e-6, stream=None, ws=None):
+    """One chunk of a chunked pre-eviction (X [b, C, D], Qwin [b, W, H_q, d], K, V [b, C, H_kv, d]).
+    pool = dict(K, V [b, H_kv, P + C, d], khat [b, P + C, d_I], I [b, P + C], pos [b, P + C]) with
+    rows 0 .. P-1 holding the pool.  Returns (next pool dict with row capacity cap_out, keep);
+    with final=True its V is dim-major [b, H_kv, d, cap_out] (the decode caches)."""
+    _contig(X, Qwin, K_, V, W_kI, gamma_k, W_qI, gamma_q, W_g, M, bvec, *pool.values())
+    b, C_, D = X.shape
+    _, W, H_q, d = Qwin.shape
+    H_kv = K_.shape[2]
+    H_I, d_I, _ = W_qI.shape
+    desc = K.ChunkDesc(b=b, D=D, H_q=H_q, H_kv=H_kv, d=d, H_I=H_I, d_I=d_I, W=W, B=B, R=R,
+                       recent_inclusive=int(bool(recent_inclusive)), P=P, C=C_, start=start, cap_out=cap_out,
+                       final=int(bool(final)), dtype=_dtype(X), lam=lam, eps_rms=eps)
+    keep = lib().kvm_chunk_keep(C.byref(desc))
+    dev = X.device
+    nxt = dict(K=torch.empty((b, H_kv, cap_out, d), dtype=K_.dtype, device=dev),
+               V=torch.empty((b, H_kv, d, cap_out) if final else (b, H_kv, cap_out, d), dtype=V.dtype, device=dev),
+               khat=torch.empty((b, cap_out, d_I), dtype=torch.float32, device=dev),
+               I=torch.empty((b, cap_out), dtype=torch.float32, device=dev),
+               pos=torch.empty((b, cap_out), dtype=torch.int32, device=dev))
+    nb = lib().kvm_chunk_workspace_size(C.byref(desc))
+    if ws is None:
+        ws = workspace(nb, dev, stream, "chunk")
+    check(lib().kvm_index_evict_chunk(C.byref(desc), _p(X), _p(Qwin), _p(K_), _p(V), _p(W_kI), _p(gamma_k),
+                                      _p(W_qI), _p(gamma_q), _p(W_g), _p(pool["K"]), _p(pool["V"]), _p(pool["khat"]),
+                                      _p(pool["I"]), _p(pool["pos"]), _p(nxt["K"]), _p(nxt["V"]), _p(nxt["khat"]),
+                                      _p(nxt["I"]), _p(nxt["pos"]), _p(M), _p(bvec), _p(ws), ws.numel(),
+                                      _stream(stream)))
+    return nxt, keep
+
+
+def index_evict_chunked(X, Q, K_, V, W_kI, gamma_k, W_qI, gamma_q, W_g, B, R, lam, C_, W, M, bvec, cap,
+                        recent_inclusive=True, eps=1e-6, stream=None):
+    """The prefill X [b, L, D], Q [b, L, H_q, d] (only each chunk's last W rows are read),
+    K, V [b, L, H_kv, d] taken in chunks of C_ tokens through kvm_index_evict_chunk.  The
+    pool buffers of every step hold exactly pool + chunk rows.  Returns the final pool
+    (K [b, H_kv, cap, d], V dim-major [b, H_kv, d, cap], khat, I, pos) and its size."""
+    b, L, D = X.shape
+    H_kv, d, d_I = K_.shape[2], K_.shape[3], W_qI.shape[1]
+    starts = list(range(0, L, C_))
+    dev = X.device
+    P, pool = 0, None
+    for i, s0 in enumerate(starts):
+        e = min(L, s0 + C_)
+        n = e - s0
+        if pool is None:
+            pool = dict(K=torch.empty((b, H_kv, n, d), dtype=K_.dtype, device=dev),
+                        V=torch.empty((b, H_kv, n, d), dtype=V.dtype, device=dev),
+                        khat=torch.empty((b, n, d_I), dtype=torch.float32, device=dev),
+                        I=torch.empty((b, n), dtype=torch.float32, device=dev),
+                        pos=torch.empty((b, n), dtype=torch.int32, device=dev))
+        last = i == len(starts) - 1
+        if last:
+            cap_out = cap
+        else:
+            keep_next = lib().kvm_chunk_keep(C.byref(K.ChunkDesc(b=b, P=P, C=n, B=B, R=R,
+                                                                 recent_inclusive=int(bool(recent_inclusive)))))
+            cap_out = keep_next + (min(L, starts[i + 1] + C_) - starts[i + 1])
+        pool, P = kvm_index_evict_chunk(X[:, s0:e].contiguous(), Q[:, e - W:e].contiguous(), K_[:, s0:e].contiguous(),
+                                        V[:, s0:e].contiguous(), W_kI, gamma_k, W_qI, gamma_q, W_g, pool, P, s0, B, R,
+                                        lam, cap_out, last, M, bvec, recent_inclusive, eps, stream)
+    return pool, P

@@ -37,6 +37,7 @@ struct IndexArgs {
   float* I;
   float* khat;   // [b, L, d_I]
   float* qt;     // [b, W, H_I, d_I]
+  size_t kh_stride;   // elements between sequences in the key projection's khat writes (L d_I)
   float* gate;   // [b, W, H_I] head gates from the key kernel (matrix-core path), or null
   int b, L, D, H_q, d, H_I, d_I, W;
   float eps;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(kKpNW * 64) __attribute__((amdgpu_waves_per_eu(KVM_
   }
   // epilogue: lane holds column (output) n = m (tile 0) and 32 + m (tile 1) for 16 rows
   const float g0 = a.gamma_k[m], g1 = a.gamma_k[32 + m];
-  float* kout = a.khat + (size_t)bb * a.L * 64;
+  float* kout = a.khat + (size_t)bb * a.kh_stride;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int row = 8 * (j / 4) + 4 * kg + (j % 4);
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(256) void keyproj_valu_kernel(IndexArgs a) {
     const float x = lane < a.d_I ? sk[tt][lane] : 0.f;
     const float ss = wave_sum(x * x);
     const float r = rsqrtf(ss / a.d_I + a.eps);
-    if (t < a.L && lane < a.d_I) a.khat[((size_t)bb * a.L + t) * a.d_I + lane] = a.gamma_k[lane] * x * r;
+    if (t < a.L && lane < a.d_I) a.khat[(size_t)bb * a.kh_stride + (size_t)t * a.d_I + lane] = a.gamma_k[lane] * x * r;
   }
 }
 
@@ -533,6 +534,49 @@ __global__ __launch_bounds__(256) void score_valu_kernel(IndexArgs a) {
   if (t < a.L) a.I[(size_t)bb * a.L + t] = best;
 }
 
+// The indexer's launches: keys (and, on the matrix-core path, the window's gate logits) over
+// a.L tokens of X into a.khat (stride a.kh_stride), the window queries, then the window's
+// scores against Ls keys from khat_s (stride Ls d_I) into I.
+static kvm_status index_launch(IndexArgs a, float* gate_ws, bool bf, const float* khat_s, int Ls, float* I,
+                               hipStream_t s) {
+  // matrix-core path: bf16, d_I = 64, H_I <= 32, d = 128, D % 64 == 0, W % 32 == 0
+  const bool mfma = bf && a.d_I == 64 && a.H_I <= 32 && a.d == 128 && a.D % 64 == 0 && a.W % 32 == 0;
+  a.gate = mfma ? gate_ws : nullptr;
+  const size_t qsmem = (size_t)((kQB * (a.H_I * a.d_I + a.H_I) + 3) & ~3) * sizeof(float) +
+                       (size_t)kQB * (a.D + a.H_q * a.d) * (bf ? 2 : 4);
+  if (mfma)
+    hipLaunchKernelGGL(keyproj_mfma_kernel, dim3((a.L + kKpTB - 1) / kKpTB, a.b), dim3(kKpNW * 64), 0, s, a);
+  else if (bf)
+    hipLaunchKernelGGL(keyproj_valu_kernel<uint16_t>, dim3((a.L + 15) / 16, a.b), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(keyproj_valu_kernel<float>, dim3((a.L + 15) / 16, a.b), dim3(256), 0, s, a);
+  const dim3 qgrid((a.W + kQB - 1) / kQB, a.b);
+  if (mfma)
+    hipLaunchKernelGGL(query_mfma_kernel, dim3(a.H_I, a.W / 32, a.b), dim3(64), 0, s, a);
+  else if (bf)
+    hipLaunchKernelGGL(query_kernel<uint16_t>, qgrid, dim3(256), qsmem, s, a);
+  else
+    hipLaunchKernelGGL(query_kernel<float>, qgrid, dim3(256), qsmem, s, a);
+  a.khat = const_cast<float*>(khat_s);
+  a.L = Ls;
+  a.I = I;
+  if (a.H_I == 32 && a.d_I == 64) {
+    static bool lds_set = false;   // a function attribute: setting it once per process suffices
+    if (!lds_set) {
+      const kvm_status st = check_hip(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_mfma_kernel),
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kScoreLds),
+                                      "score kernel LDS size");
+      if (st != KVM_OK) return st;
+      lds_set = true;
+    }
+    hipLaunchKernelGGL(score_mfma_kernel, dim3((Ls + 511) / 512, a.b), dim3(512), kScoreLds, s, a);
+  } else {
+    hipLaunchKernelGGL(score_valu_kernel, dim3((Ls + 255) / 256, a.b), dim3(256),
+                       (size_t)a.H_I * a.d_I * sizeof(float), s, a);
+  }
+  return KVM_OK;
+}
+
 struct IndexWs { size_t kh, qt, gate, total; };
 static IndexWs index_ws(const kvm_index_desc* d) {
   IndexWs w;
@@ -584,37 +628,174 @@ extern "C" kvm_status kvm_index_score(const kvm_index_desc* d, const void* X, co
   a.qt = reinterpret_cast<float*>(base + w.qt);
   a.b = d->b; a.L = d->L; a.D = d->D; a.H_q = d->H_q; a.d = d->d; a.H_I = d->H_I; a.d_I = d->d_I; a.W = d->W;
   a.eps = d->eps_rms;
+  a.kh_stride = (size_t)d->L * d->d_I;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf = d->dtype == KVM_BF16;
-  // matrix-core path: bf16, d_I = 64, H_I <= 32, d = 128, D % 64 == 0, W % 32 == 0
-  const bool mfma = bf && d->d_I == 64 && d->H_I <= 32 && d->d == 128 && d->D % 64 == 0 && d->W % 32 == 0;
-  a.gate = mfma ? reinterpret_cast<float*>(base + w.gate) : nullptr;
-  if (mfma)
-    hipLaunchKernelGGL(keyproj_mfma_kernel, dim3((d->L + kKpTB - 1) / kKpTB, d->b), dim3(kKpNW * 64), 0, s, a);
-  else if (bf)
-    hipLaunchKernelGGL(keyproj_valu_kernel<uint16_t>, dim3((d->L + 15) / 16, d->b), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(keyproj_valu_kernel<float>, dim3((d->L + 15) / 16, d->b), dim3(256), 0, s, a);
-  const dim3 qgrid((d->W + kQB - 1) / kQB, d->b);
-  if (mfma)
-    hipLaunchKernelGGL(query_mfma_kernel, dim3(d->H_I, d->W / 32, d->b), dim3(64), 0, s, a);
-  else if (bf)
-    hipLaunchKernelGGL(query_kernel<uint16_t>, qgrid, dim3(256), qsmem, s, a);
-  else
-    hipLaunchKernelGGL(query_kernel<float>, qgrid, dim3(256), qsmem, s, a);
-  if (d->H_I == 32 && d->d_I == 64) {
-    static bool lds_set = false;   // a function attribute: setting it once per process suffices
-    if (!lds_set) {
-      st = check_hip(hipFuncSetAttribute(reinterpret_cast<const void*>(&score_mfma_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kScoreLds),
-                     "score kernel LDS size");
-      if (st != KVM_OK) return st;
-      lds_set = true;
-    }
-    hipLaunchKernelGGL(score_mfma_kernel, dim3((d->L + 511) / 512, d->b), dim3(512), kScoreLds, s, a);
-  }
-  else
-    hipLaunchKernelGGL(score_valu_kernel, dim3((d->L + 255) / 256, d->b), dim3(256),
-                       (size_t)d->H_I * d->d_I * sizeof(float), s, a);
+  st = index_launch(a, reinterpret_cast<float*>(base + w.gate), d->dtype == KVM_BF16, a.khat, d->L, I, s);
+  if (st != KVM_OK) return st;
   return check_hip(hipGetLastError(), "index kernels launch");
+}
+
+// ------------------------------------------------------------------ chunked pre-eviction
+namespace kvm {
+
+// grid (ceil(C H_kv D / 8 / 256), b), 256 threads: the chunk's token-major K, V rows into the
+// pool's head-major rows P .. P + C - 1 (16 bytes per thread), and their positions.
+template <typename T>
+__global__ __launch_bounds__(256) void chunk_append_kernel(const T* K, const T* V, T* Kp, T* Vp, int32_t* pos,
+                                                           int C, int H_kv, int D, int P, int Lv, int start) {
+  constexpr int N = 16 / sizeof(T);
+  const int bb = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;          // 16-byte chunk of the batch row's C x H_kv x D
+  const int per_tok = H_kv * D / N;
+  if (i < C * per_tok) {
+    const int t = i / per_tok, r = i % per_tok, g = r / (D / N), c = (r % (D / N)) * N;
+    const size_t src = (((size_t)bb * C + t) * H_kv + g) * D + c;
+    const size_t dst = (((size_t)bb * H_kv + g) * Lv + P + t) * D + c;
+    *reinterpret_cast<uint4*>(Kp + dst) = *reinterpret_cast<const uint4*>(K + src);
+    *reinterpret_cast<uint4*>(Vp + dst) = *reinterpret_cast<const uint4*>(V + src);
+  }
+  if (i < C) pos[(size_t)bb * Lv + P + i] = start + i;
+}
+
+// grid (ceil(Lv / 256), b): a pooled key keeps the running max of its importance (NaN
+// propagates); a chunk key takes this window's.
+__global__ __launch_bounds__(256) void chunk_max_kernel(float* I, const float* Icur, int P, int Lv) {
+  const int t = blockIdx.x * 256 + threadIdx.x, bb = blockIdx.y;
+  if (t >= Lv) return;
+  const size_t i = (size_t)bb * Lv + t;
+  const float c = Icur[i];
+  if (t < P) {
+    const float o = I[i];
+    I[i] = (o != o || c != c) ? NAN : fmaxf(o, c);
+  } else {
+    I[i] = c;
+  }
+}
+
+struct ChunkWs { size_t idx, qt, gate, icur, ids, smap, comp, total; };
+static ChunkWs chunk_ws(const kvm_chunk_desc* d, size_t comp_bytes) {
+  const size_t Lv = (size_t)d->P + d->C;
+  const kvm_topk_desc td{d->b, (int32_t)Lv, d->B, d->R, d->recent_inclusive};
+  const int keep = kvm_topk_keep(&td);
+  ChunkWs w;
+  w.idx = 0;
+  w.qt = 0;
+  w.gate = align_up(w.qt + (size_t)d->b * d->W * d->H_I * d->d_I * sizeof(float), 256);
+  w.icur = align_up(w.gate + (size_t)d->b * d->W * d->H_I * sizeof(float), 256);
+  w.ids = align_up(w.icur + (size_t)d->b * Lv * sizeof(float), 256);
+  w.smap = align_up(w.ids + (size_t)d->b * (keep > 0 ? keep : 1) * sizeof(int32_t), 256);
+  w.comp = align_up(w.smap + (size_t)d->b * Lv * sizeof(int32_t), 256);
+  w.total = align_up(w.comp + comp_bytes, 256);
+  return w;
+}
+
+static kvm_compact_desc chunk_compact_desc(const kvm_chunk_desc* d, int keep) {
+  kvm_compact_desc c{};
+  c.b = d->b; c.L = d->P + d->C; c.H_kv = d->H_kv; c.d = d->d; c.cap = d->cap_out; c.keep = keep;
+  c.dtype = d->dtype; c.per_head = 0; c.kv_head_major = 1; c.flags = KVM_FUSE_MEM; c.lam = d->lam;
+  c.v_row_major = d->final ? 0 : 1;
+  return c;
+}
+
+}  // namespace kvm
+
+extern "C" int32_t kvm_chunk_keep(const kvm_chunk_desc* d) {
+  if (!d) return -1;
+  const kvm_topk_desc td{d->b, d->P + d->C, d->B, d->R, d->recent_inclusive};
+  return kvm_topk_keep(&td);
+}
+
+extern "C" size_t kvm_chunk_workspace_size(const kvm_chunk_desc* d) {
+  if (!d || d->b <= 0 || d->C <= 0 || d->P < 0 || d->W <= 0 || d->H_I <= 0 || d->d_I <= 0) return 0;
+  const int keep = kvm_chunk_keep(d);
+  if (keep < 0) return 0;
+  const kvm_compact_desc cd = chunk_compact_desc(d, keep);
+  return chunk_ws(d, kvm_compact_workspace_size(&cd)).total;
+}
+
+extern "C" kvm_status kvm_index_evict_chunk(const kvm_chunk_desc* d, const void* X, const void* Qwin, const void* K,
+                                            const void* V, const void* W_kI, const float* gamma_k, const void* W_qI,
+                                            const float* gamma_q, const void* W_g, void* Kp, void* Vp, float* khat_p,
+                                            float* I_p, int32_t* pos_p, void* Kn, void* Vn, float* khat_n,
+                                            float* I_n, int32_t* pos_n, float* M, float* bvec, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  KVM_PTR(d);
+  KVM_REQUIRE(d->b > 0 && d->D > 0 && d->H_q > 0 && d->H_kv > 0 && d->H_I > 0 && d->C > 0 && d->P >= 0,
+              KVM_ERR_SHAPE, "b, D, H_q, H_kv, H_I, C must be positive and P >= 0");
+  KVM_REQUIRE(d->d_I == 32 || d->d_I == 64, KVM_ERR_SHAPE, "d_I %d not in {32, 64}", d->d_I);
+  KVM_REQUIRE(d->d == 64 || d->d == 128, KVM_ERR_SHAPE, "head dim %d not in {64, 128}", d->d);
+  KVM_REQUIRE(d->D % 8 == 0, KVM_ERR_SHAPE, "D %% 8 != 0");
+  KVM_REQUIRE(d->H_q % d->H_kv == 0, KVM_ERR_SHAPE, "H_q %d not a multiple of H_kv %d", d->H_q, d->H_kv);
+  KVM_REQUIRE(d->dtype == KVM_F32 || d->dtype == KVM_BF16, KVM_ERR_DTYPE, "dtype %d", d->dtype);
+  KVM_REQUIRE(d->W >= 1 && d->W <= d->C && d->R >= 0 && d->R <= d->C, KVM_ERR_RANGE,
+              "the chunk (%d tokens) must hold the window %d and the recent window %d", d->C, d->W, d->R);
+  KVM_REQUIRE(d->lam >= 0.f && d->lam <= 1.f, KVM_ERR_RANGE, "lam %g outside [0, 1]", d->lam);
+  const int keep = kvm_chunk_keep(d);
+  KVM_REQUIRE(keep >= 0, KVM_ERR_RANGE, "budget %d below the recent window %d", d->B, d->R);
+  KVM_REQUIRE(d->cap_out >= keep, KVM_ERR_RANGE, "cap_out %d below the kept %d", d->cap_out, keep);
+  KVM_PTR_ALIGNED(X); KVM_PTR_ALIGNED(Qwin); KVM_PTR_ALIGNED(K); KVM_PTR_ALIGNED(V); KVM_PTR_ALIGNED(W_kI);
+  KVM_PTR_ALIGNED(gamma_k); KVM_PTR_ALIGNED(W_qI); KVM_PTR_ALIGNED(gamma_q); KVM_PTR_ALIGNED(W_g);
+  KVM_PTR_ALIGNED(Kp); KVM_PTR_ALIGNED(Vp); KVM_PTR_ALIGNED(khat_p); KVM_PTR_ALIGNED(I_p); KVM_PTR_ALIGNED(pos_p);
+  KVM_PTR_ALIGNED(Kn); KVM_PTR_ALIGNED(Vn); KVM_PTR_ALIGNED(M); KVM_PTR_ALIGNED(bvec);
+  KVM_OPT_ALIGNED(khat_n); KVM_OPT_ALIGNED(I_n); KVM_OPT_ALIGNED(pos_n);
+  const size_t esz = d->dtype == KVM_BF16 ? 2 : 4;
+  const size_t qsmem = (size_t)((kQB * (d->H_I * d->d_I + d->H_I) + 3) & ~3) * sizeof(float) +
+                       (size_t)kQB * (d->D + d->H_q * d->d) * esz;
+  KVM_REQUIRE(qsmem <= 64 * 1024, KVM_ERR_SHAPE, "D + H_q*d too large for the query kernel");
+  const kvm_compact_desc cd = chunk_compact_desc(d, keep);
+  const size_t cbytes = kvm_compact_workspace_size(&cd);
+  const ChunkWs w = chunk_ws(d, cbytes);
+  KVM_REQUIRE(ws != nullptr && ws_bytes >= w.total, KVM_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+  KVM_ALIGNED(ws);
+  kvm_status st = require_gfx950();
+  if (st != KVM_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  const int Lv = d->P + d->C;
+  // 1. the chunk's K, V and positions join the pool
+  const int nchunk16 = d->C * d->H_kv * d->d / (int)(16 / esz);
+  const dim3 agrid((std::max(nchunk16, d->C) + 255) / 256, d->b);
+  if (d->dtype == KVM_BF16)
+    hipLaunchKernelGGL(chunk_append_kernel<uint16_t>, agrid, dim3(256), 0, s, static_cast<const uint16_t*>(K),
+                       static_cast<const uint16_t*>(V), static_cast<uint16_t*>(Kp), static_cast<uint16_t*>(Vp), pos_p,
+                       d->C, d->H_kv, d->d, d->P, Lv, d->start);
+  else
+    hipLaunchKernelGGL(chunk_append_kernel<float>, agrid, dim3(256), 0, s, static_cast<const float*>(K),
+                       static_cast<const float*>(V), static_cast<float*>(Kp), static_cast<float*>(Vp), pos_p,
+                       d->C, d->H_kv, d->d, d->P, Lv, d->start);
+  // 2. the chunk's indexer keys (into pool rows P ..), its window's queries, the window's
+  //    scores against pool and chunk (in position order), the pool's running max
+  IndexArgs a{};
+  a.X = X; a.Qwin = Qwin; a.W_kI = W_kI; a.gamma_k = gamma_k; a.W_qI = W_qI; a.gamma_q = gamma_q; a.W_g = W_g;
+  a.khat = khat_p + (size_t)d->P * d->d_I;
+  a.kh_stride = (size_t)Lv * d->d_I;
+  a.qt = reinterpret_cast<float*>(base + w.qt);
+  a.b = d->b; a.L = d->C; a.D = d->D; a.H_q = d->H_q; a.d = d->d; a.H_I = d->H_I; a.d_I = d->d_I; a.W = d->W;
+  a.eps = d->eps_rms;
+  float* icur = reinterpret_cast<float*>(base + w.icur);
+  st = index_launch(a, reinterpret_cast<float*>(base + w.gate), d->dtype == KVM_BF16, khat_p, Lv, icur, s);
+  if (st != KVM_OK) return st;
+  hipLaunchKernelGGL(chunk_max_kernel, dim3((Lv + 255) / 256, d->b), dim3(256), 0, s, I_p, icur, d->P, Lv);
+  st = check_hip(hipGetLastError(), "chunk kernels launch");
+  if (st != KVM_OK) return st;
+  // 3. the budget over pool and chunk, the compaction with the memory fold, the side data
+  int32_t* ids = reinterpret_cast<int32_t*>(base + w.ids);
+  int32_t* smap = reinterpret_cast<int32_t*>(base + w.smap);
+  const kvm_topk_desc td{d->b, Lv, d->B, d->R, d->recent_inclusive};
+  st = kvm_topk_select(&td, I_p, ids, smap, stream);
+  if (st != KVM_OK) return st;
+  st = kvm_compact_kv(&cd, Kp, Vp, smap, ids, Kn, Vn, M, bvec, nullptr, nullptr, nullptr, nullptr,
+                      base + w.comp, cbytes, stream);
+  if (st != KVM_OK) return st;
+  if (khat_n) {
+    st = kvm_gather_rows(d->b, Lv, d->cap_out, d->d_I * 4, khat_p, smap, khat_n, stream);
+    if (st != KVM_OK) return st;
+  }
+  if (I_n) {
+    st = kvm_gather_rows(d->b, Lv, d->cap_out, 4, I_p, smap, I_n, stream);
+    if (st != KVM_OK) return st;
+  }
+  if (pos_n) st = kvm_gather_rows(d->b, Lv, d->cap_out, 4, pos_p, smap, pos_n, stream);
+  return st;
 }

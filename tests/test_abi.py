@@ -129,3 +129,46 @@ def test_asm_validation(L):
     # split centroid planes [H, 3, K, d] bf16, norms [H, K] f32, partial rows
     # [H, chunks of 512 queries, K, d + 4] f32, each 256-byte aligned
     assert L.kvm_asm_workspace_size(C.byref(desc())) == 32 * 3 * 256 * 128 * 2 + 32 * 256 * 4 + 32 * 8 * 256 * 132 * 4
+
+
+def _chunk(L, **kw):
+    from learned_kv_cache_mqa_amd import _lib as K
+    d = K.ChunkDesc(b=1, D=4096, H_q=32, H_kv=8, d=128, H_I=4, d_I=64, W=64, B=2048, R=64, recent_inclusive=1,
+                    P=2048, C=4096, start=4096, cap_out=2048, final=1, dtype=K.KVM_BF16, lam=0.99, eps_rms=1e-6)
+    for k, v in kw.pop("desc", {}).items():
+        setattr(d, k, v)
+    names = ["X", "Qw", "K", "V", "WkI", "gk", "WqI", "gq", "Wg", "Kp", "Vp", "khp", "Ip", "posp", "Kn", "Vn",
+             "khn", "In", "posn", "M", "b", "ws"]
+    p = {n: FAKE + 4096 * i for i, n in enumerate(names)}
+    p["wsb"] = 1 << 34
+    p.update(kw)
+    args = [None if p[n] is None else C.c_void_p(p[n]) for n in names] + [p["wsb"], None]
+    return L.kvm_index_evict_chunk(C.byref(d), *args), d
+
+
+def test_chunk_validation(L):
+    from learned_kv_cache_mqa_amd import _lib as K
+    f = lambda **kw: _chunk(L, **kw)[0]
+    assert f(desc=dict(d=96)) == 2
+    assert f(desc=dict(d_I=48)) == 2
+    assert f(desc=dict(H_q=36)) == 2                    # not a multiple of H_kv
+    assert f(desc=dict(P=-1)) == 2
+    assert f(desc=dict(dtype=5)) == 3
+    assert f(desc=dict(W=4097)) == 5                    # window longer than the chunk
+    assert f(desc=dict(R=4097)) == 5
+    assert f(desc=dict(B=32)) == 5                      # budget below the recent window
+    assert f(desc=dict(cap_out=2047)) == 5              # output pool below the kept count
+    assert f(desc=dict(lam=1.5)) == 5
+    assert f(X=None) == 1
+    assert f(khn=None, In=None, posn=None) != 1          # the new pool's side data is optional
+    assert f(Vp=FAKE + 8) == 4
+    assert f(wsb=256) == 6
+    assert b"workspace" in L.kvm_last_error()
+    _, d = _chunk(L)
+    # the pool keeps min(P + C, B) tokens; a chunk shorter than the budget keeps all
+    assert L.kvm_chunk_keep(C.byref(d)) == 2048
+    d.P, d.C = 0, 1000
+    assert L.kvm_chunk_keep(C.byref(d)) == 1000
+    d.B, d.R = 32, 64
+    assert L.kvm_chunk_keep(C.byref(d)) == -1
+    assert L.kvm_chunk_workspace_size(C.byref(d)) == 0
