@@ -560,9 +560,12 @@ struct CompactWs { size_t M, v, n, total; };
 static int compact_chunk(const kvm_compact_desc* d) {
   // 2048-token chunks: enough blocks to fill the chip at 16K tokens x 64 (sequence, KV head)
   // pairs while keeping the fp32 partial states (d*d floats per chunk) near a tenth of the
-  // K/V bytes read
-  (void)d;
-  return 2048;
+  // K/V bytes read.  Shorter inputs (a chunked prefill's pool + chunk, small batches) halve
+  // the chunk, down to 512 tokens, until every CU (256) has a block.
+  const long long pairs = (long long)d->b * d->H_kv;
+  int ch = 2048;
+  while (ch > 512 && pairs * ((d->L + ch - 1) / ch) < 256) ch /= 2;
+  return ch;
 }
 static CompactWs compact_ws(const kvm_compact_desc* d) {
   const size_t pairs = (size_t)d->b * d->H_kv;

@@ -46,6 +46,35 @@ struct IndexArgs {
 // ------------------------------------------------------------------ A1: keys, matrix cores
 constexpr int kKpPitch = 36;  // words per LDS row of a weight chunk (64 bf16 + 8 pad)
 
+// Blocks that launch at most this many leave CUs idle (256 CUs): such grids take launch
+// shapes with smaller blocks.
+constexpr int kFillBlocks = 256;
+
+// Key projection epilogue: lane holds output column m (tile 0) and 32 + m (tile 1) for 16
+// token rows; RMS-normalise each row, scale by gamma_k, store into kout (the sequence's
+// rows); window rows (the last W of L) also store their head gates sigmoid(W_g x) into
+// gout (the sequence's [W, H_I]).  Plain values only: with the argument struct passed by
+// reference the compiler keeps a private copy and spills the streaming variant.
+__device__ __forceinline__ void keyproj_epilogue(f32x16_t acc0, f32x16_t acc1, f32x16_t acc2, const float* gamma_k,
+                                                 float* kout, float* gout, int L, int W, int H_I, float eps,
+                                                 bool gate, int t0, int m, int kg) {
+  const float g0 = gamma_k[m], g1 = gamma_k[32 + m];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int row = 8 * (j / 4) + 4 * kg + (j % 4);
+    float ss = acc0[j] * acc0[j] + acc1[j] * acc1[j];
+    ss = group_sum<32>(ss);
+    const float r = rsqrtf(ss * (1.f / 64.f) + eps);
+    const int t = t0 + row;
+    if (t < L) {
+      kout[(size_t)t * 64 + m] = g0 * acc0[j] * r;
+      kout[(size_t)t * 64 + 32 + m] = g1 * acc1[j] * r;
+      if (gate && t >= L - W && m < H_I) gout[(size_t)(t - (L - W)) * H_I + m] = sigmoid_f(acc2[j]);
+    }
+  }
+}
+
+
 // Block: 128 tokens (4 waves x 32); outputs = d_I = 64 key dims (2 tiles of 32) plus, in
 // blocks that hold window positions, a third tile with the H_I (<= 32) gate logits
 // W_g[h] . x, so X is read once for both.  X streams through a ring of XS k-steps in
@@ -161,23 +190,136 @@ __global__ __launch_bounds__(kKpNW * 64) __attribute__((amdgpu_waves_per_eu(KVM_
       __syncthreads();
     }
   }
-  // epilogue: lane holds column (output) n = m (tile 0) and 32 + m (tile 1) for 16 rows
-  const float g0 = a.gamma_k[m], g1 = a.gamma_k[32 + m];
-  float* kout = a.khat + (size_t)bb * a.kh_stride;
+  keyproj_epilogue(acc0, acc1, acc2, a.gamma_k, a.khat + (size_t)bb * a.kh_stride,
+                   gate ? a.gate + (size_t)bb * a.W * a.H_I : nullptr, a.L, a.W, a.H_I, a.eps, gate, t0, m, kg);
+}
+
+// Key projection for grids that would leave CUs idle (short prefill chunks, small batches):
+// the same contraction as keyproj_mfma_kernel in blocks of NW compute waves x 32 tokens plus
+// one producer wave, so a chunk of 4096 tokens x batch 8 still gives every CU a block.
+//  - Fewer waves per CU must each keep more of X in flight: XS k-steps per wave, all loads
+//    unconditional through a buffer resource (rows past L and steps past the last read as
+//    zeros without touching memory), so the wait before each step counts only X loads.
+//  - A wave's loads complete in issue order, so the weight chunks are moved by the producer
+//    alone: a compute wave that also loaded weights would wait at every step for the X
+//    loads issued before them.  The producer keeps WD chunks in flight (a step here is short
+//    and the weights come from an L2 that the X stream keeps busy) and writes each into the
+//    idle half of the LDS double buffer one step ahead of its use.
+// Barriers: every wave, producer or not, passes one after the prologue and one per k-step.
+#ifndef KVM_KPS_NW
+#define KVM_KPS_NW 4   // compute waves per block
+#endif
+#ifndef KVM_KPS_XS
+#define KVM_KPS_XS 8   // k-steps of X in flight per compute wave
+#endif
+#ifndef KVM_KPS_WD
+#define KVM_KPS_WD 4   // weight chunks in flight in the producer
+#endif
+template <int NW, int XS, int WD>
+__global__ __launch_bounds__((NW + 1) * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void keyproj_stream_kernel(IndexArgs a) {
+  constexpr int TB = NW * 32;   // tokens per block
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool producer = wave == NW;   // wave-uniform
+  const int bb = blockIdx.y;
+  const int tb0 = blockIdx.x * TB, t0 = tb0 + (producer ? 0 : wave) * 32;
+  const int m = lane & 31, kg = lane >> 5;
+  const bool gate = tb0 + TB - 1 >= a.L - a.W && a.gate != nullptr;   // block-uniform
+  __shared__ uint32_t sW[2][96 * kKpPitch];
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(a.X) + (size_t)bb * a.L * a.D;
+  const int nk = a.D / 64;
+  // Each block starts its k loop at a different k-step (spreads the blocks' concurrent X
+  // reads over the HBM channels).
+  const int rot = (int)((blockIdx.x * 7u + blockIdx.y * 13u) % (unsigned)nk);
+  auto kofs = [&](int ks) { int k = ks + rot; return (k >= nk ? k - nk : k) * 64; };
+
+  if (producer) {
+    // weight chunk rows: 0..63 W_kI, 64..95 W_g (zeros past H_I, and outside the window's
+    // blocks); lane moves 16 bytes of rows 8 i + (lane >> 3), i = 0..11 (i < 8: W_kI)
+    const __amdgpu_buffer_rsrc_t rWk = make_rsrc(a.W_kI, 64 * a.D * 2);
+    const __amdgpu_buffer_rsrc_t rWg = make_rsrc(a.W_g, (gate ? a.H_I : 0) * a.D * 2);
+    const int wq = lane & 7, wr = lane >> 3;
+    const int nrow = gate ? 12 : 8;   // row groups of 8 in use
+    uint4 w[WD][12];
+    // chunk j lives in register set j % WD; chunks past the last step read zeros (no branch,
+    // so the wait before each store counts only the chunks issued before it)
+    auto wload = [&](int h, int ks) {
+      const bool v = ks < nk;
+      const int col = (kofs(v ? ks : 0) + wq * 8) * 2;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int row = 8 * (j / 4) + 4 * kg + (j % 4);
-    float ss = acc0[j] * acc0[j] + acc1[j] * acc1[j];
-    ss = group_sum<32>(ss);
-    const float r = rsqrtf(ss * (1.f / 64.f) + a.eps);
-    const int t = t0 + row;
-    if (t < a.L) {
-      kout[(size_t)t * 64 + m] = g0 * acc0[j] * r;
-      kout[(size_t)t * 64 + 32 + m] = g1 * acc1[j] * r;
-      if (gate && t >= a.L - a.W && m < a.H_I)
-        a.gate[((size_t)bb * a.W + (t - (a.L - a.W))) * a.H_I + m] = sigmoid_f(acc2[j]);
+      for (int i = 0; i < 12; ++i) {
+        const int off = (8 * (i & 7) + wr) * a.D * 2 + col;
+        w[h][i] = load16(i < 8 ? rWk : rWg, v ? off : 0x40000000);
+      }
+    };
+    auto wstore = [&](int h, int buf) {
+#pragma unroll
+      for (int i = 0; i < 12; ++i)
+        if (i < nrow) *reinterpret_cast<uint4*>(&sW[buf][(8 * i + wr) * kKpPitch + wq * 4]) = w[h][i];
+    };
+#pragma unroll
+    for (int h = 0; h < WD; ++h) wload(h, h);
+    wstore(0, 0);
+    wload(0, WD);   // set 0 is free again: chunk WD (step ks stores chunk ks + 1, loads ks + 1 + WD)
+    __syncthreads();
+    static_assert(WD % 2 == 0, "LDS buffer and register set of a step follow from the unrolled index");
+    for (int k0 = 0; k0 < nk; k0 += WD) {
+#pragma unroll
+      for (int u = 0; u < WD; ++u) {
+        const int ks = k0 + u;
+        if (ks >= nk) break;
+        const int hs = (u + 1) % WD;   // set of chunk ks + 1
+        if (ks + 1 < nk) wstore(hs, (u + 1) & 1);
+        wload(hs, ks + 1 + WD);
+        __syncthreads();
+      }
+    }
+    return;
+  }
+
+  // The wave's 32 X rows; MFMA j of a k-step takes dims j*16 + kg*8 .. +8 of row m.
+  const int nrows = max(0, min(32, a.L - t0));
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(X + (size_t)min(t0, a.L - 1) * a.D, nrows * a.D * 2);
+  const int xoff0 = (m * a.D + kg * 8) * 2;
+  auto xoff = [&](int ks) { return ks < nk ? xoff0 + kofs(ks) * 2 : 0x40000000; };
+  f32x16_t acc0, acc1, acc2;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) { acc0[j] = 0.f; acc1[j] = 0.f; acc2[j] = 0.f; }
+  uint4 xr[XS][4];
+#pragma unroll
+  for (int st = 0; st < XS; ++st)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[st][i] = load16(rX, xoff(st) + i * 32);
+  __syncthreads();
+  static_assert(XS % 2 == 0, "LDS buffer of a step follows from st");
+  for (int k0 = 0; k0 < nk; k0 += XS) {
+#pragma unroll
+    for (int st = 0; st < XS; ++st) {
+      const int ks = k0 + st;
+      if (ks >= nk) break;
+      const int buf = st & 1;   // == ks & 1
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8_t A, B0, B1, B2;
+        __builtin_memcpy(&A, &xr[st][j], 16);
+        const uint4 b0 = *reinterpret_cast<const uint4*>(&sW[buf][m * kKpPitch + j * 8 + kg * 4]);
+        const uint4 b1 = *reinterpret_cast<const uint4*>(&sW[buf][(32 + m) * kKpPitch + j * 8 + kg * 4]);
+        __builtin_memcpy(&B0, &b0, 16);
+        __builtin_memcpy(&B1, &b1, 16);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B1, acc1, 0, 0, 0);
+        if (gate) {
+          const uint4 b2 = *reinterpret_cast<const uint4*>(&sW[buf][(64 + m) * kKpPitch + j * 8 + kg * 4]);
+          __builtin_memcpy(&B2, &b2, 16);
+          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B2, acc2, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[st][i] = load16(rX, xoff(ks + XS) + i * 32);
+      __syncthreads();
     }
   }
+  keyproj_epilogue(acc0, acc1, acc2, a.gamma_k, a.khat + (size_t)bb * a.kh_stride,
+                   gate ? a.gate + (size_t)bb * a.W * a.H_I : nullptr, a.L, a.W, a.H_I, a.eps, gate, t0, m, kg);
 }
 
 // ------------------------------------------------------------------ A1: keys, fp32 FMA
@@ -362,11 +504,16 @@ constexpr int kSQ = 4;
 constexpr int kSQWords = 32 * kQPitch;                                   // one operand plane
 constexpr size_t kScoreLds = (size_t)2 * kSQ * 2 * kSQWords * sizeof(uint32_t);   // 73,728 B
 
+// grid (ceil(L / 512), b, parts): block z of a (key block, sequence) scores its keys against
+// the z-th of `parts` contiguous runs of the window's query groups and writes the running max
+// to a.I + z b L; the max over the parts is the importance (exact in any order).
 __global__ __launch_bounds__(512) void score_mfma_kernel(IndexArgs a) {
   // block: 512 keys (8 waves x 2 tiles x 32); H_I = 32, d_I = 64
   extern __shared__ uint32_t sQd[];   // [buf][query][hi/lo][head row * kQPitch]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bb = blockIdx.y;
+  const int ng = (a.W + kSQ - 1) / kSQ;
+  const int gb = (int)(blockIdx.z * (unsigned)ng / gridDim.z), ge = (int)((blockIdx.z + 1) * (unsigned)ng / gridDim.z);
   const int kbase = blockIdx.x * 512 + wave * 64;
   const int m = lane & 31, kg = lane >> 5;
 
@@ -416,13 +563,12 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(IndexArgs a) {
     }
   };
   float best0 = -INFINITY, best1 = -INFINITY;
-  fetch(0);
+  fetch(gb * kSQ);
   stage(0);
   __syncthreads();
-  const int ng = (a.W + kSQ - 1) / kSQ;
-  for (int gi = 0; gi < ng; ++gi) {
-    const int buf = gi & 1, g0 = gi * kSQ;
-    if (gi + 1 < ng) fetch(g0 + kSQ);
+  for (int gi = gb; gi < ge; ++gi) {
+    const int buf = (gi - gb) & 1, g0 = gi * kSQ;
+    if (gi + 1 < ge) fetch(g0 + kSQ);
     const int nq = min(kSQ, a.W - g0);
     // A operands (query heads x dims, hi and lo) of query r are read from LDS while the
     // epilogue of query r - 1 runs
@@ -496,10 +642,10 @@ __global__ __launch_bounds__(512) void score_mfma_kernel(IndexArgs a) {
         epi_tile(1, r, c1, x1, best1);
       }
     }
-    if (gi + 1 < ng) stage(buf ^ 1);
+    if (gi + 1 < ge) stage(buf ^ 1);
     __syncthreads();
   }
-  float* Ir = a.I + (size_t)bb * a.L;
+  float* Ir = a.I + ((size_t)blockIdx.z * a.b + bb) * a.L;
   if (kg == 0) {
     if (kbase + m < a.L) Ir[kbase + m] = best0;
     if (kbase + 32 + m < a.L) Ir[kbase + 32 + m] = best1;
@@ -534,18 +680,44 @@ __global__ __launch_bounds__(256) void score_valu_kernel(IndexArgs a) {
   if (t < a.L) a.I[(size_t)bb * a.L + t] = best;
 }
 
+// Window splits of the score launch: one unless the (key block, sequence) grid leaves CUs
+// idle; then enough runs of query groups to give every CU a block.
+static int score_parts(int b, int Ls, int W, int H_I, int d_I) {
+  if (H_I != 32 || d_I != 64) return 1;
+  const long long blocks = (long long)b * ((Ls + 511) / 512);
+  const int ng = (W + kSQ - 1) / kSQ;
+  if (blocks >= kFillBlocks) return 1;
+  return (int)std::min<long long>(ng, (kFillBlocks + blocks - 1) / blocks);
+}
+
+// Max over `parts` partial importances [parts][n] -> I [n] (NaN if any part is NaN).
+__global__ __launch_bounds__(256) void part_max_kernel(float* I, const float* part, int parts, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float m = part[i];
+  for (int z = 1; z < parts; ++z) {
+    const float c = part[(size_t)z * n + i];
+    m = (m != m || c != c) ? NAN : fmaxf(m, c);
+  }
+  I[i] = m;
+}
+
 // The indexer's launches: keys (and, on the matrix-core path, the window's gate logits) over
 // a.L tokens of X into a.khat (stride a.kh_stride), the window queries, then the window's
-// scores against Ls keys from khat_s (stride Ls d_I) into I.
+// scores against Ls keys from khat_s (stride Ls d_I) into I, as `parts` partial maxima
+// [parts][b][Ls] (score_parts of the same shape).
 static kvm_status index_launch(IndexArgs a, float* gate_ws, bool bf, const float* khat_s, int Ls, float* I,
-                               hipStream_t s) {
+                               int parts, hipStream_t s) {
   // matrix-core path: bf16, d_I = 64, H_I <= 32, d = 128, D % 64 == 0, W % 32 == 0
   const bool mfma = bf && a.d_I == 64 && a.H_I <= 32 && a.d == 128 && a.D % 64 == 0 && a.W % 32 == 0;
   a.gate = mfma ? gate_ws : nullptr;
   const size_t qsmem = (size_t)((kQB * (a.H_I * a.d_I + a.H_I) + 3) & ~3) * sizeof(float) +
                        (size_t)kQB * (a.D + a.H_q * a.d) * (bf ? 2 : 4);
-  if (mfma)
+  if (mfma && (long long)a.b * ((a.L + kKpTB - 1) / kKpTB) >= kFillBlocks)
     hipLaunchKernelGGL(keyproj_mfma_kernel, dim3((a.L + kKpTB - 1) / kKpTB, a.b), dim3(kKpNW * 64), 0, s, a);
+  else if (mfma)
+    hipLaunchKernelGGL((keyproj_stream_kernel<KVM_KPS_NW, KVM_KPS_XS, KVM_KPS_WD>), dim3((a.L + KVM_KPS_NW * 32 - 1) / (KVM_KPS_NW * 32), a.b),
+                       dim3((KVM_KPS_NW + 1) * 64), 0, s, a);
   else if (bf)
     hipLaunchKernelGGL(keyproj_valu_kernel<uint16_t>, dim3((a.L + 15) / 16, a.b), dim3(256), 0, s, a);
   else
@@ -569,7 +741,7 @@ static kvm_status index_launch(IndexArgs a, float* gate_ws, bool bf, const float
       if (st != KVM_OK) return st;
       lds_set = true;
     }
-    hipLaunchKernelGGL(score_mfma_kernel, dim3((Ls + 511) / 512, a.b), dim3(512), kScoreLds, s, a);
+    hipLaunchKernelGGL(score_mfma_kernel, dim3((Ls + 511) / 512, a.b, parts), dim3(512), kScoreLds, s, a);
   } else {
     hipLaunchKernelGGL(score_valu_kernel, dim3((Ls + 255) / 256, a.b), dim3(256),
                        (size_t)a.H_I * a.d_I * sizeof(float), s, a);
@@ -577,13 +749,16 @@ static kvm_status index_launch(IndexArgs a, float* gate_ws, bool bf, const float
   return KVM_OK;
 }
 
-struct IndexWs { size_t kh, qt, gate, total; };
+struct IndexWs { size_t kh, qt, gate, part, total; int parts; };
 static IndexWs index_ws(const kvm_index_desc* d) {
   IndexWs w;
+  w.parts = score_parts(d->b, d->L, d->W, d->H_I, d->d_I);
   w.kh = 0;
   w.qt = align_up(w.kh + (size_t)d->b * d->L * d->d_I * sizeof(float), 256);
   w.gate = align_up(w.qt + (size_t)d->b * d->W * d->H_I * d->d_I * sizeof(float), 256);
-  w.total = align_up(w.gate + (size_t)d->b * d->W * d->H_I * sizeof(float), 256);
+  w.part = align_up(w.gate + (size_t)d->b * d->W * d->H_I * sizeof(float), 256);
+  const size_t part_bytes = w.parts > 1 ? (size_t)w.parts * d->b * d->L * sizeof(float) : 0;
+  w.total = align_up(w.part + part_bytes, 256);
   return w;
 }
 
@@ -630,8 +805,13 @@ extern "C" kvm_status kvm_index_score(const kvm_index_desc* d, const void* X, co
   a.eps = d->eps_rms;
   a.kh_stride = (size_t)d->L * d->d_I;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = index_launch(a, reinterpret_cast<float*>(base + w.gate), d->dtype == KVM_BF16, a.khat, d->L, I, s);
+  float* part = w.parts > 1 ? reinterpret_cast<float*>(base + w.part) : I;
+  st = index_launch(a, reinterpret_cast<float*>(base + w.gate), d->dtype == KVM_BF16, a.khat, d->L, part, w.parts, s);
   if (st != KVM_OK) return st;
+  if (w.parts > 1) {
+    const size_t n = (size_t)d->b * d->L;
+    hipLaunchKernelGGL(part_max_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, I, part, w.parts, n);
+  }
   return check_hip(hipGetLastError(), "index kernels launch");
 }
 
@@ -659,11 +839,15 @@ __global__ __launch_bounds__(256) void chunk_append_kernel(const T* K, const T* 
 
 // grid (ceil(Lv / 256), b): a pooled key keeps the running max of its importance (NaN
 // propagates); a chunk key takes this window's.
-__global__ __launch_bounds__(256) void chunk_max_kernel(float* I, const float* Icur, int P, int Lv) {
+__global__ __launch_bounds__(256) void chunk_max_kernel(float* I, const float* Icur, int parts, int b, int P, int Lv) {
   const int t = blockIdx.x * 256 + threadIdx.x, bb = blockIdx.y;
   if (t >= Lv) return;
   const size_t i = (size_t)bb * Lv + t;
-  const float c = Icur[i];
+  float c = Icur[i];
+  for (int z = 1; z < parts; ++z) {
+    const float x = Icur[(size_t)z * b * Lv + i];
+    c = (c != c || x != x) ? NAN : fmaxf(c, x);
+  }
   if (t < P) {
     const float o = I[i];
     I[i] = (o != o || c != c) ? NAN : fmaxf(o, c);
@@ -682,7 +866,7 @@ static ChunkWs chunk_ws(const kvm_chunk_desc* d, size_t comp_bytes) {
   w.qt = 0;
   w.gate = align_up(w.qt + (size_t)d->b * d->W * d->H_I * d->d_I * sizeof(float), 256);
   w.icur = align_up(w.gate + (size_t)d->b * d->W * d->H_I * sizeof(float), 256);
-  w.ids = align_up(w.icur + (size_t)d->b * Lv * sizeof(float), 256);
+  w.ids = align_up(w.icur + (size_t)score_parts(d->b, (int)Lv, d->W, d->H_I, d->d_I) * d->b * Lv * sizeof(float), 256);
   w.smap = align_up(w.ids + (size_t)d->b * (keep > 0 ? keep : 1) * sizeof(int32_t), 256);
   w.comp = align_up(w.smap + (size_t)d->b * Lv * sizeof(int32_t), 256);
   w.total = align_up(w.comp + comp_bytes, 256);
@@ -774,9 +958,11 @@ extern "C" kvm_status kvm_index_evict_chunk(const kvm_chunk_desc* d, const void*
   a.b = d->b; a.L = d->C; a.D = d->D; a.H_q = d->H_q; a.d = d->d; a.H_I = d->H_I; a.d_I = d->d_I; a.W = d->W;
   a.eps = d->eps_rms;
   float* icur = reinterpret_cast<float*>(base + w.icur);
-  st = index_launch(a, reinterpret_cast<float*>(base + w.gate), d->dtype == KVM_BF16, khat_p, Lv, icur, s);
+  const int parts = score_parts(d->b, Lv, d->W, d->H_I, d->d_I);
+  st = index_launch(a, reinterpret_cast<float*>(base + w.gate), d->dtype == KVM_BF16, khat_p, Lv, icur, parts, s);
   if (st != KVM_OK) return st;
-  hipLaunchKernelGGL(chunk_max_kernel, dim3((Lv + 255) / 256, d->b), dim3(256), 0, s, I_p, icur, d->P, Lv);
+  hipLaunchKernelGGL(chunk_max_kernel, dim3((Lv + 255) / 256, d->b), dim3(256), 0, s, I_p, icur, parts, d->b, d->P,
+                     Lv);
   st = check_hip(hipGetLastError(), "chunk kernels launch");
   if (st != KVM_OK) return st;
   // 3. the budget over pool and chunk, the compaction with the memory fold, the side data
