@@ -38,8 +38,9 @@ constexpr int kPT = 32;   // keys per tile
 constexpr int kPW = 8;    // waves per block (items sharing the block's K/V tiles)
 
 // grid (ceil(G * ceil(N / 32) / kPW), H_kv), 64 kPW threads.  Wave w of block x takes item
-// i = kPW x + w: query tile i / G of head g G + i % G.  Tiles reach LDS two ahead of use
-// (a ring of two register stages), so a tile's load latency spans two tiles of compute.  S^T = K Q^T puts keys on the rows of
+// i = kPW x + w: query tile i / G of head g G + i % G.  At the top of step t the tile t + 1
+// (loaded during step t - 1) is staged into the idle LDS buffer and tile t + 2 is loaded into
+// the freed registers, so a tile's load latency spans a tile of compute.  S^T = K Q^T puts keys on the rows of
 // the 32 x 32 accumulator, so each lane holds 16 keys of one query column: the row max and
 // sum need one exchange between the half-waves, and the lane's probabilities are already
 // the A operand of P V (with V's keys gathered in the same order from a dim-major tile).
@@ -78,25 +79,30 @@ __global__ __launch_bounds__(64 * kPW) void prefix_states_kernel(PrefixArgs a) {
   const int span = ((a.L - 1) * a.ts + D) * 2;
   const auto rk = make_rsrc(a.K + (size_t)g * a.hs, span);
   const auto rv = make_rsrc(a.V + (size_t)g * a.hs, span);
-  uint4 pk[2][CPT], pv[2][CPT];   // register ring: tile t sits in slot t % 2 until staged
-  auto fetch = [&](int slot, int k0) {
+  uint4 pk[CPT], pv[CPT];   // the next tile to stage
+  // K chunk c: key c / (D / 8), dims (c % (D / 8)) * 8 .. + 8 (16 lanes read one key's row);
+  // V chunk c: key c % 32, dims (c / 32) * 8 .. + 8, so that the transposed 2-byte writes of
+  // a wave's 32 lanes land on 32 consecutive keys of one dim row (16 banks) instead of 16
+  // dim rows of one key.
+  auto fetch = [&](int k0) {   // k0 past the prefix: zeros
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = tid + NTH * u, kk = c / (D / 8), dc = c % (D / 8);
-      const int off = c < CH ? ((k0 + kk) * a.ts + dc * 8) * 2 : span;
-      pk[slot][u] = load16(rk, off);
-      pv[slot][u] = load16(rv, off);
+      const int c = tid + NTH * u;
+      const int kk = c / (D / 8), dc = c % (D / 8), vk = c % kPT, vd = c / kPT;
+      pk[u] = load16(rk, c < CH ? ((k0 + kk) * a.ts + dc * 8) * 2 : span);
+      pv[u] = load16(rv, c < CH ? ((k0 + vk) * a.ts + vd * 8) * 2 : span);
     }
   };
-  auto stage = [&](int slot, int buf) {
+  auto stage = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = tid + NTH * u, kk = c / (D / 8), dc = c % (D / 8);
+      const int c = tid + NTH * u;
+      const int kk = c / (D / 8), dc = c % (D / 8), vk = c % kPT, vd = c / kPT;
       if (c < CH) {
-        *reinterpret_cast<uint4*>(sK[buf] + kk * KP + dc * 8) = pk[slot][u];
-        const uint16_t* e = reinterpret_cast<const uint16_t*>(&pv[slot][u]);
+        *reinterpret_cast<uint4*>(sK[buf] + kk * KP + dc * 8) = pk[u];
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(&pv[u]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sV[buf][(dc * 8 + i) * VP + kk] = e[i];
+        for (int i = 0; i < 8; ++i) sV[buf][(vd * 8 + i) * VP + vk] = e[i];
       }
     }
   };
@@ -109,16 +115,17 @@ __global__ __launch_bounds__(64 * kPW) void prefix_states_kernel(PrefixArgs a) {
     for (int j = 0; j < 16; ++j) acc[nt][j] = 0.f;
 
   const int ntile = (a.L + kPT - 1) / kPT;
-  fetch(0, 0);
-  if (ntile > 1) fetch(1, kPT);
-  stage(0, 0);
+  fetch(0);
+  stage(0);
+  fetch(kPT);
   __syncthreads();
   for (int t = 0; t < ntile; ++t) {
     const int cur = t & 1;
-    // slot t % 2 was staged before this tile: it takes tile t + 2
-    if (t + 2 < ntile) {
-      if (cur == 0) fetch(0, (t + 2) * kPT);
-      else fetch(1, (t + 2) * kPT);
+    // tile t + 1 into the other buffer (free since the last barrier), tile t + 2 into the
+    // registers
+    if (t + 1 < ntile) {
+      stage(cur ^ 1);
+      if (t + 2 < ntile) fetch((t + 2) * kPT);
     }
     if (active) {
       f32x16_t s;
@@ -138,8 +145,12 @@ __global__ __launch_bounds__(64 * kPW) void prefix_states_kernel(PrefixArgs a) {
         mx = fmaxf(mx, p[j]);
       }
       mx = fmaxf(mx, shfl_xor32(mx));
-      const float mn = fmaxf(m, mx);   // finite: every tile holds a key of the prefix
-      const float corr = __builtin_amdgcn_exp2f(m - mn);
+      // Lazy rescaling: the running max m moves only when a tile's max exceeds it by more
+      // than 8 (log2 units), so every probability stays below 2^8 and the accumulators are
+      // rescaled on few tiles; a / l is the same for any such m.  The first tile always moves
+      // it (m = -inf; every tile holds a key of the prefix, so mx is finite).
+      const float mn = mx > m + 8.f ? mx : m;
+      const float corr = __builtin_amdgcn_exp2f(m - mn);   // 1 unless m moved
       float ls = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -149,15 +160,16 @@ __global__ __launch_bounds__(64 * kPW) void prefix_states_kernel(PrefixArgs a) {
       ls += shfl_xor32(ls);
       l = fmaf(l, corr, ls);
       m = mn;
-      // the output rows are queries: their factors come through LDS (in order within a wave)
-      if (half == 0) sRow[wave][col] = corr;
-      float cr[16];
+      if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {   // wave-uniform
+        // the output rows are queries: their factors come through LDS (in order within a wave)
+        if (half == 0) sRow[wave][col] = corr;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) cr[j] = sRow[wave][8 * (j / 4) + 4 * half + (j & 3)];
+        for (int j = 0; j < 16; ++j) {
+          const float cr = sRow[wave][8 * (j / 4) + 4 * half + (j & 3)];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[nt][j] *= cr[j];
+          for (int nt = 0; nt < NT; ++nt) acc[nt][j] *= cr;
+        }
+      }
       // P V: K-step kk takes this lane's p[8 kk .. 8 kk + 7], keys 16 kk + 8 (i / 4) + 4 half + i % 4
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -177,10 +189,6 @@ __global__ __launch_bounds__(64 * kPW) void prefix_states_kernel(PrefixArgs a) {
           acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pm, B, acc[nt], 0, 0, 0);
         }
       }
-    }
-    if (t + 1 < ntile) {   // tile t + 1 (fetched a tile ago) into the other LDS buffer
-      if (cur == 0) stage(1, 1);
-      else stage(0, 0);
     }
     __syncthreads();
   }
