@@ -193,6 +193,22 @@ kvm_status kvm_mem_update(const kvm_mem_desc* desc, const void* K_rows, const vo
                           const int32_t* row_slot, float* M, float* bvec, void* stream);
 
 /* ------------------------------------------------------------------------------------ *
+ * V2  Moment update from evicted rows                                       [MKV part 1]
+ *
+ * The moment sums of each (sequence, KV head) take every evicted row, in the given order:
+ *   n_e += r,  s_k += sum_i k_i,  s_v += sum_i v_i,  S += sum_i v_i k_i^T.
+ * Rows as in kvm_mem_update (desc->lam is not used): K_rows, V_rows [b, r, H_kv, d]
+ * (dtype), or, with row_slot != NULL, r = 1 and the row comes from the caches at slot
+ * row_slot[b] (a sequence whose row_slot is outside [0, cap) is left as is).  n_e [b, H_kv]
+ * i32, s_k, s_v [b, H_kv, d] f32, S [b, H_kv, d, d] f32 (rows index v, columns index k),
+ * updated in place.  The same update runs fused into kvm_compact_kv (KVM_FUSE_MOMENTS)
+ * when the evicted rows are those of a selection.
+ * ------------------------------------------------------------------------------------ */
+kvm_status kvm_moment_update(const kvm_mem_desc* desc, const void* K_rows, const void* V_rows,
+                             const int32_t* row_slot, int32_t* n_e, float* s_k, float* s_v, float* S,
+                             void* stream);
+
+/* ------------------------------------------------------------------------------------ *
  * N4  Chunked pre-eviction during prefill                                   [IM 2.A]
  *
  * The indexer predicts the entries to keep before the whole prefill is held: the prefill

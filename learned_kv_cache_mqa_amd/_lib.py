@@ -90,6 +90,7 @@ SIGNATURES = {
                                  vp, sz, vp]),
     "kvm_gather_rows": (C.c_int, [i32, i32, i32, i32, vp, vp, vp, vp]),
     "kvm_mem_update": (C.c_int, [C.POINTER(MemDesc), vp, vp, vp, vp, vp, vp]),
+    "kvm_moment_update": (C.c_int, [C.POINTER(MemDesc), vp, vp, vp, vp, vp, vp, vp, vp]),
     "kvm_decode_workspace_size": (sz, [C.POINTER(DecodeDesc)]),
     "kvm_decode_attn_mem": (C.c_int, [C.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),

@@ -186,6 +186,22 @@ def kvm_mem_update(K_rows, V_rows, M, bvec, lam, row_slot=None, stream=None):
     return M, bvec
 
 
+def kvm_moment_update(K_rows, V_rows, moments, row_slot=None, stream=None):
+    """Fold evicted rows into the moment sums moments = dict(n_e [b,H_kv] i32, s_k, s_v
+    [b,H_kv,d], S [b,H_kv,d,d] f32); rows as in kvm_mem_update."""
+    _contig(K_rows, V_rows, row_slot, *moments.values())
+    if row_slot is not None:
+        b, H_kv, cap, d = K_rows.shape
+        r = 1
+    else:
+        b, r, H_kv, d = K_rows.shape
+        cap = 0
+    desc = K.MemDesc(b=b, H_kv=H_kv, d=d, r=r, cap=cap, dtype=_dtype(K_rows), lam=1.0)
+    check(lib().kvm_moment_update(C.byref(desc), _p(K_rows), _p(V_rows), _p(row_slot), _p(moments["n_e"]),
+                                  _p(moments["s_k"]), _p(moments["s_v"]), _p(moments["S"]), _stream(stream)))
+    return moments
+
+
 # ------------------------------------------------------------------------------- indexer
 
 def kvm_index_score(X, Qwin, W_kI, gamma_k, W_qI, gamma_q, W_g, I=None, khat=None, eps=1e-6, stream=None,

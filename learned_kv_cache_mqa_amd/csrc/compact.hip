@@ -487,17 +487,22 @@ __global__ void gather_rows_kernel(int rows, int L, int cap, int words, const ui
 }
 
 // ------------------------------------------------------------------ rank-r update
+// Latent memory (MOM = false): M <- lam^r M + sum_i lam^(r-i) v_i phi(k_i)^T, bvec likewise.
+// Moments (MOM = true): S += sum_i v_i k_i^T, s_k (in bvec) += sum k, s_v += sum v,
+// n_e += r.  Rows are summed in order i = 1 .. r (deterministic).
 struct MemArgs {
   const void* K;
   const void* V;
   const int32_t* row_slot;
-  float* M;
-  float* bvec;
+  float* M;      // M, or S
+  float* bvec;   // bvec, or s_k
   int H_kv, r, cap;
   float lam;
+  float* s_v;    // moments only
+  int32_t* n_e;  // moments only
 };
 
-template <typename T, int D>
+template <typename T, int D, bool MOM>
 __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
   // grid (D*D/1024, H_kv, b): each thread updates 4 consecutive elements of one row
   const int g = blockIdx.y, bb = blockIdx.z;
@@ -529,10 +534,10 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
           v = load_scalar<T>(vp + dd);
         }
         const int e = a.r - 1 - ri;  // lam^(r-i) with i = ri + 1
-        w = a.lam == 0.f ? (e == 0 ? 1.f : 0.f) : __powf(a.lam, (float)e);
+        w = MOM ? 1.f : a.lam == 0.f ? (e == 0 ? 1.f : 0.f) : __powf(a.lam, (float)e);
       }
       sv[ii][dd] = v;
-      su[ii][dd] = w * phi_f(k);
+      su[ii][dd] = MOM ? w * k : w * phi_f(k);
     }
     __syncthreads();
     for (int ii = 0; ii < nr; ++ii) {
@@ -542,9 +547,11 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
     }
     if (blockIdx.x == 0 && threadIdx.x < D)
       for (int ii = 0; ii < nr; ++ii) bacc += su[ii][threadIdx.x];
+    if (MOM && blockIdx.x == 0 && threadIdx.x >= D && threadIdx.x < 2 * D)
+      for (int ii = 0; ii < nr; ++ii) bacc += sv[ii][threadIdx.x - D];
     __syncthreads();
   }
-  const float dec = a.lam == 0.f ? (a.r == 0 ? 1.f : 0.f) : __powf(a.lam, (float)a.r);
+  const float dec = MOM ? 1.f : a.lam == 0.f ? (a.r == 0 ? 1.f : 0.f) : __powf(a.lam, (float)a.r);
   float* Mp = a.M + pair * D * D + (size_t)row * D + col;
   float4 m = *reinterpret_cast<float4*>(Mp);
   m.x = fmaf(dec, m.x, acc[0]); m.y = fmaf(dec, m.y, acc[1]);
@@ -554,6 +561,8 @@ __global__ __launch_bounds__(256) void mem_update_kernel(MemArgs a) {
     float* bp = a.bvec + pair * D + threadIdx.x;
     *bp = fmaf(dec, *bp, bacc);
   }
+  if (MOM && blockIdx.x == 0 && threadIdx.x >= D && threadIdx.x < 2 * D) a.s_v[pair * D + threadIdx.x - D] += bacc;
+  if (MOM && blockIdx.x == 1 && threadIdx.x == 0) a.n_e[pair] += a.r;   // grid.x = D D / 1024 >= 4
 }
 
 struct CompactWs { size_t M, v, n, total; };
@@ -696,6 +705,21 @@ extern "C" kvm_status kvm_gather_rows(int32_t rows, int32_t L, int32_t cap, int3
   return check_hip(hipGetLastError(), "gather_rows launch");
 }
 
+namespace kvm {
+template <bool MOM>
+static kvm_status mem_update_launch(const kvm_mem_desc* d, const MemArgs& a, hipStream_t s) {
+  const dim3 grid(d->d * d->d / 1024, d->H_kv, d->b);
+  if (d->dtype == KVM_BF16) {
+    if (d->d == 128) hipLaunchKernelGGL((mem_update_kernel<uint16_t, 128, MOM>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((mem_update_kernel<uint16_t, 64, MOM>), grid, dim3(256), 0, s, a);
+  } else {
+    if (d->d == 128) hipLaunchKernelGGL((mem_update_kernel<float, 128, MOM>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((mem_update_kernel<float, 64, MOM>), grid, dim3(256), 0, s, a);
+  }
+  return check_hip(hipGetLastError(), MOM ? "moment_update launch" : "mem_update launch");
+}
+}  // namespace kvm
+
 extern "C" kvm_status kvm_mem_update(const kvm_mem_desc* d, const void* K_rows, const void* V_rows,
                                      const int32_t* row_slot, float* M, float* bvec, void* stream) {
   KVM_PTR(d);
@@ -709,15 +733,24 @@ extern "C" kvm_status kvm_mem_update(const kvm_mem_desc* d, const void* K_rows, 
   kvm_status st = require_gfx950();
   if (st != KVM_OK) return st;
   if (d->r == 0) return KVM_OK;
-  MemArgs a{K_rows, V_rows, row_slot, M, bvec, d->H_kv, d->r, d->cap, d->lam};
-  dim3 grid(d->d * d->d / 1024, d->H_kv, d->b);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d->dtype == KVM_BF16) {
-    if (d->d == 128) hipLaunchKernelGGL((mem_update_kernel<uint16_t, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((mem_update_kernel<uint16_t, 64>), grid, dim3(256), 0, s, a);
-  } else {
-    if (d->d == 128) hipLaunchKernelGGL((mem_update_kernel<float, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((mem_update_kernel<float, 64>), grid, dim3(256), 0, s, a);
-  }
-  return check_hip(hipGetLastError(), "mem_update launch");
+  MemArgs a{K_rows, V_rows, row_slot, M, bvec, d->H_kv, d->r, d->cap, d->lam, nullptr, nullptr};
+  return mem_update_launch<false>(d, a, static_cast<hipStream_t>(stream));
+}
+
+extern "C" kvm_status kvm_moment_update(const kvm_mem_desc* d, const void* K_rows, const void* V_rows,
+                                        const int32_t* row_slot, int32_t* n_e, float* s_k, float* s_v, float* S,
+                                        void* stream) {
+  KVM_PTR(d);
+  KVM_REQUIRE(d->b > 0 && d->H_kv > 0 && d->r >= 0, KVM_ERR_SHAPE, "b, H_kv positive and r >= 0 required");
+  KVM_REQUIRE(d->d == 64 || d->d == 128, KVM_ERR_SHAPE, "head dim %d not in {64, 128}", d->d);
+  KVM_REQUIRE(d->dtype == KVM_F32 || d->dtype == KVM_BF16, KVM_ERR_DTYPE, "dtype %d", d->dtype);
+  KVM_REQUIRE(row_slot == nullptr || (d->r == 1 && d->cap > 0), KVM_ERR_RANGE, "row_slot needs r == 1 and cap > 0");
+  KVM_PTR_ALIGNED(K_rows); KVM_PTR_ALIGNED(V_rows);
+  KVM_PTR_ALIGNED(n_e); KVM_PTR_ALIGNED(s_k); KVM_PTR_ALIGNED(s_v); KVM_PTR_ALIGNED(S);
+  KVM_OPT_ALIGNED(row_slot);
+  kvm_status st = require_gfx950();
+  if (st != KVM_OK) return st;
+  if (d->r == 0) return KVM_OK;
+  MemArgs a{K_rows, V_rows, row_slot, S, s_k, d->H_kv, d->r, d->cap, 1.f, s_v, n_e};
+  return mem_update_launch<true>(d, a, static_cast<hipStream_t>(stream));
 }

@@ -172,3 +172,21 @@ def test_chunk_validation(L):
     d.B, d.R = 32, 64
     assert L.kvm_chunk_keep(C.byref(d)) == -1
     assert L.kvm_chunk_workspace_size(C.byref(d)) == 0
+
+
+def test_moment_update_validation(L):
+    from learned_kv_cache_mqa_amd import _lib as K
+    P = lambda *xs: [C.c_void_p(FAKE + 4096 * i) for i in range(len(xs))]
+
+    def f(row_slot=None, **kw):
+        d = K.MemDesc(b=2, H_kv=8, d=128, r=4, cap=0, dtype=K.KVM_BF16, lam=1.0)
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return L.kvm_moment_update(C.byref(d), *P(1, 2), row_slot, *P(3, 4, 5, 6), None)
+    assert f(d=96) == 2
+    assert f(b=0) == 2
+    assert f(dtype=9) == 3
+    assert f(row_slot=C.c_void_p(FAKE)) == 5          # a cache slot needs r == 1 and cap > 0
+    assert f(row_slot=C.c_void_p(FAKE + 4), r=1, cap=8) == 4
+    d = K.MemDesc(b=2, H_kv=8, d=128, r=4, cap=0, dtype=K.KVM_BF16, lam=1.0)
+    assert L.kvm_moment_update(C.byref(d), *P(1, 2), None, None, *P(4, 5, 6), None) == 1

@@ -202,6 +202,55 @@ def test_gather_rows_and_rank_r_update():
             assert normwise(to_np(bv)[i, g], rb) < 1e-5
 
 
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+def test_moment_update_matches_oracle(dt, d):
+    """kvm_moment_update: rows folded into the moment sums of each (sequence, KV head)
+    [MKV part 1], against the oracle's running sums; then one row per sequence taken from
+    the caches at a device-given slot (a slot outside the cache leaves the sums as they are)."""
+    import torch
+    from oracle import momentkv as mk
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, normwise
+    b, rr, H = 3, 45, 2
+    rg = gen.rng(96, d, 0, 0)
+    Kr = gen.to_storage(rg.standard_normal((b, rr, H, d)), dt)
+    Vr = gen.to_storage(rg.standard_normal((b, rr, H, d)), dt)
+    n0 = rg.integers(0, 50, (b, H)).astype(np.int32)
+    sk0 = rg.standard_normal((b, H, d)).astype(np.float32)
+    sv0 = rg.standard_normal((b, H, d)).astype(np.float32)
+    S0 = rg.standard_normal((b, H, d, d)).astype(np.float32)
+    mom = dict(n_e=to_dev(n0.copy()), s_k=to_dev(sk0.copy()), s_v=to_dev(sv0.copy()), S=to_dev(S0.copy()))
+    api.kvm_moment_update(to_dev(Kr), to_dev(Vr), mom)
+    torch.cuda.synchronize()
+    Kd, Vd = gen.from_storage(Kr, dt), gen.from_storage(Vr, dt)
+    got = {k: to_np(v) for k, v in mom.items()}
+    for i in range(b):
+        for g in range(H):
+            ref = mk.add(dict(n=int(n0[i, g]), sk=sk0[i, g], sv=sv0[i, g], S=S0[i, g]), Kd[i, :, g], Vd[i, :, g])
+            assert got["n_e"][i, g] == ref["n"]
+            assert normwise(got["s_k"][i, g], ref["sk"]) < 1e-6
+            assert normwise(got["s_v"][i, g], ref["sv"]) < 1e-6
+            assert normwise(got["S"][i, g], ref["S"]) < 1e-6
+    cap = 24
+    Kc = gen.to_storage(rg.standard_normal((b, H, cap, d)), dt)
+    Vc = gen.to_storage(rg.standard_normal((b, H, cap, d)), dt)
+    slots = np.array([5, cap, 17], np.int32)   # the second sequence: no row
+    mom = dict(n_e=to_dev(n0.copy()), s_k=to_dev(sk0.copy()), s_v=to_dev(sv0.copy()), S=to_dev(S0.copy()))
+    api.kvm_moment_update(to_dev(Kc), to_dev(np.ascontiguousarray(Vc.transpose(0, 1, 3, 2))), mom,
+                          row_slot=to_dev(slots))
+    torch.cuda.synchronize()
+    Kd, Vd = gen.from_storage(Kc, dt), gen.from_storage(Vc, dt)
+    got = {k: to_np(v) for k, v in mom.items()}
+    for i in range(b):
+        for g in range(H):
+            m0 = dict(n=int(n0[i, g]), sk=sk0[i, g], sv=sv0[i, g], S=S0[i, g])
+            ref = m0 if slots[i] >= cap else mk.add(m0, Kd[i, g, slots[i]][None], Vd[i, g, slots[i]][None])
+            assert got["n_e"][i, g] == ref["n"]
+            assert normwise(got["s_k"][i, g], ref["sk"]) < 1e-6
+            assert normwise(got["s_v"][i, g], ref["sv"]) < 1e-6
+            assert normwise(got["S"][i, g], ref["S"]) < 1e-6
+
 def _compact_sweep(n=24):
     """Seeded random shapes for the top-k + compaction + memory build chain."""
     r = np.random.default_rng(777)
