@@ -56,13 +56,14 @@ __global__ __launch_bounds__(64 * kPW) void prefix_states_kernel(PrefixArgs a) {
   __shared__ float sRow[kPW][kPT];
   __shared__ float sLse[kPW][kPT];
 
-  const int g = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index through readfirstlane keeps the head and the query buffer resource scalar
+  const int g = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int nqt = (a.N + 31) / 32;
   const int item = blockIdx.x * kPW + wave;
   const bool active = item < a.G * nqt;
-  const int h = g * a.G + (active ? item % a.G : 0);
-  const int q0 = (active ? item / a.G : 0) * 32;
+  const int h = __builtin_amdgcn_readfirstlane(g * a.G + (active ? item % a.G : 0));
+  const int q0 = __builtin_amdgcn_readfirstlane((active ? item / a.G : 0) * 32);
 
   // B operand: lane (query q0 + col) holds dims ks * 16 + half * 8 .. + 8 (zeros past N)
   bf16x8_t qb[KS];

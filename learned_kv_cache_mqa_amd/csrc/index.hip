@@ -218,7 +218,9 @@ __global__ __launch_bounds__(kKpNW * 64) __attribute__((amdgpu_waves_per_eu(KVM_
 template <int NW, int XS, int WD>
 __global__ __launch_bounds__((NW + 1) * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void keyproj_stream_kernel(IndexArgs a) {
   constexpr int TB = NW * 32;   // tokens per block
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index through readfirstlane: the producer branch and the X buffer resource stay
+  // scalar (a per-lane value there turns every load into a loop over the distinct lane values)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool producer = wave == NW;   // wave-uniform
   const int bb = blockIdx.y;
   const int tb0 = blockIdx.x * TB, t0 = tb0 + (producer ? 0 : wave) * 32;
@@ -277,8 +279,9 @@ __global__ __launch_bounds__((NW + 1) * 64) __attribute__((amdgpu_waves_per_eu(2
   }
 
   // The wave's 32 X rows; MFMA j of a k-step takes dims j*16 + kg*8 .. +8 of row m.
-  const int nrows = max(0, min(32, a.L - t0));
-  const __amdgpu_buffer_rsrc_t rX = make_rsrc(X + (size_t)min(t0, a.L - 1) * a.D, nrows * a.D * 2);
+  const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(32, a.L - t0)));
+  const int xrow0 = __builtin_amdgcn_readfirstlane(min(t0, a.L - 1));
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(X + (size_t)xrow0 * a.D, nrows * a.D * 2);
   const int xoff0 = (m * a.D + kg * 8) * 2;
   auto xoff = [&](int ks) { return ks < nk ? xoff0 + kofs(ks) * 2 : 0x40000000; };
   f32x16_t acc0, acc1, acc2;

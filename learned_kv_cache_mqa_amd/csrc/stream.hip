@@ -56,7 +56,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void stream_proj_kernel(StreamArgs a, int long_blocks) {
   constexpr int N = Vec16<T>::N;
   constexpr int TB = (int)sizeof(T);
-  const int bb = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index through readfirstlane: buffer resources built from it stay scalar (a
+  // per-lane value there turns every load into a loop over the distinct lane values)
+  const int bb = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   float* out = a.proj + (size_t)bb * a.NP;
   if ((int)blockIdx.x < long_blocks) {
     const int row = blockIdx.x * 4 + wave;
