@@ -190,3 +190,40 @@ def test_moment_update_validation(L):
     assert f(row_slot=C.c_void_p(FAKE + 4), r=1, cap=8) == 4
     d = K.MemDesc(b=2, H_kv=8, d=128, r=4, cap=0, dtype=K.KVM_BF16, lam=1.0)
     assert L.kvm_moment_update(C.byref(d), *P(1, 2), None, None, *P(4, 5, 6), None) == 1
+
+
+def test_header_is_c99_and_links(tmp_path):
+    """include/kvm.h compiles as strict C99, and a C program linked against libkvmem.so calls
+    the library directly: version, status strings, and argument validation that fails before
+    any HIP call (so no GPU is needed)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    libdir = os.path.join(ROOT, "learned_kv_cache_mqa_amd")
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "kvm.h"
+int main(void) {
+  kvm_topk_desc d = {1, 64, 80, 0, 1};      /* budget above L: keep everything */
+  kvm_topk_desc bad = {1, 64, 8, 16, 1};    /* budget below the recent window */
+  int st;
+  printf("abi %d\n", (int)kvm_abi_version());
+  printf("keep %d bad %d\n", (int)kvm_topk_keep(&d), (int)kvm_topk_keep(&bad));
+  st = (int)kvm_topk_select(NULL, NULL, NULL, NULL, NULL);
+  printf("null %d %s\n", st, kvm_status_string(st));
+  return 0;
+}
+''')
+    exe = tmp_path / "abi"
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+           str(src), "-L", libdir, "-lkvmem", f"-Wl,-rpath,{libdir}", "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    lines = r.stdout.split("\n")
+    assert lines[0] == "abi 2"
+    assert lines[1] == "keep 64 bad -1"
+    assert lines[2].startswith("null 1 ")
