@@ -716,7 +716,9 @@ static kvm_status index_launch(IndexArgs a, float* gate_ws, bool bf, const float
   a.gate = mfma ? gate_ws : nullptr;
   const size_t qsmem = (size_t)((kQB * (a.H_I * a.d_I + a.H_I) + 3) & ~3) * sizeof(float) +
                        (size_t)kQB * (a.D + a.H_q * a.d) * (bf ? 2 : 4);
-  if (mfma && (long long)a.b * ((a.L + kKpTB - 1) / kKpTB) >= kFillBlocks)
+  // the streaming variant addresses its buffers with 32-bit byte offsets (64 D 2 bytes of
+  // weights): wide models fall back to the wide-grid kernel
+  if (mfma && ((long long)a.b * ((a.L + kKpTB - 1) / kKpTB) >= kFillBlocks || a.D > (1 << 20)))
     hipLaunchKernelGGL(keyproj_mfma_kernel, dim3((a.L + kKpTB - 1) / kKpTB, a.b), dim3(kKpNW * 64), 0, s, a);
   else if (mfma)
     hipLaunchKernelGGL((keyproj_stream_kernel<KVM_KPS_NW, KVM_KPS_XS, KVM_KPS_WD>), dim3((a.L + KVM_KPS_NW * 32 - 1) / (KVM_KPS_NW * 32), a.b),
