@@ -196,7 +196,8 @@ __global__ __launch_bounds__(kKpNW * 64) __attribute__((amdgpu_waves_per_eu(KVM_
 
 // Key projection for grids that would leave CUs idle (short prefill chunks, small batches):
 // the same contraction as keyproj_mfma_kernel in blocks of NW compute waves x 32 tokens plus
-// one producer wave, so a chunk of 4096 tokens x batch 8 still gives every CU a block.
+// one producer wave, so a chunk of 4096 tokens x batch 8 still gives every CU a block (NW = 4;
+// NW = 2 where even that grid is short, e.g. batch 1: 74 instead of 82 us at 16K tokens).
 //  - Fewer waves per CU must each keep more of X in flight: XS k-steps per wave, all loads
 //    unconditional through a buffer resource (rows past L and steps past the last read as
 //    zeros without touching memory), so the wait before each step counts only X loads.
@@ -720,9 +721,11 @@ static kvm_status index_launch(IndexArgs a, float* gate_ws, bool bf, const float
   // weights): wide models fall back to the wide-grid kernel
   if (mfma && ((long long)a.b * ((a.L + kKpTB - 1) / kKpTB) >= kFillBlocks || a.D > (1 << 20)))
     hipLaunchKernelGGL(keyproj_mfma_kernel, dim3((a.L + kKpTB - 1) / kKpTB, a.b), dim3(kKpNW * 64), 0, s, a);
-  else if (mfma)
+  else if (mfma && (long long)a.b * ((a.L + KVM_KPS_NW * 32 - 1) / (KVM_KPS_NW * 32)) >= kFillBlocks)
     hipLaunchKernelGGL((keyproj_stream_kernel<KVM_KPS_NW, KVM_KPS_XS, KVM_KPS_WD>), dim3((a.L + KVM_KPS_NW * 32 - 1) / (KVM_KPS_NW * 32), a.b),
                        dim3((KVM_KPS_NW + 1) * 64), 0, s, a);
+  else if (mfma)   // smaller still (batch 1): 2 compute waves per block, twice the blocks
+    hipLaunchKernelGGL((keyproj_stream_kernel<2, KVM_KPS_XS, KVM_KPS_WD>), dim3((a.L + 63) / 64, a.b), dim3(3 * 64), 0, s, a);
   else if (bf)
     hipLaunchKernelGGL(keyproj_valu_kernel<uint16_t>, dim3((a.L + 15) / 16, a.b), dim3(256), 0, s, a);
   else
