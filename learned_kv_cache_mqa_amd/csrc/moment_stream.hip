@@ -12,7 +12,7 @@
 // moments mode).
 //
 // Two kernels:
-//   mstream_score_kernel   per (64-slot chunk, KV head, sequence): the residual norms on
+//   mstream_score_kernel   per (64- or 128-slot chunk, KV head, sequence): the residual norms on
 //                          the matrix cores (S' = S~/(n_e sqrt d) as three bf16 terms
 //                          against the exact bf16 keys) and the group's logits q_h . k_j
 //                          (one more product, queries as rows); advances next_pos
@@ -42,14 +42,15 @@ struct MsArgs {
   float scale;            // 1 / sqrt(D)
 };
 
-constexpr int kMsKeys = 64;    // pool slots per score block
-
-// grid (ceil(P / kMsKeys), H_kv, b), D / 32 waves.  Wave w owns residual dims 32w .. 32w+31
+// grid (ceil(P / KEYS), H_kv, b), D / 32 waves; KEYS pool slots per block (64, or 128 where
+// that still gives every CU a block: each block splits its KV head's S once, so larger blocks
+// repeat that less; 1024-slot pools at batch 4: 36.3 -> 31.7 us per step).  Wave w owns residual dims 32w .. 32w+31
 // of 32 slots per tile: C[i][slot] = sum_c S'[i][c] k[slot][c], r = v - v_bar - C, and
 // ||r||^2 sums the lane's rows, the two half-waves and the waves.  Wave 0 also forms
 // C[h][slot] = q_h . k[slot] with the group's queries as the rows of a fourth product.
-template <int D>
+template <int D, int KEYS>
 __global__ __launch_bounds__(D * 2) void mstream_score_kernel(MsArgs a) {
+  constexpr int kMsKeys = KEYS;
   constexpr int KS = D / 16;
   constexpr int NW = D / 32;
   const int c = blockIdx.x, g = blockIdx.y, bb = blockIdx.z;
@@ -388,12 +389,16 @@ extern "C" kvm_status kvm_moment_stream_evict(const kvm_mstream_desc* d, const v
   a.H_q = d->H_q; a.H_kv = d->H_kv; a.G = d->H_q / d->H_kv; a.P = d->P; a.cap = d->cap; a.R = d->R;
   a.scale = 1.f / sqrtf((float)d->d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 sgrid((d->P + kMsKeys - 1) / kMsKeys, d->H_kv, d->b), cgrid(d->H_kv, d->b);
+  const bool wide = (long long)((d->P + 127) / 128) * d->H_kv * d->b >= 256;
+  const int keys = wide ? 128 : 64;
+  const dim3 sgrid((d->P + keys - 1) / keys, d->H_kv, d->b), cgrid(d->H_kv, d->b);
   if (d->d == 128) {
-    hipLaunchKernelGGL(mstream_score_kernel<128>, sgrid, dim3(256), 0, s, a);
+    if (wide) hipLaunchKernelGGL((mstream_score_kernel<128, 128>), sgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((mstream_score_kernel<128, 64>), sgrid, dim3(256), 0, s, a);
     launch_commit<128>(a.G, cgrid, s, a);
   } else {
-    hipLaunchKernelGGL(mstream_score_kernel<64>, sgrid, dim3(128), 0, s, a);
+    if (wide) hipLaunchKernelGGL((mstream_score_kernel<64, 128>), sgrid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((mstream_score_kernel<64, 64>), sgrid, dim3(128), 0, s, a);
     launch_commit<64>(a.G, cgrid, s, a);
   }
   return check_hip(hipGetLastError(), "moment stream launch");

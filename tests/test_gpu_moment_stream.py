@@ -69,6 +69,9 @@ CASES = [
     ("d64_ragged_empty_moments", 2, 8, 2, 64, 200, 5, 16, 0),
     ("G1", 1, 8, 8, 128, 300, 0, 12, 50),
     ("G8_ragged_by_one", 1, 16, 2, 64, 129, 0, 16, 20),
+    # grids of >= 256 blocks of 128 slots: the score kernel's wide-block variant
+    ("pool1024_batch4_wide_blocks", 4, 32, 8, 128, 1024, 16, 5, 2000),
+    ("d64_wide_blocks_ragged", 4, 8, 8, 64, 1000, 0, 4, 300),
 ]
 
 
