@@ -133,7 +133,7 @@ def time_rows(torch, api, KL, dev):
     """Timings of the rows outside the IndexMem decode path, at their workloads' shapes
     (device-drawn inputs): the streaming step (131072-token workload, pool 1024 + 64) and
     MomentKV's alpha, one score round and the read-out (Qwen3-4B shape, 32K tokens, batch 4)."""
-    from synth import CONFIGS
+    from synth import WORKLOADS
     bf = torch.bfloat16
     g = torch.Generator(device=dev)
     g.manual_seed(4_000_000)
@@ -141,7 +141,7 @@ def time_rows(torch, api, KL, dev):
     ev = lambda: torch.cuda.Event(enable_timing=True)
     rows = {}
     # A7: streaming eviction step + decode over the pool
-    c4 = CONFIGS[4]
+    c4 = WORKLOADS["llama8b_layer_131k_stream"]
     P = c4.B + c4.R
     cap = api.cache_cap(P)
     Kc = rn(1, c4.H_kv, cap, c4.d)
@@ -184,7 +184,7 @@ def time_rows(torch, api, KL, dev):
     rows["A7_stream_step_us"] = round(e0.elapsed_time(e1) * 1e3 / steps, 2)
     rows["A7_workload"] = f"1 sequence, pool {P} slots, D {c4.D}, stream step + decode per token, HIP graph"
     # V1 / V3: MomentKV at the Qwen3-4B shape
-    c5 = CONFIGS[5]
+    c5 = WORKLOADS["qwen3_4b_momentkv_32k"]
     Q = rn(c5.b, c5.W, c5.H_q, c5.d)
     K5, V5 = rn(c5.b, c5.L, c5.H_kv, c5.d), rn(c5.b, c5.L, c5.H_kv, c5.d)
     mom = dict(n_e=torch.full((c5.b, c5.H_kv), 1000, dtype=torch.int32, device=dev),
@@ -245,7 +245,7 @@ def time_rows(torch, api, KL, dev):
                            "eviction step + decode with the NC mix per token, HIP graph")
     # N2: the read-out projection: decode layer-steps at the 16K workload's shapes, with and
     # without the projected query (kvm_mem_query + decode reading q_mem)
-    c3 = CONFIGS[3]
+    c3 = WORKLOADS["llama8b_32L_16k_b8"]
     cap3, n3 = api.cache_cap(c3.keep + 512), c3.keep + 256
     K3, V3 = rn(c3.b, c3.H_kv, cap3, c3.d), rn(c3.b, c3.H_kv, c3.d, cap3)
     q3, kn3, vn3 = rn(steps, c3.b, c3.H_q, c3.d), rn(steps, c3.b, c3.H_kv, c3.d), rn(steps, c3.b, c3.H_kv, c3.d)
@@ -405,11 +405,11 @@ def main():
     if args.calibrate_copy:
         return calibrate_copy()
     import torch
-    from synth import CONFIGS
+    from synth import WORKLOADS
     from learned_kv_cache_mqa_amd import api
     from learned_kv_cache_mqa_amd import _lib as KL
 
-    cfg = CONFIGS[3].with_(layers=args.layers, T=args.decode_steps)
+    cfg = WORKLOADS["llama8b_32L_16k_b8"].with_(layers=args.layers, T=args.decode_steps)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     T, layers = cfg.T, cfg.layers

@@ -4,5 +4,5 @@ This package is shared by the fp64 oracle's tests and by the GPU path's tests an
 benchmark.  It holds workload shapes, seeded random draws and number-format
 conversions (bf16 <-> float) only; none of the method's arithmetic lives here.
 """
-from .configs import CONFIGS, Config, get_config  # noqa: F401
+from .configs import WORKLOADS, Config, workload  # noqa: F401
 from . import gen  # noqa: F401

@@ -79,8 +79,8 @@ CFG5 = Config(name="qwen3_4b_momentkv_32k", cfg_id=5, dtype="bf16", layers=36, b
               H_q=32, H_kv=8, d=128, L=32768, W=64, B=128, R=0, T=256, momentkv=True,
               budgets=(128, 256, 512, 1024))
 
-CONFIGS = {1: CFG1, 2: CFG2, 3: CFG3, 4: CFG4, 5: CFG5}
+WORKLOADS = {c.name: c for c in (CFG1, CFG2, CFG3, CFG4, CFG5)}
 
 
-def get_config(i: int) -> Config:
-    return CONFIGS[i]
+def workload(name: str) -> Config:
+    return WORKLOADS[name]

@@ -11,31 +11,31 @@ import numpy as np
 import pytest
 
 from oracle import chunked as ck
-from synth import CONFIGS, gen
+from synth import WORKLOADS, gen
 
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # config, overrides, chunk, batch elements
-    (2, dict(L=1500, B=300, R=32, needles=0), 512, 2),
-    (2, dict(L=1200, B=256, R=32, needles=0), 1200, 1),   # one chunk: the one-shot pre-eviction
-    (1, dict(L=512, B=64, R=0), 128, 1),                  # fp32, the fused-multiply-add kernels
-    (1, dict(L=400, B=90, R=16), 100, 2),
+    # workload, overrides, chunk, batch elements
+    ("llama8b_layer_4k", dict(L=1500, B=300, R=32, needles=0), 512, 2),
+    ("llama8b_layer_4k", dict(L=1200, B=256, R=32, needles=0), 1200, 1),   # one chunk: the one-shot pre-eviction
+    ("tiny_fp32", dict(L=512, B=64, R=0), 128, 1),                  # fp32, the fused-multiply-add kernels
+    ("tiny_fp32", dict(L=400, B=90, R=16), 100, 2),
 ]
 
 
-@pytest.mark.parametrize("cfg_id,over,C,nb", CASES)
-def test_chunked_pre_eviction_matches_oracle(cfg_id, over, C, nb):
+@pytest.mark.parametrize("wl,over,C,nb", CASES)
+def test_chunked_pre_eviction_matches_oracle(wl, over, C, nb):
     import torch
     from learned_kv_cache_mqa_amd import api
     from tests.gpu_util import to_dev, to_np, normwise, set_check
 
-    cfg = CONFIGS[cfg_id].with_(**over)
+    cfg = WORKLOADS[wl].with_(**over)
     dt, L, W, B, R = cfg.dtype, cfg.L, cfg.W, cfg.B, cfg.R
     lam = float(np.float32(cfg.lam))
     bl = list(range(nb))
     p = gen.make_prefill(cfg, batches=bl)
-    r = gen.rng(210, cfg_id, L, C)
+    r = gen.rng(210, cfg.cfg_id, L, C)
     Q = gen.to_storage(r.standard_normal((nb, L, cfg.H_q, cfg.d)), dt)
     f = lambda x: gen.from_storage(x, dt)
     W_kI, W_qI, W_g = f(p["W_kI"]), f(p["W_qI"]), f(p["W_g"])

@@ -16,7 +16,7 @@ import pytest
 from oracle import indexmem as im
 from oracle import momentkv as mk
 from oracle import streaming as so
-from synth import CONFIGS, gen
+from synth import WORKLOADS, gen
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -26,7 +26,7 @@ DEC_STEPS = 3     # decode steps checked here
 
 @pytest.fixture(scope="module")
 def cfg3_layer():
-    cfg = CONFIGS[3].with_(layers=1)
+    cfg = WORKLOADS["llama8b_32L_16k_b8"].with_(layers=1)
     p = gen.make_prefill(cfg)
     return cfg, p
 
@@ -204,7 +204,7 @@ def test_stream_step_full_pool():
     import torch
     from learned_kv_cache_mqa_amd import api
     from tests.gpu_util import to_dev, to_np, normwise
-    cfg = CONFIGS[4]
+    cfg = WORKLOADS["llama8b_layer_131k_stream"]
     dt = cfg.dtype
     lam = float(np.float32(cfg.lam))
     P = cfg.B + cfg.R
@@ -255,7 +255,7 @@ def test_momentkv_alpha_full_size():
     import torch
     from learned_kv_cache_mqa_amd import api
     from tests.gpu_util import to_dev, to_np, normwise
-    cfg = CONFIGS[5].with_(layers=1)
+    cfg = WORKLOADS["qwen3_4b_momentkv_32k"].with_(layers=1)
     p = gen.make_prefill(cfg)
     al = to_np(api.kvm_moment_alpha(to_dev(p["Qwin"]), to_dev(p["K"])))
     torch.cuda.synchronize()

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from oracle import indexmem as im
-from synth import CONFIGS, gen
+from synth import WORKLOADS, gen
 
 pytestmark = pytest.mark.gpu
 
@@ -30,13 +30,13 @@ def _run(cfg, p):
 
 
 CASES = [
-    CONFIGS[1],
-    CONFIGS[1].with_(L=300, W=7, B=40),
-    CONFIGS[2],
-    CONFIGS[2].with_(b=2, L=1000, B=100, R=8, needles=4),
-    CONFIGS[2].with_(L=777, W=1, B=77, R=0, needles=0),
-    CONFIGS[2].with_(L=1500, W=10, B=150, R=4, needles=2),   # staged query groups of 4, 4 and 2
-    CONFIGS[2].with_(L=64, W=64, B=16, R=4, needles=0),
+    WORKLOADS["tiny_fp32"],
+    WORKLOADS["tiny_fp32"].with_(L=300, W=7, B=40),
+    WORKLOADS["llama8b_layer_4k"],
+    WORKLOADS["llama8b_layer_4k"].with_(b=2, L=1000, B=100, R=8, needles=4),
+    WORKLOADS["llama8b_layer_4k"].with_(L=777, W=1, B=77, R=0, needles=0),
+    WORKLOADS["llama8b_layer_4k"].with_(L=1500, W=10, B=150, R=4, needles=2),   # staged query groups of 4, 4 and 2
+    WORKLOADS["llama8b_layer_4k"].with_(L=64, W=64, B=16, R=4, needles=0),
 ]
 
 
@@ -58,7 +58,7 @@ def test_index_scores_and_set(cfg):
         assert n_diff == 0 or n_diff <= 2
 
 
-@pytest.mark.parametrize("cfg", [CONFIGS[1], CONFIGS[2], CONFIGS[2].with_(b=2, L=2500, B=250, R=16, needles=4)],
+@pytest.mark.parametrize("cfg", [WORKLOADS["tiny_fp32"], WORKLOADS["llama8b_layer_4k"], WORKLOADS["llama8b_layer_4k"].with_(b=2, L=2500, B=250, R=16, needles=4)],
                          ids=lambda c: f"{c.name}-L{c.L}")
 def test_prefill_end_to_end(cfg):
     """score -> select -> compact + memory on the GPU vs the oracle's prefill."""

@@ -9,7 +9,7 @@ import pytest
 
 from oracle import indexmem as im
 from oracle import momentkv as mk
-from synth import CONFIGS, gen
+from synth import WORKLOADS, gen
 
 pytestmark = pytest.mark.gpu
 
@@ -137,7 +137,7 @@ def test_momentkv_prefill_and_decode(L, B, b, T):
     import torch
     from learned_kv_cache_mqa_amd import api
     from tests.gpu_util import to_dev, to_np, normwise, assert_output
-    cfg = CONFIGS[5].with_(L=L, B=B, b=b, T=T)
+    cfg = WORKLOADS["qwen3_4b_momentkv_32k"].with_(L=L, B=B, b=b, T=T)
     H, d, W, H_q = cfg.H_kv, cfg.d, cfg.W, cfg.H_q
     p = gen.make_prefill(cfg)
     dec = gen.make_decode(cfg, steps=T)

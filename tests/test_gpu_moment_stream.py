@@ -11,7 +11,7 @@ import pytest
 
 from oracle import moment_stream as ms
 from oracle import momentkv as mk
-from synth import CONFIGS, gen
+from synth import WORKLOADS, gen
 
 pytestmark = pytest.mark.gpu
 
@@ -82,7 +82,7 @@ def test_moment_stream_steps_match_oracle(name, b, H_q, H_kv, d, P, R, T, n_ev):
     from tests.gpu_util import to_dev, to_np, normwise, assert_output
 
     if P is None:
-        cfg = CONFIGS[5].with_(L=1024, B=128, b=b, T=T)
+        cfg = WORKLOADS["qwen3_4b_momentkv_32k"].with_(L=1024, B=128, b=b, T=T)
         pools = _prefill_pool(cfg)
         qs, ks, vs = (gen.make_decode(cfg, steps=T)[k] for k in ("q", "k_new", "v_new"))
     else:

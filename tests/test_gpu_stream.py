@@ -11,27 +11,27 @@ import pytest
 
 from oracle import indexmem as im
 from oracle import streaming as so
-from synth import CONFIGS, gen
+from synth import WORKLOADS, gen
 
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # config, overrides, steps, batch elements
-    (4, dict(L=1024, B=120, R=64), 48, 1),
-    (4, dict(L=700, B=33, R=17, W=32, needles=0), 40, 2),
-    (1, dict(streaming=True, B=40, R=8, recent_inclusive=False), 40, 1),
+    # workload, overrides, steps, batch elements
+    ("llama8b_layer_131k_stream", dict(L=1024, B=120, R=64), 48, 1),
+    ("llama8b_layer_131k_stream", dict(L=700, B=33, R=17, W=32, needles=0), 40, 2),
+    ("tiny_fp32", dict(streaming=True, B=40, R=8, recent_inclusive=False), 40, 1),
     # the timed pool: 1024 + 64 slots (68 score blocks of 16 keys), shorter prefill
-    (4, dict(L=2048, B=1024, R=64), 16, 1),
+    ("llama8b_layer_131k_stream", dict(L=2048, B=1024, R=64), 16, 1),
 ]
 
 
-@pytest.mark.parametrize("cfg_id,over,steps,nb", CASES)
-def test_stream_steps_match_oracle(cfg_id, over, steps, nb):
+@pytest.mark.parametrize("wl,over,steps,nb", CASES)
+def test_stream_steps_match_oracle(wl, over, steps, nb):
     import torch
     from learned_kv_cache_mqa_amd import api
     from tests.gpu_util import to_dev, to_np, normwise, assert_output
 
-    cfg = CONFIGS[cfg_id].with_(**over)
+    cfg = WORKLOADS[wl].with_(**over)
     dt = cfg.dtype
     lam = float(np.float32(cfg.lam))
     bl = list(range(nb))
