@@ -21,6 +21,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2516.6   # dense bf16 matrix cores: 256 CU x 2.4 GHz x 4096 flop/clk
 METRIC = "decode tok/s & %HBM peak (evicted cache+memory); index+evict ms @16K prefill"
 
 
@@ -362,6 +363,23 @@ def time_rows(torch, api, KL, dev):
     rows["N4_workload"] = (f"one layer at the 16K workload's shapes (batch {c3.b}, {c3.L} tokens, budget {c3.B}, "
                            f"recent {c3.R}): {nck} chunks of {Cn} tokens, each scored by its own {c3.W}-query window "
                            f"against pool + chunk, vs the one-shot index + evict holding all {c3.L} rows")
+    # each row's fraction of the roofline that bounds it, from its algorithmic work
+    kv5 = c5.b * c5.L * c5.H_kv * c5.d * 2 * 2                       # K and V of the 32K-token batch
+    alpha_flop = 2 * 2.0 * (c5.W * c5.H_q // c5.H_kv) * c5.L * c5.d * c5.b * c5.H_kv   # two passes of logits
+    pre_bytes = prefill_bytes(c3, c3.keep)                           # one layer of index+evict
+    frac = lambda bound, achieved, peak, unit: {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
+                                                "unit": unit, "frac": round(achieved / peak, 4)}
+    rows["roofline"] = {
+        "N3_prefix_states": frac("mfma", rows["N3_prefix_states_tflops"], MFMA_BF16_PEAK_TFS, "TFLOP/s"),
+        "V1_alpha": frac("mfma", alpha_flop / (rows["V1_alpha_ms"] * 1e-3) / 1e12, MFMA_BF16_PEAK_TFS, "TFLOP/s"),
+        "V1_score_round": frac("hbm", kv5 / (rows["V1_score_round_ms"] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"),
+        "N4_chunked_index_evict": frac("hbm", pre_bytes / (rows["N4_chunked_index_evict_ms"] * 1e-3) / 1e9,
+                                       HBM_PEAK_GBS, "GB/s"),
+        "N4_one_shot_index_evict": frac("hbm", pre_bytes / (rows["N4_one_shot_index_evict_ms"] * 1e-3) / 1e9,
+                                        HBM_PEAK_GBS, "GB/s"),
+        "latency_bound": ["A7_stream_step", "N1_moment_stream_step", "N2_decode_step", "N3_lookup_merge",
+                          "V3_readout"],
+    }
     return rows
 
 
