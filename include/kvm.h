@@ -216,7 +216,9 @@ kvm_status kvm_moment_update(const kvm_mem_desc* desc, const void* K_rows, const
  * P + C <= B + C tokens are ever held.  One call is one chunk of C tokens starting at
  * position `start`, with P tokens pooled before it:
  *   1. the chunk's K, V (token-major [b, C, H_kv, d]) and positions join the pool after its
- *      P rows;
+ *      P rows.  K = V = NULL: rows P .. P+C-1 of Kp, Vp already hold the chunk's keys and
+ *      values (e.g. written there by the prefill attention of the chunk), and only the
+ *      positions are written;
  *   2. the chunk's indexer keys; the queries of its last W positions (Qwin [b, W, H_q, d],
  *      X rows C-W .. C-1); their scores against pool and chunk keys in position order
  *      (each window query sees every key at or before it);

@@ -410,22 +410,24 @@ def kvm_asm_lookup(q, C_, a_bar, lse_bar, o_loc, lse_loc, o=None, lse_out=None, 
 
 def kvm_index_evict_chunk(X, Qwin, K_, V, W_kI, gamma_k, W_qI, gamma_q, W_g, pool, P, start, B, R, lam, cap_out,
                           final, M, bvec, recent_inclusive=True, eps=1e-6, stream=None, ws=None):
-    """One chunk of a chunked pre-eviction (X [b, C, D], Qwin [b, W, H_q, d], K, V [b, C, H_kv, d]).
+    """One chunk of a chunked pre-eviction (X [b, C, D], Qwin [b, W, H_q, d], K, V [b, C, H_kv, d],
+    or K = V = None when rows P .. P+C-1 of pool K, V already hold the chunk).
     pool = dict(K, V [b, H_kv, P + C, d], khat [b, P + C, d_I], I [b, P + C], pos [b, P + C]) with
     rows 0 .. P-1 holding the pool.  Returns (next pool dict with row capacity cap_out, keep);
     with final=True its V is dim-major [b, H_kv, d, cap_out] (the decode caches)."""
     _contig(X, Qwin, K_, V, W_kI, gamma_k, W_qI, gamma_q, W_g, M, bvec, *pool.values())
     b, C_, D = X.shape
     _, W, H_q, d = Qwin.shape
-    H_kv = K_.shape[2]
+    H_kv = pool["K"].shape[1]
     H_I, d_I, _ = W_qI.shape
     desc = K.ChunkDesc(b=b, D=D, H_q=H_q, H_kv=H_kv, d=d, H_I=H_I, d_I=d_I, W=W, B=B, R=R,
                        recent_inclusive=int(bool(recent_inclusive)), P=P, C=C_, start=start, cap_out=cap_out,
                        final=int(bool(final)), dtype=_dtype(X), lam=lam, eps_rms=eps)
     keep = lib().kvm_chunk_keep(C.byref(desc))
     dev = X.device
-    nxt = dict(K=torch.empty((b, H_kv, cap_out, d), dtype=K_.dtype, device=dev),
-               V=torch.empty((b, H_kv, d, cap_out) if final else (b, H_kv, cap_out, d), dtype=V.dtype, device=dev),
+    kdt = pool["K"].dtype
+    nxt = dict(K=torch.empty((b, H_kv, cap_out, d), dtype=kdt, device=dev),
+               V=torch.empty((b, H_kv, d, cap_out) if final else (b, H_kv, cap_out, d), dtype=kdt, device=dev),
                khat=torch.empty((b, cap_out, d_I), dtype=torch.float32, device=dev),
                I=torch.empty((b, cap_out), dtype=torch.float32, device=dev),
                pos=torch.empty((b, cap_out), dtype=torch.int32, device=dev))

@@ -826,8 +826,9 @@ extern "C" kvm_status kvm_index_score(const kvm_index_desc* d, const void* X, co
 // ------------------------------------------------------------------ chunked pre-eviction
 namespace kvm {
 
-// grid (ceil(C H_kv D / 8 / 256), b), 256 threads: the chunk's token-major K, V rows into the
-// pool's head-major rows P .. P + C - 1 (16 bytes per thread), and their positions.
+// grid (ceil(max(C H_kv D / 8, C) / 256), b), 256 threads: the chunk's token-major K, V rows
+// into the pool's head-major rows P .. P + C - 1 (16 bytes per thread; skipped when K is
+// NULL: the rows are already there), and their positions.
 template <typename T>
 __global__ __launch_bounds__(256) void chunk_append_kernel(const T* K, const T* V, T* Kp, T* Vp, int32_t* pos,
                                                            int C, int H_kv, int D, int P, int Lv, int start) {
@@ -835,7 +836,7 @@ __global__ __launch_bounds__(256) void chunk_append_kernel(const T* K, const T* 
   const int bb = blockIdx.y;
   const int i = blockIdx.x * 256 + threadIdx.x;          // 16-byte chunk of the batch row's C x H_kv x D
   const int per_tok = H_kv * D / N;
-  if (i < C * per_tok) {
+  if (K && i < C * per_tok) {
     const int t = i / per_tok, r = i % per_tok, g = r / (D / N), c = (r % (D / N)) * N;
     const size_t src = (((size_t)bb * C + t) * H_kv + g) * D + c;
     const size_t dst = (((size_t)bb * H_kv + g) * Lv + P + t) * D + c;
@@ -925,7 +926,8 @@ extern "C" kvm_status kvm_index_evict_chunk(const kvm_chunk_desc* d, const void*
   const int keep = kvm_chunk_keep(d);
   KVM_REQUIRE(keep >= 0, KVM_ERR_RANGE, "budget %d below the recent window %d", d->B, d->R);
   KVM_REQUIRE(d->cap_out >= keep, KVM_ERR_RANGE, "cap_out %d below the kept %d", d->cap_out, keep);
-  KVM_PTR_ALIGNED(X); KVM_PTR_ALIGNED(Qwin); KVM_PTR_ALIGNED(K); KVM_PTR_ALIGNED(V); KVM_PTR_ALIGNED(W_kI);
+  KVM_REQUIRE((K == nullptr) == (V == nullptr), KVM_ERR_NULL, "K and V must both be given or both NULL (in place)");
+  KVM_PTR_ALIGNED(X); KVM_PTR_ALIGNED(Qwin); KVM_OPT_ALIGNED(K); KVM_OPT_ALIGNED(V); KVM_PTR_ALIGNED(W_kI);
   KVM_PTR_ALIGNED(gamma_k); KVM_PTR_ALIGNED(W_qI); KVM_PTR_ALIGNED(gamma_q); KVM_PTR_ALIGNED(W_g);
   KVM_PTR_ALIGNED(Kp); KVM_PTR_ALIGNED(Vp); KVM_PTR_ALIGNED(khat_p); KVM_PTR_ALIGNED(I_p); KVM_PTR_ALIGNED(pos_p);
   KVM_PTR_ALIGNED(Kn); KVM_PTR_ALIGNED(Vn); KVM_PTR_ALIGNED(M); KVM_PTR_ALIGNED(bvec);
@@ -945,8 +947,8 @@ extern "C" kvm_status kvm_index_evict_chunk(const kvm_chunk_desc* d, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
   const int Lv = d->P + d->C;
-  // 1. the chunk's K, V and positions join the pool
-  const int nchunk16 = d->C * d->H_kv * d->d / (int)(16 / esz);
+  // 1. the chunk's K, V (unless already in place: K = V = NULL) and positions join the pool
+  const int nchunk16 = K ? d->C * d->H_kv * d->d / (int)(16 / esz) : 0;
   const dim3 agrid((std::max(nchunk16, d->C) + 255) / 256, d->b);
   if (d->dtype == KVM_BF16)
     hipLaunchKernelGGL(chunk_append_kernel<uint16_t>, agrid, dim3(256), 0, s, static_cast<const uint16_t*>(K),

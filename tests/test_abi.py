@@ -160,6 +160,8 @@ def test_chunk_validation(L):
     assert f(desc=dict(cap_out=2047)) == 5              # output pool below the kept count
     assert f(desc=dict(lam=1.5)) == 5
     assert f(X=None) == 1
+    assert f(K=None) == 1                                # K and V: both given, or both NULL (in place)
+    assert f(K=None, V=None) not in (1, 4)               # in place: accepted by the checks
     assert f(khn=None, In=None, posn=None) != 1          # the new pool's side data is optional
     assert f(Vp=FAKE + 8) == 4
     assert f(wsb=256) == 6

@@ -101,3 +101,51 @@ def test_chunked_pre_eviction_matches_oracle(wl, over, C, nb):
             bar = 1e-4 if dt == "bf16" else 1e-5   # bf16: the hi + lo split of lam^(n-i) phi(k)
             assert normwise(gM[i, g], ref["M"][g]) < bar
             assert normwise(gb[i, g], ref["b"][g]) < bar
+
+
+def test_chunked_in_place_matches_copy():
+    """The chunk's K/V already in the pool's rows P .. P+C-1 (K = V = NULL) gives the same pools,
+    caches and memory, bit for bit, as handing the chunk's token-major K/V to the call."""
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev
+
+    cfg = WORKLOADS["llama8b_layer_4k"].with_(L=1500, B=300, R=32, needles=0)
+    C, nb, W = 512, 2, cfg.W
+    p = gen.make_prefill(cfg, batches=list(range(nb)))
+    r = gen.rng(212, cfg.cfg_id, cfg.L, C)
+    Qd = to_dev(gen.to_storage(r.standard_normal((nb, cfg.L, cfg.H_q, cfg.d)), cfg.dtype))
+    X, K, V = to_dev(p["X"]), to_dev(p["K"]), to_dev(p["V"])
+    wts = [to_dev(p[k]) for k in ("W_kI", "gamma_k", "W_qI", "gamma_q", "W_g")]
+    cap = api.cache_cap(min(cfg.B, cfg.L))
+    starts = list(range(0, cfg.L, C))
+    outs = []
+    for in_place in (False, True):
+        M = torch.zeros((nb, cfg.H_kv, cfg.d, cfg.d), device="cuda")
+        bv = torch.zeros((nb, cfg.H_kv, cfg.d), device="cuda")
+        P, pool = 0, None
+        for c, s0 in enumerate(starts):
+            e = min(cfg.L, s0 + C)
+            n = e - s0
+            if pool is None:
+                pool = dict(K=torch.empty((nb, cfg.H_kv, n, cfg.d), dtype=torch.bfloat16, device="cuda"),
+                            V=torch.empty((nb, cfg.H_kv, n, cfg.d), dtype=torch.bfloat16, device="cuda"),
+                            khat=torch.empty((nb, n, cfg.d_I), device="cuda"),
+                            I=torch.empty((nb, n), device="cuda"),
+                            pos=torch.empty((nb, n), dtype=torch.int32, device="cuda"))
+            last = c == len(starts) - 1
+            cap_out = cap if last else min(P + n, cfg.B) + (min(cfg.L, starts[c + 1] + C) - starts[c + 1])
+            Kc, Vc = K[:, s0:e].contiguous(), V[:, s0:e].contiguous()
+            if in_place:   # the chunk's rows written into the pool tail, head-major
+                pool["K"][:, :, P:P + n] = Kc.transpose(1, 2)
+                pool["V"][:, :, P:P + n] = Vc.transpose(1, 2)
+                Kc = Vc = None
+            pool, P = api.kvm_index_evict_chunk(X[:, s0:e].contiguous(), Qd[:, e - W:e].contiguous(), Kc, Vc, *wts,
+                                                pool, P, s0, cfg.B, cfg.R, float(np.float32(cfg.lam)), cap_out, last,
+                                                M, bv, eps=cfg.eps_rms)
+        torch.cuda.synchronize()
+        outs.append({**{k: v[..., :P] if k != "V" else v[..., :P] for k, v in pool.items() if k in ("I", "pos")},
+                     "K": pool["K"][:, :, :P].clone(), "V": pool["V"][:, :, :, :P].clone(),
+                     "khat": pool["khat"][:, :P].clone(), "M": M.clone(), "b": bv.clone()})
+    for k in outs[0]:
+        assert torch.equal(outs[0][k], outs[1][k]), k
