@@ -226,7 +226,8 @@ kvm_status kvm_moment_update(const kvm_mem_desc* desc, const void* K_rows, const
  *      score, a chunk key's is its max over this window (kvm_index_score's form);
  *   4. kvm_topk_select over pool and chunk (L = P + C, budget B, recent R = the chunk's
  *      last R positions), kvm_compact_kv with KVM_FUSE_MEM (evictions folded into M, bvec
- *      in ascending position order) and kvm_gather_rows of keys, importances, positions.
+ *      in ascending position order), and the kept tokens' keys, importances and positions
+ *      carried into the next pool in one gather.
  * The per-chunk schedule is this library's reading of the section; one chunk covering the
  * prefill is the one-shot pre-eviction.  Pool buffers hold P + C rows per sequence (the
  * stride of every pool array is P + C): Kp, Vp [b, H_kv, P+C, d] row-major (dtype),

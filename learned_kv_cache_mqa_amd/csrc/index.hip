@@ -865,6 +865,29 @@ __global__ __launch_bounds__(256) void chunk_max_kernel(float* I, const float* I
   }
 }
 
+// One thread per (row, token, word) of the kept tokens' side data, words 0 .. d_I-1 the
+// indexer key, d_I the importance, d_I+1 the position: each into the token's slot of the next
+// pool (slot_map; tokens without a slot in [0, cap) are dropped).  Absent outputs are skipped.
+__global__ __launch_bounds__(256) void chunk_side_kernel(const float* khat_p, const float* I_p, const int32_t* pos_p,
+                                                         const int32_t* smap, float* khat_n, float* I_n,
+                                                         int32_t* pos_n, int rows, int Lv, int cap, int d_I) {
+  const int words = d_I + 2;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)rows * Lv * words) return;
+  const size_t rt = i / words;
+  const int w = (int)(i % words);
+  const int slot = smap[rt];
+  if (slot < 0 || slot >= cap) return;
+  const size_t dst = (size_t)(rt / Lv) * cap + slot;
+  if (w < d_I) {
+    if (khat_n) khat_n[dst * d_I + w] = khat_p[rt * d_I + w];
+  } else if (w == d_I) {
+    if (I_n) I_n[dst] = I_p[rt];
+  } else if (pos_n) {
+    pos_n[dst] = pos_p[rt];
+  }
+}
+
 struct ChunkWs { size_t idx, qt, gate, icur, ids, smap, comp, total; };
 static ChunkWs chunk_ws(const kvm_chunk_desc* d, size_t comp_bytes) {
   const size_t Lv = (size_t)d->P + d->C;
@@ -984,14 +1007,11 @@ extern "C" kvm_status kvm_index_evict_chunk(const kvm_chunk_desc* d, const void*
   st = kvm_compact_kv(&cd, Kp, Vp, smap, ids, Kn, Vn, M, bvec, nullptr, nullptr, nullptr, nullptr,
                       base + w.comp, cbytes, stream);
   if (st != KVM_OK) return st;
-  if (khat_n) {
-    st = kvm_gather_rows(d->b, Lv, d->cap_out, d->d_I * 4, khat_p, smap, khat_n, stream);
-    if (st != KVM_OK) return st;
+  if (khat_n || I_n || pos_n) {
+    const size_t total = (size_t)d->b * Lv * (d->d_I + 2);
+    hipLaunchKernelGGL(chunk_side_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, khat_p, I_p, pos_p,
+                       smap, khat_n, I_n, pos_n, d->b, Lv, d->cap_out, d->d_I);
+    st = check_hip(hipGetLastError(), "chunk side-data launch");
   }
-  if (I_n) {
-    st = kvm_gather_rows(d->b, Lv, d->cap_out, 4, I_p, smap, I_n, stream);
-    if (st != KVM_OK) return st;
-  }
-  if (pos_n) st = kvm_gather_rows(d->b, Lv, d->cap_out, 4, pos_p, smap, pos_n, stream);
   return st;
 }
