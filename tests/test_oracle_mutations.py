@@ -11,6 +11,7 @@ from oracle import asm
 from oracle import chunked as ck
 from oracle import moment_stream as ms
 from oracle import momentkv as mk
+from oracle import streaming as sm
 from tests import test_oracle_golden as gold
 from tests import test_oracle_pins as pins
 
@@ -19,6 +20,7 @@ _orig_mk = {name: getattr(mk, name) for name in dir(mk) if callable(getattr(mk, 
 _orig_ms = {name: getattr(ms, name) for name in dir(ms) if callable(getattr(ms, name))}
 _orig_asm = {name: getattr(asm, name) for name in dir(asm) if callable(getattr(asm, name))}
 _orig_ck = {name: getattr(ck, name) for name in dir(ck) if callable(getattr(ck, name))}
+_orig_sm = {name: getattr(sm, name) for name in dir(sm) if callable(getattr(sm, name))}
 
 
 def _phi_no_plus_one(x):
@@ -194,6 +196,64 @@ def _chunked_window_at_start(X, Q, K, V, W_kI, gamma_k, W_qI, gamma_q, W_g, B, R
                                        recent_inclusive, act, eps)
 
 
+def _select_lowest(scores, pos, keep):
+    # each MomentKV round keeps the lowest scores instead of the highest
+    return _orig_mk["select_round"](-np.asarray(scores, np.float64), pos, keep)
+
+
+def _score_empty_moments(alpha_j, k, v, mom, d):
+    # every round scored as if nothing had been evicted yet
+    return _orig_mk["score"](alpha_j, k, v, mk.empty(d), d)
+
+
+def _mk_decode_no_append(q_steps, k_steps, v_steps, K, V, heads, T=None):
+    # the decode attends over the kept rows only: the new K/V never joins them
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    T = q_steps.shape[0] if T is None else T
+    H_q, d = q_steps.shape[1], q_steps.shape[2]
+    G = H_q // K.shape[1]
+    out, lses, ws = np.zeros((T, H_q, d)), np.zeros((T, H_q)), np.zeros((T, H_q))
+    for t in range(T):
+        for h in range(H_q):
+            g = h // G
+            q = np.asarray(q_steps[t, h], np.float64)
+            f_R, lse_R = im.attention_state(q, K[heads[g]["kept"], g], V[heads[g]["kept"], g], d ** -0.5)
+            out[t, h], ws[t, h] = mk.mix(q, f_R, lse_R, heads[g]["mom"], d)
+            lses[t, h] = lse_R
+    return out, lses, ws
+
+
+def _stream_readout_before_fold(st, x_new, q_new, k_new, v_new, W_kI, gamma_k, W_qI, gamma_q, W_g,
+                                w_g, lam, eps=1e-6, eps_mem=1e-6):
+    # the step reads the memory out with M, b from before the evicted row's fold
+    M0, b0 = st.M.copy(), st.b.copy()
+    o, lse, ev, e = _orig_sm["step"](st, x_new, q_new, k_new, v_new, W_kI, gamma_k, W_qI, gamma_q,
+                                     W_g, w_g, lam, eps, eps_mem)
+    m1, g = im.memory_readout(q_new, st.M, st.b, w_g, eps_mem)
+    m0, _ = im.memory_readout(q_new, M0, b0, w_g, eps_mem)
+    return o - g[:, None] * m1 + g[:, None] * m0, lse, ev, e
+
+
+def _residual_without_gate(o_attn, m, g):
+    return o_attn + m
+
+
+MUTATIONS_COMPOSITION = [
+    ("MomentKV round keeps the lowest scores", mk, "select_round", _select_lowest,
+     [pins.test_moment_rounds_selection_and_residuals_brute_force]),
+    ("MomentKV later rounds scored with empty moments", mk, "score", _score_empty_moments,
+     [pins.test_moment_rounds_selection_and_residuals_brute_force]),
+    ("MomentKV decode does not append the new K/V", mk, "decode", _mk_decode_no_append,
+     [lambda: pins.test_momentkv_decode_appends_then_mixes_brute_force(5),
+      lambda: pins.test_momentkv_decode_appends_then_mixes_brute_force(60)]),
+    ("stream step reads the memory before the fold", sm, "step", _stream_readout_before_fold,
+     [pins.test_streaming_step_output_brute_force]),
+    ("decode drops the memory gate", im, "residual_output", _residual_without_gate,
+     [pins.test_indexmem_decode_with_memory_brute_force]),
+]
+
+
 MUTATIONS_STREAM = [
     ("stream alpha drops the new token", ms, "step_alpha", _stream_alpha_without_new,
      [pins.test_stream_alpha_is_textbook_softmax_and_window_of_one]),
@@ -239,8 +299,10 @@ MUTATIONS = [
 ]
 
 
-@pytest.mark.parametrize("name,mod,attr,fn,tests", MUTATIONS + MUTATIONS_STREAM,
-                         ids=[m[0] for m in MUTATIONS + MUTATIONS_STREAM])
+ALL_MUTATIONS = MUTATIONS + MUTATIONS_STREAM + MUTATIONS_COMPOSITION
+
+
+@pytest.mark.parametrize("name,mod,attr,fn,tests", ALL_MUTATIONS, ids=[m[0] for m in ALL_MUTATIONS])
 def test_mutation_is_caught(monkeypatch, name, mod, attr, fn, tests):
     monkeypatch.setattr(mod, attr, fn)
     for t in tests:

@@ -606,7 +606,7 @@ def test_stream_steps_brute_force_choice_and_moments():
         q, kn, vn = r.standard_normal((H_q, d)), r.standard_normal((H_kv, d)), r.standard_normal((H_kv, d))
         p = st_.next_pos
         pos0, K0, V0 = st_.slot_pos.copy(), st_.Kc.copy(), st_.Vc.copy()
-        _, _, slots, evp, _ = ms.step(st_, q, kn, vn)
+        o, lse, slots, evp, _ = ms.step(st_, q, kn, vn)
         for g in range(H_kv):
             Ke = np.array([k for k, _ in evicted[g]])
             Ve = np.array([v for _, v in evicted[g]])
@@ -633,6 +633,20 @@ def test_stream_steps_brute_force_choice_and_moments():
             np.testing.assert_allclose(m["S"], S_ref, rtol=1e-12, atol=1e-13 * np.abs(S_ref).max())
             assert sorted(st_.slot_pos[g].tolist()) == sorted(set(pos0[g].tolist()) - {evp[g]} | {p})
             assert np.array_equal(st_.Kc[g, best], kn[g]) and np.array_equal(st_.Vc[g, best], vn[g])
+            # the output: the post-hand-over pool mixed with the estimate of every row
+            # evicted so far, this step's included (Jensen weight, plain loops)
+            Ks = [kn[g] if j == best else K0[g, j] for j in range(P)]
+            Vs = [vn[g] if j == best else V0[g, j] for j in range(P)]
+            ne = len(Ke)
+            kb, vb, St = _moments_s(Ke, Ve)
+            for h in (2 * g, 2 * g + 1):
+                fR, lz = _attend_s(q[h], Ks, Vs, 1 / math.sqrt(d))
+                ZE = ne * math.exp(_dot_s(q[h], kb) / math.sqrt(d))
+                wR = math.exp(lz) / (math.exp(lz) + ZE)
+                fE = [vb[a] + _dot_s(St[a], q[h]) / (ne * math.sqrt(d)) for a in range(d)]
+                np.testing.assert_allclose(o[h], [wR * fR[a] + (1 - wR) * fE[a] for a in range(d)],
+                                           rtol=1e-10, atol=1e-12)
+                assert lse[h] == pytest.approx(lz, rel=1e-12)
 
 
 # ============================================================================ read-out projection
@@ -831,3 +845,210 @@ def test_chunked_running_max_budget_and_fold_composition():
         Mr, br = im.memory_build(c["K"][evicted_all, g], c["V"][evicted_all, g], lam)
         np.testing.assert_allclose(out["M"][g], Mr, rtol=1e-12)
         np.testing.assert_allclose(out["b"][g], br, rtol=1e-12)
+
+
+# ============================================================================ compositions, by brute force
+#
+# Each pipeline function below is checked end to end against the definitions written out
+# as plain loops over scalars: no oracle helper other than the function under test takes
+# part in the expected value.
+
+def _phi_s(x):
+    return x + 1.0 if x > 0 else math.exp(x)
+
+
+def _sig_s(x):
+    return 1.0 / (1.0 + math.exp(-x))
+
+
+def _dot_s(a, b):
+    return sum(float(x) * float(y) for x, y in zip(a, b))
+
+
+def _attend_s(q, Ks, Vs, scale):
+    """Plain softmax attention of one query over a list of rows: output and log Z."""
+    s = [scale * _dot_s(q, k) for k in Ks]
+    mx = max(s)
+    e = [math.exp(x - mx) for x in s]
+    Z = sum(e)
+    out = np.array([sum(e[j] * float(Vs[j][i]) for j in range(len(Ks))) / Z for i in range(len(q))])
+    return out, mx + math.log(Z)
+
+
+def _moments_s(Ke, Ve):
+    """Key mean, value mean and sum_i (v_i - v_bar)(k_i - k_bar)^T over evicted rows."""
+    n, d = len(Ke), len(Ke[0])
+    kbar = [sum(float(Ke[i][c]) for i in range(n)) / n for c in range(d)]
+    vbar = [sum(float(Ve[i][c]) for i in range(n)) / n for c in range(d)]
+    St = [[sum((float(Ve[i][a]) - vbar[a]) * (float(Ke[i][c]) - kbar[c]) for i in range(n))
+           for c in range(d)] for a in range(d)]
+    return kbar, vbar, St
+
+
+def _alpha_s(Q, K, g, G, q_pos, scale):
+    """alpha_j of KV head g: causal softmax weight of key j, averaged over window queries
+    and the G query heads of the group."""
+    W, L = Q.shape[0], K.shape[0]
+    al = [0.0] * L
+    for s in range(W):
+        for h in range(g * G, (g + 1) * G):
+            n = int(q_pos[s]) + 1
+            lg = [scale * _dot_s(Q[s, h], K[j, g]) for j in range(n)]
+            mx = max(lg)
+            e = [math.exp(x - mx) for x in lg]
+            Z = sum(e)
+            for j in range(n):
+                al[j] += e[j] / Z
+    return [a / (W * G) for a in al]
+
+
+def test_moment_rounds_selection_and_residuals_brute_force():
+    # Every round of the moment-informed prefill: the round's scores equal
+    # alpha_j * ||v_j - v_bar - S~ k_j / (n_e sqrt d)|| with the moments of every token
+    # evicted in EARLIER rounds (r_j = v_j before any eviction), the round keeps
+    # max(B, ceil(n/2)) tokens, and every kept score beats every evicted one (equal
+    # scores: the lower position is kept).
+    # catches: keeping the lowest scores; later rounds scored with empty or stale moments.
+    r = np.random.default_rng(21)
+    W, Hq, Hkv, d, L, B = 3, 4, 2, 6, 41, 5
+    Q, K, V = r.standard_normal((W, Hq, d)), r.standard_normal((L, Hkv, d)), r.standard_normal((L, Hkv, d))
+    out = mk.prefill(Q, K, V, B)
+    G, scale = Hq // Hkv, 1 / math.sqrt(d)
+    q_pos = list(range(L - W, L))
+    for g in range(Hkv):
+        al = _alpha_s(Q, K, g, G, q_pos, scale)
+        hd = out["heads"][g]
+        pos = list(range(L))
+        evicted = []
+        assert len(hd["rounds"]) == 4          # 41 -> 21 -> 11 -> 6 -> 5
+        for rd in hd["rounds"]:
+            assert rd["pos"].tolist() == pos
+            if evicted:
+                n_e = len(evicted)
+                kbar, vbar, St = _moments_s([K[e, g] for e in evicted], [V[e, g] for e in evicted])
+            want = []
+            for j in pos:
+                if not evicted:
+                    res = [float(x) for x in V[j, g]]
+                else:
+                    res = [float(V[j, g][a]) - vbar[a] - _dot_s(St[a], K[j, g]) / (n_e * math.sqrt(d))
+                           for a in range(d)]
+                want.append(al[j] * math.sqrt(sum(x * x for x in res)))
+            np.testing.assert_allclose(rd["scores"], want, rtol=1e-10)
+            keep_n = max(B, -(-len(pos) // 2))
+            kept, ev = rd["kept"].tolist(), rd["evicted"].tolist()
+            assert len(kept) == keep_n and sorted(kept + ev) == pos and kept == sorted(kept)
+            sc = dict(zip(pos, want))
+            for a in kept:
+                for e in ev:
+                    assert sc[a] > sc[e] or (sc[a] == sc[e] and a < e)
+            evicted += ev
+            pos = kept
+        assert hd["kept"].tolist() == pos and hd["mom"]["n"] == len(evicted) == L - B
+
+
+@pytest.mark.parametrize("B", [5, 60])
+def test_momentkv_decode_appends_then_mixes_brute_force(B):
+    # Decode over each KV head's kept tokens PLUS every token appended so far, mixed with
+    # the first-order estimate by the Jensen weight.  B >= L (nothing evicted) must be
+    # textbook softmax attention over the whole sequence.
+    # catches: attending without appending the new K/V; mixing weight or estimate slips.
+    r = np.random.default_rng(22)
+    W, Hq, Hkv, d, L, T = 3, 4, 2, 6, 23, 3
+    Q, K, V = r.standard_normal((W, Hq, d)), r.standard_normal((L, Hkv, d)), r.standard_normal((L, Hkv, d))
+    qs, ks, vs = r.standard_normal((T, Hq, d)), r.standard_normal((T, Hkv, d)), r.standard_normal((T, Hkv, d))
+    heads = mk.prefill(Q, K, V, B)["heads"]
+    o, lse, w = mk.decode(qs, ks, vs, K, V, heads)
+    G, scale = Hq // Hkv, 1 / math.sqrt(d)
+    for g in range(Hkv):
+        kept = heads[g]["kept"].tolist()
+        evicted = [t for t in range(L) if t not in kept]
+        assert (len(evicted) == 0) == (B >= L)
+        if evicted:
+            kbar, vbar, St = _moments_s([K[e, g] for e in evicted], [V[e, g] for e in evicted])
+        for t in range(T):
+            Ks = [K[j, g] for j in kept] + [ks[u, g] for u in range(t + 1)]
+            Vs = [V[j, g] for j in kept] + [vs[u, g] for u in range(t + 1)]
+            for h in range(g * G, (g + 1) * G):
+                fR, lseR = _attend_s(qs[t, h], Ks, Vs, scale)
+                assert lse[t, h] == pytest.approx(lseR, rel=1e-12)
+                if not evicted:
+                    np.testing.assert_allclose(o[t, h], fR, rtol=1e-11, atol=1e-13)
+                    assert w[t, h] == 1.0
+                    continue
+                n_e = len(evicted)
+                ZE = n_e * math.exp(scale * _dot_s(qs[t, h], kbar))
+                wR = math.exp(lseR) / (math.exp(lseR) + ZE)
+                fE = [vbar[a] + _dot_s(St[a], qs[t, h]) / (n_e * math.sqrt(d)) for a in range(d)]
+                want = [wR * fR[a] + (1 - wR) * fE[a] for a in range(d)]
+                assert w[t, h] == pytest.approx(wR, rel=1e-11)
+                np.testing.assert_allclose(o[t, h], want, rtol=1e-10, atol=1e-12)
+
+
+def test_streaming_step_output_brute_force():
+    # Each streaming step's output is plain softmax attention over the pool AFTER the
+    # hand-over (the evicted slot holds the new token) plus sigmoid(w_g.q) M' phi(q) /
+    # (b'.phi(q) + eps), where M' = lam M + v_e phi(k_e)^T and b' = lam b + phi(k_e) fold the
+    # evicted row in first.
+    # catches: reading out with the memory from before the fold; attending before the
+    # hand-over; the gate or the fold applied wrongly.
+    w, pre, (xs, qs, ks, vs), wg = _stream_setup(seed=8, T=12)
+    Rw, lam, eps = 3, 0.9, 1e-6
+    st_ = sm.from_prefill(pre, 30, Rw)
+    Hkv, P, d = st_.Kc.shape
+    G = qs.shape[1] // Hkv
+    for t in range(len(xs)):
+        Kc0, Vc0, M0, b0 = st_.Kc.copy(), st_.Vc.copy(), st_.M.copy(), st_.b.copy()
+        o, lse, ev_pos, e = sm.step(st_, xs[t], qs[t], ks[t], vs[t], w["W_kI"], w["gamma_k"],
+                                    w["W_qI"], w["gamma_q"], w["W_g"], wg, lam, eps_mem=eps)
+        for g in range(Hkv):
+            fk = [_phi_s(float(x)) for x in Kc0[g, e]]
+            Mg = [[lam * M0[g][a][c] + float(Vc0[g, e][a]) * fk[c] for c in range(d)] for a in range(d)]
+            bg = [lam * b0[g][c] + fk[c] for c in range(d)]
+            Ks = [ks[t, g] if j == e else Kc0[g, j] for j in range(P)]
+            Vs = [vs[t, g] if j == e else Vc0[g, j] for j in range(P)]
+            for h in range(g * G, (g + 1) * G):
+                q = qs[t, h]
+                att, lz = _attend_s(q, Ks, Vs, 1 / math.sqrt(d))
+                fq = [_phi_s(float(x)) for x in q]
+                den = _dot_s(bg, fq) + eps
+                gate = _sig_s(_dot_s(wg[h], q))
+                want = [att[a] + gate * _dot_s(Mg[a], fq) / den for a in range(d)]
+                np.testing.assert_allclose(o[h], want, rtol=1e-10, atol=1e-12)
+                assert lse[h] == pytest.approx(lz, rel=1e-12)
+
+
+def test_indexmem_decode_with_memory_brute_force():
+    # Decode with a non-zero memory: o = softmax attention over the retained slots plus the
+    # appended ones, plus sigmoid(w_g.q) M phi(q) / (b.phi(q) + eps), with M, b held fixed.
+    # catches: the gate dropped (the only other end-to-end pin has M = 0).
+    r = np.random.default_rng(23)
+    Hq, Hkv, d, n0, T, lam, eps = 4, 2, 6, 7, 3, 0.8, 1e-6
+    cap = n0 + T
+    Kc, Vc = np.zeros((Hkv, cap, d)), np.zeros((Hkv, cap, d))
+    Kc[:, :n0], Vc[:, :n0] = r.standard_normal((Hkv, n0, d)), r.standard_normal((Hkv, n0, d))
+    # the memory of 9 evicted rows per KV head, folded one at a time
+    M, b = np.zeros((Hkv, d, d)), np.zeros((Hkv, d))
+    for g in range(Hkv):
+        for _ in range(9):
+            k, v = r.standard_normal(d), r.standard_normal(d)
+            for a in range(d):
+                for c in range(d):
+                    M[g, a, c] = lam * M[g, a, c] + v[a] * _phi_s(k[c])
+            for c in range(d):
+                b[g, c] = lam * b[g, c] + _phi_s(k[c])
+    qs, ks, vs = r.standard_normal((T, Hq, d)), r.standard_normal((T, Hkv, d)), r.standard_normal((T, Hkv, d))
+    wg = r.standard_normal((Hq, d))
+    o, lse, _, _ = im.decode(qs, ks, vs, Kc, Vc, n0, M, b, wg, eps=eps)
+    G = Hq // Hkv
+    for t in range(T):
+        for h in range(Hq):
+            g, q = h // G, qs[t, h]
+            Ks = [Kc[g, j] for j in range(n0)] + [ks[u, g] for u in range(t + 1)]
+            Vs = [Vc[g, j] for j in range(n0)] + [vs[u, g] for u in range(t + 1)]
+            att, lz = _attend_s(q, Ks, Vs, 1 / math.sqrt(d))
+            fq = [_phi_s(float(x)) for x in q]
+            gate = _sig_s(_dot_s(wg[h], q))
+            want = [att[a] + gate * _dot_s(M[g, a], fq) / (_dot_s(b[g], fq) + eps) for a in range(d)]
+            np.testing.assert_allclose(o[t, h], want, rtol=1e-10, atol=1e-12)
+            assert lse[t, h] == pytest.approx(lz, rel=1e-12)
