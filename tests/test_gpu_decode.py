@@ -308,3 +308,107 @@ def test_readout_projection_matches_oracle(dtype, b, H_q, H_kv, d, cap, lens, n_
         m, g = im.memory_readout(qd[i], c["M"][i].astype(np.float64), c["bv"][i].astype(np.float64), f(c["w_g"]),
                                  1e-6, q_mem=qm_ref[i])
         assert_output(o2[i], im.residual_output(oa, m, g), dtype, f"seq {i}: projection pipeline")
+
+
+def _merge_stress_inputs(r, layers, steps, b, H_q, H_kv, d, cap, lens):
+    st = lambda x: gen.to_storage(x, "bf16")
+    Ls = []
+    for _ in range(layers):
+        M = np.zeros((b, H_kv, d, d))
+        bv = np.zeros((b, H_kv, d))
+        for bi in range(b):
+            for g in range(H_kv):
+                M[bi, g], bv[bi, g] = im.memory_build(r.standard_normal((30, d)), r.standard_normal((30, d)), 0.99)
+        Ls.append(dict(Kc=st(r.standard_normal((b, H_kv, cap, d))), Vc=st(r.standard_normal((b, H_kv, cap, d))),
+                       w_g=st(r.standard_normal((H_q, d)) / math.sqrt(d)), M=M.astype(np.float32),
+                       bv=bv.astype(np.float32),
+                       q=st(r.standard_normal((steps, b, H_q, d))), kn=st(r.standard_normal((steps, b, H_kv, d))),
+                       vn=st(r.standard_normal((steps, b, H_kv, d)))))
+    return Ls
+
+
+def _merge_stress_ref(Ls, l, t, lens, d):
+    """Oracle output of layer l at step t: caches grown by steps 0..t, memory read-out."""
+    f = lambda x: gen.from_storage(x, "bf16")
+    c = Ls[l]
+    out = []
+    for bi in range(len(lens)):
+        K, V = f(c["Kc"][bi]).copy(), f(c["Vc"][bi]).copy()
+        for u in range(t + 1):
+            K[:, lens[bi] + u], V[:, lens[bi] + u] = f(c["kn"][u, bi]), f(c["vn"][u, bi])
+        o, _ = im.decode_attention(f(c["q"][t, bi]), K, V, lens[bi] + t + 1, 1 / math.sqrt(d))
+        m, g = im.memory_readout(f(c["q"][t, bi]), c["M"][bi].astype(np.float64), c["bv"][bi].astype(np.float64),
+                                 f(c["w_g"]), 1e-6)
+        out.append(im.residual_output(o, m, g))
+    return np.stack(out)
+
+
+def test_decode_many_launches_and_graph_replays():
+    """Back-to-back decode launches at the 16K workload's decode shape (batch 8, 32/8 heads,
+    ~1900 slots), two layers sharing one workspace, new inputs every step: every launch's
+    output must match the oracle (a merge reading block states left by an earlier launch
+    would not), eagerly and replayed from a HIP graph with fresh inputs copied in between
+    replays."""
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np, assert_output
+
+    b, H_q, H_kv, d, layers, steps = 8, 32, 8, 128, 2, 12
+    cap = api.cache_cap(1900 + steps)
+    r = gen.rng(94, 0, 0, 0)
+    lens = [1880 + 3 * i for i in range(b)]
+    Ls = _merge_stress_inputs(r, layers, steps, b, H_q, H_kv, d, cap, lens)
+    ws = torch.zeros(8 << 20, dtype=torch.uint8, device="cuda")
+    D = []
+    for c in Ls:
+        D.append(dict(Kc=to_dev(c["Kc"]), Vc=to_dev(np.ascontiguousarray(c["Vc"].transpose(0, 1, 3, 2))),
+                      M=to_dev(c["M"]), bv=to_dev(c["bv"]), w_g=to_dev(c["w_g"])))
+    lens_t = to_dev(np.array(lens, np.int32))
+    outs = [[None] * steps for _ in range(layers)]
+    # eager: steps 0 .. steps/2 - 1
+    half = steps // 2
+    for t in range(half):
+        for l in range(layers):
+            c = Ls[l]
+            outs[l][t] = api.kvm_decode_attn_mem(to_dev(c["q"][t]), D[l]["Kc"], D[l]["Vc"], lens_t,
+                                                 k_new=to_dev(c["kn"][t]), v_new=to_dev(c["vn"][t]), M=D[l]["M"],
+                                                 bvec=D[l]["bv"], w_g=D[l]["w_g"], ws=ws)
+        api.kvm_len_add(lens_t, 1)
+    torch.cuda.synchronize()
+    # graph: one step of both layers captured over static input buffers, replayed with the
+    # remaining steps' inputs copied in
+    qb = [torch.empty((b, H_q, d), dtype=torch.bfloat16, device=lens_t.device) for _ in range(layers)]
+    kb = [torch.empty((b, H_kv, d), dtype=torch.bfloat16, device=lens_t.device) for _ in range(layers)]
+    vb = [torch.empty((b, H_kv, d), dtype=torch.bfloat16, device=lens_t.device) for _ in range(layers)]
+    ob = [torch.empty((b, H_q, d), dtype=torch.float32, device=lens_t.device) for _ in range(layers)]
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for l in range(layers):
+                api.kvm_decode_attn_mem(qb[l], D[l]["Kc"], D[l]["Vc"], lens_t, k_new=kb[l], v_new=vb[l], M=D[l]["M"],
+                                        bvec=D[l]["bv"], w_g=D[l]["w_g"], o=ob[l], ws=ws, stream=stream)
+            api.kvm_len_add(lens_t, 1, stream=stream)
+    torch.cuda.synchronize()
+    # capture launched nothing: the caches and lengths still stand after the eager steps
+    assert to_np(lens_t).tolist() == [x + half for x in lens]
+    for t in range(half, steps):
+        for l in range(layers):
+            c = Ls[l]
+            qb[l].copy_(to_dev(c["q"][t]))
+            kb[l].copy_(to_dev(c["kn"][t]))
+            vb[l].copy_(to_dev(c["vn"][t]))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(layers):
+            outs[l][t] = ob[l].clone()
+    torch.cuda.synchronize()
+    for l in range(layers):
+        for t in range(steps):
+            ref = _merge_stress_ref(Ls, l, t, lens, d)
+            got = to_np(outs[l][t])
+            for bi in range(b):
+                assert_output(got[bi], ref[bi], "bf16", f"layer {l} step {t} seq {bi}")
+                np.testing.assert_allclose(got[bi], ref[bi], rtol=2e-4, atol=2e-4 * np.abs(ref[bi]).max(),
+                                           err_msg=f"layer {l} step {t} seq {bi}")
