@@ -121,6 +121,63 @@ def test_kmeans_matches_oracle(N, H, d, K, iters, nc):
         np.testing.assert_allclose(Cg[h], Cr, rtol=1e-5, atol=1e-6)
 
 
+def _d2(X, C):
+    """Squared distances [N, K] in fp64 (for validity checks of the GPU's own results)."""
+    return (X * X).sum(1)[:, None] - 2.0 * X @ C.T + (C * C).sum(1)[None, :]
+
+
+def test_kmeans_benchmark_seeding_band():
+    """K-means as the benchmark seeds it: unclustered N(0, 1) queries, the first K queries as
+    the initial centroids, so near-ties between centroids do occur.  Per head and iteration t
+    (the library run for t rounds), the assignment must equal the oracle's except at points
+    whose two candidate distances agree to 1e-5 (after such a point the trajectories
+    legitimately part, and that head is no longer compared with the oracle); the centroids
+    must match while the assignments agree.  At every t the GPU's own trajectory must also be
+    valid: each point at a nearest centroid of C_t (within the band), and C_t the mean of the
+    members under the previous assignment (a centroid without members stays)."""
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np
+    N, H, d, K, iters = 2048, 2, 128, 128, 6
+    r = gen.rng(203, 0, 0, 0)
+    Xs = _bf(r.standard_normal((N, H, d)))
+    X = _f(Xs)
+    C0 = np.ascontiguousarray(X[:K].transpose(1, 0, 2)).astype(np.float32)
+    Cs, ids = [], []
+    for t in range(iters + 1):
+        Cd = to_dev(C0)
+        ids.append(to_np(api.kvm_asm_kmeans(to_dev(Xs), Cd, t)))
+        Cs.append(to_np(Cd).astype(np.float64))
+    compared = 0
+    for h in range(H):
+        Xh = X[:, h]
+        # validity of the GPU's own trajectory
+        for t in range(iters + 1):
+            d2 = _d2(Xh, Cs[t][h])
+            got = d2[np.arange(N), ids[t][h]]
+            assert (got <= d2.min(1) * (1 + 1e-5) + 1e-9).all(), f"head {h} t {t}: a point not at a nearest centroid"
+            if t:
+                for k in range(K):
+                    m = ids[t - 1][h] == k
+                    want = Xh[m].mean(0) if m.any() else Cs[t - 1][h][k]
+                    np.testing.assert_allclose(Cs[t][h][k], want, rtol=1e-5, atol=1e-5)
+        # against the oracle's trajectory, until a near-tie
+        C = C0[h].astype(np.float64)
+        idx_r, d2r = asm.kmeans_assign(Xh, C)
+        for t in range(iters + 1):
+            if t:
+                C = asm.kmeans_update(Xh, idx_r, C)
+                idx_r, d2r = asm.kmeans_assign(Xh, C)
+            diff = np.nonzero(ids[t][h] != idx_r)[0]
+            if len(diff):
+                g = ids[t][h][diff]
+                gap = np.abs(d2r[diff, g] - d2r[diff, idx_r[diff]])
+                assert (gap <= 1e-5 * d2r[diff, idx_r[diff]]).all(), f"head {h} t {t}: assignment outside the band"
+                break
+            np.testing.assert_allclose(Cs[t][h], C, rtol=1e-5, atol=1e-6)
+            compared += 1
+    assert compared >= iters, f"only {compared} iterations compared with the oracle"
+
+
 def test_cluster_states_match_oracle():
     from learned_kv_cache_mqa_amd import api
     from tests.gpu_util import to_dev, to_np
