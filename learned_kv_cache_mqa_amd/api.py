@@ -420,6 +420,23 @@ def kvm_index_evict_chunk(X, Qwin, K_, V, W_kI, gamma_k, W_qI, gamma_q, W_g, poo
     _, W, H_q, d = Qwin.shape
     H_kv = pool["K"].shape[1]
     H_I, d_I, _ = W_qI.shape
+    # the library addresses every pool array with a row stride of exactly P + C
+    rows = P + C_
+    want = dict(K=(b, H_kv, rows, d), V=(b, H_kv, rows, d), khat=(b, rows, d_I), I=(b, rows), pos=(b, rows))
+    for k, shape in want.items():
+        if tuple(pool[k].shape) != shape:
+            raise ValueError(f"pool[{k!r}] has shape {tuple(pool[k].shape)}, expected {shape} (P + C = {rows} rows)")
+    if pool["khat"].dtype != torch.float32 or pool["I"].dtype != torch.float32 or pool["pos"].dtype != torch.int32:
+        raise ValueError("pool khat and I must be float32, pos int32")
+    if pool["K"].dtype != X.dtype or pool["V"].dtype != X.dtype:
+        raise ValueError(f"pool K/V dtype {pool['K'].dtype} differs from X's {X.dtype}")
+    if (K_ is None) != (V is None):
+        raise ValueError("K and V must both be given or both be None (in-place mode)")
+    if K_ is not None:
+        if tuple(K_.shape) != (b, C_, H_kv, d) or tuple(V.shape) != (b, C_, H_kv, d):
+            raise ValueError(f"chunk K/V must be {(b, C_, H_kv, d)}")
+        if K_.dtype != X.dtype or V.dtype != X.dtype:
+            raise ValueError("chunk K/V dtype differs from X's")
     desc = K.ChunkDesc(b=b, D=D, H_q=H_q, H_kv=H_kv, d=d, H_I=H_I, d_I=d_I, W=W, B=B, R=R,
                        recent_inclusive=int(bool(recent_inclusive)), P=P, C=C_, start=start, cap_out=cap_out,
                        final=int(bool(final)), dtype=_dtype(X), lam=lam, eps_rms=eps)

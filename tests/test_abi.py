@@ -229,3 +229,33 @@ int main(void) {
     assert lines[0] == "abi 2"
     assert lines[1] == "keep 64 bad -1"
     assert lines[2].startswith("null 1 ")
+
+
+def test_chunk_wrapper_rejects_mismatched_pool():
+    """The chunked pre-eviction addresses every pool array with a row stride of P + C, so the
+    binding refuses pools of any other row count or dtype before calling the library."""
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    b, C_, D, W, H_q, H_kv, d, H_I, d_I, P = 1, 64, 32, 16, 4, 2, 8, 4, 8, 40
+    X = torch.zeros((b, C_, D), dtype=torch.bfloat16)
+    Q = torch.zeros((b, W, H_q, d), dtype=torch.bfloat16)
+    Kt = torch.zeros((b, C_, H_kv, d), dtype=torch.bfloat16)
+    w = [torch.zeros((d_I, D), dtype=torch.bfloat16), torch.ones(d_I), torch.zeros((H_I, d_I, d), dtype=torch.bfloat16),
+         torch.ones(d_I), torch.zeros((H_I, D), dtype=torch.bfloat16)]
+    M, bv = torch.zeros((b, H_kv, d, d)), torch.zeros((b, H_kv, d))
+
+    def pool(rows, kdt=torch.bfloat16):
+        return dict(K=torch.zeros((b, H_kv, rows, d), dtype=kdt), V=torch.zeros((b, H_kv, rows, d), dtype=kdt),
+                    khat=torch.zeros((b, rows, d_I)), I=torch.zeros((b, rows)),
+                    pos=torch.zeros((b, rows), dtype=torch.int32))
+
+    call = lambda pl, K_=Kt, V_=Kt: api.kvm_index_evict_chunk(X, Q, K_, V_, *w, pl, P, 0, 32, 4, 0.99, 64, False,
+                                                              M, bv)
+    for bad in (pool(P + C_ + 64), pool(P + C_ - 1), pool(P + C_, torch.float32)):
+        with pytest.raises(ValueError):
+            call(bad)
+    with pytest.raises(ValueError):
+        call(pool(P + C_), K_=None)                    # only one of K, V
+    with pytest.raises(ValueError):
+        call(pool(P + C_), K_=Kt[:, :10].contiguous(), V_=Kt[:, :10].contiguous())
+
