@@ -505,6 +505,25 @@ kvm_status kvm_decode_attn_mem(const kvm_decode_desc* desc, const void* q, const
                                const float* s_k, const float* s_v, const float* S, float* o,
                                float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory or hand over a workspace: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * kvm_decode_attn_mem_noalloc takes the arguments of kvm_decode_attn_mem minus (ws,
+ * ws_bytes) and computes the same result with the same kernels; its split states live in a
+ * fixed device array of kvm_decode_noalloc_max_bytes() bytes (4 MiB) that the library holds
+ * on each GPU it runs on until the process ends.  It calls no allocator.  A shape whose
+ * split states need more than that (kvm_decode_workspace_size(desc) > the maximum) returns
+ * KVM_ERR_WORKSPACE before any HIP call.  Every call on one GPU uses that GPU's array, so
+ * calls that overlap in time on one GPU (two streams or two threads) race: the caller
+ * serialises them.  The array needs no clearing between calls: a call writes every word of
+ * it that it reads. */
+size_t kvm_decode_noalloc_max_bytes(void);
+kvm_status kvm_decode_attn_mem_noalloc(const kvm_decode_desc* desc, const void* q, const void* k_new,
+                                       const void* v_new, const int32_t* append_slot, void* Kc, void* Vc,
+                                       const int32_t* len, const float* M, const float* bvec,
+                                       const void* w_g, const void* q_mem, const int32_t* n_e,
+                                       const float* s_k, const float* s_v, const float* S, float* o,
+                                       float* lse, void* stream);
+
 /* ------------------------------------------------------------------------------------ *
  * N2  The read-out projection (slow weights)                                [IM 2.B]
  *

@@ -94,6 +94,9 @@ SIGNATURES = {
     "kvm_decode_workspace_size": (sz, [C.POINTER(DecodeDesc)]),
     "kvm_decode_attn_mem": (C.c_int, [C.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+    "kvm_decode_attn_mem_noalloc": (C.c_int, [C.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              vp, vp, vp, vp, vp, vp, vp, vp]),
+    "kvm_decode_noalloc_max_bytes": (sz, []),
     "kvm_mem_query": (C.c_int, [i32, i32, i32, vp, vp, vp, vp]),
     "kvm_chunk_keep": (i32, [C.POINTER(ChunkDesc)]),
     "kvm_chunk_workspace_size": (sz, [C.POINTER(ChunkDesc)]),

@@ -82,6 +82,26 @@ def kvm_decode_attn_mem(q, Kc, Vc, len_, k_new=None, v_new=None, append_slot=Non
     return o
 
 
+def kvm_decode_attn_mem_noalloc(q, Kc, Vc, len_, k_new=None, v_new=None, append_slot=None, M=None, bvec=None,
+                                w_g=None, moments=None, o=None, lse=None, n_split=0, scale=None, eps=1e-6,
+                                stream=None, q_mem=None):
+    """kvm_decode_attn_mem without a workspace: the split states live in the library's own
+    per-device scratch array (kvm_decode_noalloc_max_bytes()).  The library call allocates
+    nothing; pass `o` (and `lse`) to keep this wrapper from allocating either.  Calls that
+    overlap in time on one GPU race on that array."""
+    _contig(q, Kc, Vc, len_, k_new, v_new, append_slot, M, bvec, w_g, q_mem, o, lse)
+    mode = K.KVM_READ_MEMORY if M is not None else (K.KVM_READ_MOMENTS if moments is not None else K.KVM_READ_NONE)
+    desc = decode_desc(q, Kc, mode, n_split, scale, eps)
+    if o is None:
+        o = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    mo = moments or {}
+    check(lib().kvm_decode_attn_mem_noalloc(C.byref(desc), _p(q), _p(k_new), _p(v_new), _p(append_slot), _p(Kc),
+                                            _p(Vc), _p(len_), _p(M), _p(bvec), _p(w_g), _p(q_mem),
+                                            _p(mo.get("n_e")), _p(mo.get("s_k")), _p(mo.get("s_v")),
+                                            _p(mo.get("S")), _p(o), _p(lse), _stream(stream)))
+    return o
+
+
 def kvm_mem_query(q, W_m, q_mem=None, stream=None):
     """q_mem = W_m q per query row (q [..., d], W_m [d, d], same dtype): the projected query
     that the memory read-out addresses M with."""

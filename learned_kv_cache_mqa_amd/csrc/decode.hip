@@ -34,6 +34,8 @@
 // without touching memory, so no load sits behind a branch and each wait is for exactly the
 // tile being consumed.  K/V bytes are read once for all G heads.  Other shapes (fp32,
 // d = 64) use an FMA path.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace kvm {
@@ -831,6 +833,14 @@ extern "C" size_t kvm_decode_workspace_size(const kvm_decode_desc* d) {
   return decode_ws(d, auto_split(d)).total;
 }
 
+// Validation and launch shared by both decode entry points; ws == nullptr asks for the
+// library's own scratch array instead of a caller workspace.
+static kvm_status decode_entry(const kvm_decode_desc* d, const void* q, const void* k_new, const void* v_new,
+                               const int32_t* append_slot, void* Kc, void* Vc, const int32_t* len, const float* M,
+                               const float* bvec, const void* w_g, const void* q_mem, const int32_t* n_e,
+                               const float* s_k, const float* s_v, const float* S, float* o, float* lse, void* ws,
+                               size_t ws_bytes, bool own_scratch, void* stream);
+
 extern "C" kvm_status kvm_decode_attn_mem(const kvm_decode_desc* d, const void* q, const void* k_new,
                                           const void* v_new, const int32_t* append_slot, void* Kc,
                                           void* Vc, const int32_t* len, const float* M,
@@ -838,6 +848,57 @@ extern "C" kvm_status kvm_decode_attn_mem(const kvm_decode_desc* d, const void* 
                                           const int32_t* n_e, const float* s_k, const float* s_v,
                                           const float* S, float* o, float* lse, void* ws,
                                           size_t ws_bytes, void* stream) {
+  return decode_entry(d, q, k_new, v_new, append_slot, Kc, Vc, len, M, bvec, w_g, q_mem, n_e, s_k, s_v, S, o, lse,
+                      ws, ws_bytes, false, stream);
+}
+
+// ------------------------------------------------------------------ no-allocation variant
+// The split states of kvm_decode_attn_mem_noalloc live in one file-scope device array per GPU
+// (the runtime gives each device its own copy).  Host code never passes the array's name to a
+// kernel: that name is a host-side stand-in, not a device address.  The device address comes
+// from hipGetSymbolAddress, once per device, on the first call with that device current.
+// The decode writes every scratch word it reads within the same call, so nothing in the
+// array needs clearing between calls; calls that overlap on one GPU race on it.
+static constexpr size_t kDecodeScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char decode_scratch[kDecodeScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+static kvm_status decode_scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return check_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return set_error(KVM_ERR_ARCH, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(decode_scratch));
+    if (e != hipSuccess || p == nullptr) return check_hip(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                          "hipGetSymbolAddress(decode scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVM_OK;
+}
+
+extern "C" size_t kvm_decode_noalloc_max_bytes(void) { return kDecodeScratchBytes; }
+
+extern "C" kvm_status kvm_decode_attn_mem_noalloc(const kvm_decode_desc* d, const void* q, const void* k_new,
+                                                  const void* v_new, const int32_t* append_slot, void* Kc,
+                                                  void* Vc, const int32_t* len, const float* M,
+                                                  const float* bvec, const void* w_g, const void* q_mem,
+                                                  const int32_t* n_e, const float* s_k, const float* s_v,
+                                                  const float* S, float* o, float* lse, void* stream) {
+  return decode_entry(d, q, k_new, v_new, append_slot, Kc, Vc, len, M, bvec, w_g, q_mem, n_e, s_k, s_v, S, o, lse,
+                      nullptr, 0, true, stream);
+}
+
+static kvm_status decode_entry(const kvm_decode_desc* d, const void* q, const void* k_new, const void* v_new,
+                               const int32_t* append_slot, void* Kc, void* Vc, const int32_t* len, const float* M,
+                               const float* bvec, const void* w_g, const void* q_mem, const int32_t* n_e,
+                               const float* s_k, const float* s_v, const float* S, float* o, float* lse, void* ws,
+                               size_t ws_bytes, bool own_scratch, void* stream) {
   KVM_PTR(d);
   KVM_REQUIRE(d->b > 0 && d->H_q > 0 && d->H_kv > 0 && d->cap > 0, KVM_ERR_SHAPE,
               "b, H_q, H_kv and cap must be positive");
@@ -863,10 +924,21 @@ extern "C" kvm_status kvm_decode_attn_mem(const kvm_decode_desc* d, const void* 
   }
   const int ns = auto_split(d);
   const DecodeWs w = decode_ws(d, ns);
-  KVM_REQUIRE(ws != nullptr && ws_bytes >= w.total, KVM_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
-  KVM_ALIGNED(ws);
+  if (own_scratch) {
+    KVM_REQUIRE(w.total <= kDecodeScratchBytes, KVM_ERR_WORKSPACE,
+                "kvm_decode_attn_mem_noalloc: this shape needs %zu bytes of split states, above the %zu-byte "
+                "scratch array (use kvm_decode_attn_mem with a workspace, or fewer splits)",
+                w.total, kDecodeScratchBytes);
+  } else {
+    KVM_REQUIRE(ws != nullptr && ws_bytes >= w.total, KVM_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
+    KVM_ALIGNED(ws);
+  }
   kvm_status st = require_gfx950();
   if (st != KVM_OK) return st;
+  if (own_scratch) {
+    st = decode_scratch_ptr(&ws);
+    if (st != KVM_OK) return st;
+  }
 
   DecodeArgs a{};
   a.q = q; a.q_mem = q_mem ? q_mem : q; a.k_new = k_new; a.v_new = v_new; a.append_slot = append_slot;

@@ -259,3 +259,24 @@ def test_chunk_wrapper_rejects_mismatched_pool():
     with pytest.raises(ValueError):
         call(pool(P + C_), K_=Kt[:, :10].contiguous(), V_=Kt[:, :10].contiguous())
 
+
+def test_decode_noalloc_rejects_shapes_beyond_its_scratch(L):
+    """The no-allocation decode holds its split states in a fixed array; a shape that needs
+    more is refused before any HIP call, with a message naming the limit."""
+    from learned_kv_cache_mqa_amd import _lib as K
+    cap = int(L.kvm_decode_noalloc_max_bytes())
+    assert cap == 4 << 20
+
+    def call(**dk):
+        d = K.DecodeDesc(b=1, H_q=32, H_kv=8, d=128, cap=2176, n_split=0, dtype=K.KVM_BF16,
+                         mode=K.KVM_READ_MEMORY, scale=0.088, eps=1e-6)
+        for k, v in dk.items():
+            setattr(d, k, v)
+        ptr = [C.c_void_p(FAKE)] * 3 + [None] + [C.c_void_p(FAKE)] * 7 + [None] * 4 + [C.c_void_p(FAKE), None]
+        return L.kvm_decode_attn_mem_noalloc(C.byref(d), *ptr, None), L.kvm_decode_workspace_size(C.byref(d))
+
+    st, need = call(b=4, H_q=64, n_split=64)
+    assert need > cap and st == 6
+    assert b"scratch" in L.kvm_last_error()
+    st, need = call(d=96)
+    assert st == 2
