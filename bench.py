@@ -410,6 +410,183 @@ def time_rows(torch, api, KL, dev):
     return rows
 
 
+def source_sha16():
+    """Hash of the library sources, the header and this script (the GPU machine has no git)."""
+    import glob
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    files = sorted(glob.glob(os.path.join(root, "learned_kv_cache_mqa_amd", "csrc", "*")))
+    files += [os.path.join(root, "include", "kvm.h"), os.path.abspath(__file__)]
+    h = hashlib.sha256()
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_peaks(torch, dev):
+    """Achievable figures measured on this device, beside the datasheet peaks: a plain 1 GiB
+    device copy (read + write bytes over its time, best of 5) and a large bf16 GEMM through
+    torch.matmul (the vendor library; best of 5)."""
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    best = 1e9
+    for _ in range(6):
+        e0, e1 = ev(), ev()
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    copy_gbs = 2 * n / (best * 1e-3) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn((m, m), device=dev, dtype=torch.bfloat16)
+    y = torch.randn((m, m), device=dev, dtype=torch.bfloat16)
+    best = 1e9
+    for _ in range(6):
+        e0, e1 = ev(), ev()
+        e0.record()
+        torch.matmul(x, y)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    gemm_tfs = 2.0 * m ** 3 / (best * 1e-3) / 1e12
+    del x, y
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tfs, 1),
+            "how": "1 GiB device copy (2 x bytes / time) and an 8192^3 bf16 torch.matmul, best of 5 each"}
+
+
+def time_long_prefill(torch, api, dev):
+    """The 131072-token workload's one-shot index + evict (batch 1): indexer scores over the
+    whole prefill, the top 1024 plus a recent window of 64, compaction + memory build, and
+    the top-k of the 131072-token row on its own; mean of 5 after a warm-up."""
+    from synth import WORKLOADS
+    c4 = WORKLOADS["llama8b_layer_131k_stream"]
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(5_000_000)
+    rn = lambda *sh, std=1.0: (torch.randn(*sh, generator=g, device=dev) * std).to(bf)
+    X = torch.empty((1, c4.L, c4.D), dtype=bf, device=dev)
+    for r0 in range(0, c4.L, 16384):
+        X[0, r0:r0 + 16384] = rn(16384, c4.D)
+    Q, K4, V4 = rn(1, c4.W, c4.H_q, c4.d), rn(1, c4.L, c4.H_kv, c4.d), rn(1, c4.L, c4.H_kv, c4.d)
+    Wt = [rn(c4.d_I, c4.D, std=c4.D ** -0.5), torch.ones(c4.d_I, device=dev),
+          rn(c4.H_I, c4.d_I, c4.d, std=c4.d ** -0.5), torch.ones(c4.d_I, device=dev),
+          rn(c4.H_I, c4.D, std=c4.D ** -0.5)]
+    keep = api.kvm_topk_keep(c4.L, c4.B, c4.R, False)
+    cap = api.cache_cap(keep)
+    I = torch.empty((1, c4.L), device=dev)
+    idx = torch.empty((1, keep), dtype=torch.int32, device=dev)
+    sm = torch.empty((1, c4.L), dtype=torch.int32, device=dev)
+    Kc = torch.empty((1, c4.H_kv, cap, c4.d), dtype=bf, device=dev)
+    Vc = torch.empty((1, c4.H_kv, c4.d, cap), dtype=bf, device=dev)
+    M = torch.zeros((1, c4.H_kv, c4.d, c4.d), device=dev)
+    bv = torch.zeros((1, c4.H_kv, c4.d), device=dev)
+    lam = float(c4.lam)
+
+    def run():
+        api.kvm_index_score(X, Q, *Wt, I=I, eps=c4.eps_rms)
+        api.kvm_topk_select(I, c4.B, c4.R, False, idx=idx, slot_map=sm)
+        api.kvm_compact_kv(K4, V4, sm, idx, keep, cap, Kc=Kc, Vc=Vc, M=M, bvec=bv, lam=lam)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    ms = timed(run, 5)
+    topk_us = 1e3 * timed(lambda: api.kvm_topk_select(I, c4.B, c4.R, False, idx=idx, slot_map=sm), 20)
+    nbytes = prefill_bytes(c4, keep)
+    out = {"ms": round(ms, 4), "topk_us": round(topk_us, 2), "bytes": nbytes,
+           "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "workload": f"1 sequence, {c4.L}-token prefill, {c4.D} hidden, {c4.H_q}/{c4.H_kv} heads: indexer "
+                       f"scores ({c4.H_I}x{c4.d_I}, window {c4.W}), top {c4.B} + recent {c4.R} ({keep} slots), "
+                       f"compaction + memory build; bytes = X + K + V read once + kept rows written"}
+    del X, K4, V4
+    torch.cuda.empty_cache()
+    return out
+
+
+def time_momentkv_decode(torch, api, dev, steps=32):
+    """MomentKV decode at the Qwen3-4B shape (36 layers, batch 4, 32/8 heads, d 128) for each
+    budget: `steps` decode steps x 36 layers replayed from a HIP graph, each layer with its own
+    cache of B retained slots (plus the appended tokens) and its own moment sums; the step is
+    the attention over the retained cache with the NC mix.  tok/s = batch x steps / time."""
+    from synth import WORKLOADS
+    c5 = WORKLOADS["qwen3_4b_momentkv_32k"]
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(6_000_000)
+    rn = lambda *sh: torch.randn(*sh, generator=g, device=dev).to(bf)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    out = {}
+    pairs = c5.b * c5.H_kv
+    for B in c5.budgets:
+        cap = api.cache_cap(B + steps)
+        Ks = [rn(c5.b, c5.H_kv, cap, c5.d) for _ in range(c5.layers)]
+        Vs = [rn(c5.b, c5.H_kv, c5.d, cap) for _ in range(c5.layers)]
+        moms = [dict(n_e=torch.full((c5.b, c5.H_kv), c5.L - B, dtype=torch.int32, device=dev),
+                     s_k=torch.randn((c5.b, c5.H_kv, c5.d), generator=g, device=dev),
+                     s_v=torch.randn((c5.b, c5.H_kv, c5.d), generator=g, device=dev),
+                     S=torch.randn((c5.b, c5.H_kv, c5.d, c5.d), generator=g, device=dev))
+                for _ in range(c5.layers)]
+        qs = rn(steps, c5.layers, c5.b, c5.H_q, c5.d)
+        kn, vn = rn(steps, c5.layers, c5.b, c5.H_kv, c5.d), rn(steps, c5.layers, c5.b, c5.H_kv, c5.d)
+        lens = torch.full((c5.b,), B, dtype=torch.int32, device=dev)
+        o = torch.empty((c5.b, c5.H_q, c5.d), device=dev)
+        ws = torch.zeros(1 << 22, dtype=torch.uint8, device=dev)
+
+        def dsteps():
+            for t in range(steps):
+                for l in range(c5.layers):
+                    api.kvm_decode_attn_mem(qs[t, l], Ks[l], Vs[l], lens, k_new=kn[t, l], v_new=vn[t, l],
+                                            moments=moms[l], o=o, ws=ws)
+                api.kvm_len_add(lens, 1)
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            dsteps()
+            lens.fill_(B)
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=st):
+                dsteps()
+        torch.cuda.synchronize()
+        lens.fill_(B)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        with torch.cuda.stream(st):
+            e0.record(st)
+            gr.replay()
+            e1.record(st)
+        torch.cuda.synchronize()
+        t_ms = e0.elapsed_time(e1)
+        n_avg = B + (steps + 1) / 2.0
+        nbytes = (pairs * n_avg * c5.d * 2 * 2 + pairs * (c5.d * c5.d + 2 * c5.d + 1) * 4
+                  + c5.b * c5.H_q * c5.d * (2 + 4) + pairs * c5.d * 2 * 2 * 2) * c5.layers
+        launch_s = t_ms * 1e-3 / steps
+        out[f"B{B}"] = {"tok_s": round(c5.b * steps / (t_ms * 1e-3), 1),
+                        "layer_step_us": round(launch_s / c5.layers * 1e6, 2),
+                        "hbm_frac": round(nbytes / launch_s / 1e9 / HBM_PEAK_GBS, 4)}
+        del Ks, Vs, moms, gr
+        torch.cuda.empty_cache()
+    out["workload"] = (f"MomentKV decode, {c5.layers} layers, batch {c5.b}, {c5.H_q}/{c5.H_kv} heads, d {c5.d}, "
+                       f"retained B slots per KV head + appended tokens, {steps} steps from a HIP graph; bytes = "
+                       "K/V of the attended slots + S, s_k, s_v, n_e + q, o, new K/V")
+    return out
+
+
 def cpu_baseline(cfg, decode_steps):
     """The fp64 oracle on one (layer, sequence) of the workload: prefill index+evict and
     `decode_steps` decode steps, scaled to the workload's units."""
@@ -438,7 +615,47 @@ def cpu_baseline(cfg, decode_steps):
                 sample=f"1 layer x 1 sequence of the workload: prefill index+evict ({t_pre:.2f} s) and "
                        f"{decode_steps} decode steps ({t_dec * 1e3:.2f} ms each); decode tok/s = "
                        f"1/(32 layers x step time), sequences run one after another",
-                index_evict_ms=round(index_evict_ms, 1))
+                cpu_model=_cpu_model(),
+                index_evict_ms_estimate=round(index_evict_ms, 1),
+                index_evict_estimate_from=f"one layer x one sequence measured ({t_pre * 1e3:.1f} ms) x "
+                                          f"{cfg.layers} layers x {cfg.b} sequences",
+                single_thread_4k_layer=_oracle_4k_one_thread())
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _oracle_4k_one_thread(decode_steps=8):
+    """The oracle on the Llama-3.1-8B-shaped 4K layer (batch 1, budget 410) with one BLAS
+    thread: prefill index+evict and `decode_steps` decode steps, for a per-core figure."""
+    from threadpoolctl import threadpool_limits
+    from oracle import indexmem as im
+    from synth import WORKLOADS, gen
+    c2 = WORKLOADS["llama8b_layer_4k"].with_(needles=0)
+    p = gen.make_prefill(c2)
+    dec = gen.make_decode(c2, steps=decode_steps)
+    f = lambda x: gen.from_storage(x, c2.dtype)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        pre = im.prefill(f(p["X"][0]), f(p["Qwin"][0]), f(p["K"][0]), f(p["V"][0]), f(p["W_kI"]), p["gamma_k"],
+                         f(p["W_qI"]), p["gamma_q"], f(p["W_g"]), c2.B, c2.R, c2.lam, cap=c2.keep + decode_steps)
+        t_pre = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        im.decode(f(dec["q"][:, 0]), f(dec["k_new"][:, 0]), f(dec["v_new"][:, 0]), pre["Kc"], pre["Vc"], c2.keep,
+                  pre["M"], pre["b"], f(p["w_g"]))
+        t_dec = (time.perf_counter() - t0) / decode_steps
+    return {"threads": 1, "prefill_index_evict_ms": round(t_pre * 1e3, 1),
+            "decode_step_ms": round(t_dec * 1e3, 3),
+            "workload": f"{c2.L}-token layer, batch 1, {c2.H_q}/{c2.H_kv} heads, budget {c2.B} (recent {c2.R})"}
 
 
 def main():
@@ -576,9 +793,24 @@ def main():
         "decode_ms_per_step": round(dec_mean / T, 4),
         "roofline": roofline,
     }
+    peaks = measured_peaks(torch, dev)
+    roofline["measured_peak"] = peaks["hbm_copy_GBps"]
+    roofline["frac_of_measured"] = round(achieved / peaks["hbm_copy_GBps"], 4)
+    out["measured_peaks"] = peaks
+    out["index_evict_frac_of_measured_hbm"] = round(pbytes / (pre_mean / 1e3) / 1e9 / peaks["hbm_copy_GBps"], 4)
+    out["src_sha16"] = source_sha16()
+    out["seeds"] = "device torch.Generator: 3000000 + layer (stack inputs), 4000000 (rows), 5000000 (long prefill), " \
+                   "6000000 (MomentKV decode)"
     if not args.no_rows:
+        log("long prefill: 131072 tokens one-shot ...")
+        out["long_prefill_131k"] = time_long_prefill(torch, api, dev)
+        log("MomentKV decode per budget ...")
+        out["momentkv_decode"] = time_momentkv_decode(torch, api, dev)
         log("rows: streaming step and MomentKV timings ...")
         out["rows"] = time_rows(torch, api, KL, dev)
+        for k in ("N3_prefix_states", "V1_alpha"):
+            r = out["rows"]["roofline"][k]
+            r["frac_of_measured"] = round(r["achieved"] / peaks["bf16_gemm_TFLOPs"], 4)
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on one layer x one sequence ...")
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_decode_steps)
