@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define KVM_ABI_VERSION 2
+#define KVM_ABI_VERSION 3
 
 typedef enum {
   KVM_OK = 0,
@@ -119,8 +119,13 @@ typedef struct {
 } kvm_topk_desc;
 
 int32_t kvm_topk_keep(const kvm_topk_desc* desc);  /* keep = number of kept positions   */
+/* ws: NULL, or at least kvm_topk_workspace_size(desc) bytes of device memory (any contents).
+ * With a workspace, rows longer than 32768 positions are spread over many blocks (chunks of
+ * 4096 positions, six launches); without one, or for shorter rows, one block per row.  Both
+ * give the same result, bit for bit. */
+size_t kvm_topk_workspace_size(const kvm_topk_desc* desc);
 kvm_status kvm_topk_select(const kvm_topk_desc* desc, const float* I, int32_t* idx,
-                           int32_t* slot_map, void* stream);
+                           int32_t* slot_map, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------ *
  * A5 + A6 / V2  Compaction with a fused latent-memory or moment build  [IM 2.A, 2.B; MKV 1]

@@ -84,7 +84,8 @@ SIGNATURES = {
     "kvm_index_workspace_size": (sz, [C.POINTER(IndexDesc)]),
     "kvm_index_score": (C.c_int, [C.POINTER(IndexDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     "kvm_topk_keep": (i32, [C.POINTER(TopkDesc)]),
-    "kvm_topk_select": (C.c_int, [C.POINTER(TopkDesc), vp, vp, vp, vp]),
+    "kvm_topk_select": (C.c_int, [C.POINTER(TopkDesc), vp, vp, vp, vp, sz, vp]),
+    "kvm_topk_workspace_size": (sz, [C.POINTER(TopkDesc)]),
     "kvm_compact_workspace_size": (sz, [C.POINTER(CompactDesc)]),
     "kvm_compact_kv": (C.c_int, [C.POINTER(CompactDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  vp, sz, vp]),

@@ -125,8 +125,11 @@ def kvm_topk_keep(L, B, R=0, recent_inclusive=True, rows=1):
     return lib().kvm_topk_keep(C.byref(d))
 
 
-def kvm_topk_select(I, B, R=0, recent_inclusive=True, idx=None, slot_map=None, stream=None):
-    """I [rows, L] f32 -> (idx [rows, keep] i32 ascending, slot_map [rows, L] i32)."""
+def kvm_topk_select(I, B, R=0, recent_inclusive=True, idx=None, slot_map=None, stream=None, ws=None,
+                    one_block=False):
+    """I [rows, L] f32 -> (idx [rows, keep] i32 ascending, slot_map [rows, L] i32).  With the
+    workspace (the default) long rows spread over many blocks; one_block=True asks for one
+    block per row (no workspace).  Both give the same result."""
     _contig(I)
     if I.dim() == 1:
         I = I[None]
@@ -137,7 +140,14 @@ def kvm_topk_select(I, B, R=0, recent_inclusive=True, idx=None, slot_map=None, s
         idx = torch.empty((rows, max(keep, 0)), dtype=torch.int32, device=I.device)
     if slot_map is None:
         slot_map = torch.empty((rows, L), dtype=torch.int32, device=I.device)
-    check(lib().kvm_topk_select(C.byref(d), _p(I), _p(idx), _p(slot_map), _stream(stream)))
+    if one_block:
+        ws, nb = None, 0
+    else:
+        nb = lib().kvm_topk_workspace_size(C.byref(d))
+        if ws is None:
+            ws = workspace(nb, I.device, stream, "topk")
+        nb = ws.numel()
+    check(lib().kvm_topk_select(C.byref(d), _p(I), _p(idx), _p(slot_map), _p(ws), nb, _stream(stream)))
     return idx, slot_map
 
 

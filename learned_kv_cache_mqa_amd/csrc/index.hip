@@ -1002,7 +1002,7 @@ extern "C" kvm_status kvm_index_evict_chunk(const kvm_chunk_desc* d, const void*
   int32_t* ids = reinterpret_cast<int32_t*>(base + w.ids);
   int32_t* smap = reinterpret_cast<int32_t*>(base + w.smap);
   const kvm_topk_desc td{d->b, Lv, d->B, d->R, d->recent_inclusive};
-  st = kvm_topk_select(&td, I_p, ids, smap, stream);
+  st = kvm_topk_select(&td, I_p, ids, smap, nullptr, 0, stream);
   if (st != KVM_OK) return st;
   st = kvm_compact_kv(&cd, Kp, Vp, smap, ids, Kn, Vn, M, bvec, nullptr, nullptr, nullptr, nullptr,
                       base + w.comp, cbytes, stream);

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_strings(L):
-    assert L.kvm_abi_version() == 2
+    assert L.kvm_abi_version() == 3
     assert L.kvm_status_string(6) == b"workspace too small"
 
 
@@ -213,7 +213,7 @@ int main(void) {
   int st;
   printf("abi %d\n", (int)kvm_abi_version());
   printf("keep %d bad %d\n", (int)kvm_topk_keep(&d), (int)kvm_topk_keep(&bad));
-  st = (int)kvm_topk_select(NULL, NULL, NULL, NULL, NULL);
+  st = (int)kvm_topk_select(NULL, NULL, NULL, NULL, NULL, 0, NULL);
   printf("null %d %s\n", st, kvm_status_string(st));
   return 0;
 }
@@ -226,7 +226,7 @@ int main(void) {
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
     lines = r.stdout.split("\n")
-    assert lines[0] == "abi 2"
+    assert lines[0] == "abi 3"
     assert lines[1] == "keep 64 bad -1"
     assert lines[2].startswith("null 1 ")
 

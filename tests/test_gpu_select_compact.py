@@ -38,16 +38,29 @@ TOPK = [  # rows, L, B, R, inclusive, ties, specials
     (4, 3000, 3000, 0, True, 0, False),   # keep all
     (4, 3000, 7, 7, True, 0, False),      # recent window only
     (2, 1025, 1024, 64, False, 50, True),  # more slots than candidates
+    # rows longer than 32768 positions take the many-blocks-per-row path with a workspace
+    (3, 40000, 999, 13, True, 0, True),   # ragged last chunk, specials
+    (2, 36000, 36000, 0, True, 0, False),  # keep all
+    (2, 36000, 16, 16, True, 0, False),   # recent window only
+    (1, 40000, 4000, 64, False, 2, False),  # long runs of equal keys across chunk boundaries
+    (2, 50000, 300, 0, True, 0, False),   # scores spread over many binades (three levels)
 ]
 
 
 @pytest.mark.parametrize("rows,L,B,R,inc,ties,specials", TOPK)
-def test_topk_bit_exact(rows, L, B, R, inc, ties, specials):
+@pytest.mark.parametrize("one_block", [False, True], ids=["wide", "one_block"])
+def test_topk_bit_exact(rows, L, B, R, inc, ties, specials, one_block):
     import torch
     from learned_kv_cache_mqa_amd import api
     from tests.gpu_util import to_dev, to_np
     I = _scores(rows, L, seed=L + B, ties=ties, specials=specials)
-    idx, sm = api.kvm_topk_select(to_dev(I), B, R, inc)
+    if (L, B) == (50000, 300):
+        # magnitudes from 1e-30 to 1e30, both signs: a key span that needs three 12-bit levels
+        r = gen.rng(7, 2, 0, 0)
+        I = (np.sign(r.standard_normal((rows, L))) * 10.0 ** r.uniform(-30, 30, (rows, L))).astype(np.float32)
+    # a workspace holding garbage: the result must not depend on its contents
+    ws = torch.full((1 << 22,), 0x5a, dtype=torch.uint8, device="cuda")
+    idx, sm = api.kvm_topk_select(to_dev(I), B, R, inc, ws=None if one_block else ws, one_block=one_block)
     torch.cuda.synchronize()
     gi, gs = to_np(idx), to_np(sm)
     for r in range(rows):
