@@ -156,19 +156,15 @@ __device__ __forceinline__ void stage_tile(const CompactArgs& a, int pr, int db,
   }
 }
 
-#ifndef KVM_COMPACT_NB
-#define KVM_COMPACT_NB 2
-#endif
-#ifndef KVM_COMPACT_WPE
-#define KVM_COMPACT_WPE 2
-#endif
+constexpr int kCompactNB = 2;    // K/V tiles in flight per wave (register ring depth)
+constexpr int kCompactWPE = 2;   // waves per SIMD the kernel is compiled for
 // Contraction of the evicted rows of one chunk of positions of one (sequence, KV head):
 // grid (chunks, H_kv, b), 256 threads.  Raw K/V rows stream through a register ring NB tiles
 // deep; staged tiles alternate between two LDS buffers so that the staging of tile t + 1 (VALU)
 // overlaps the matrix-core work on tile t, with one barrier per tile.  Each wave owns a
 // 2 x 2 block of 32 x 32 output tiles (D = 128) or one tile (D = 64).
 template <int D, bool MEM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KVM_COMPACT_WPE, KVM_COMPACT_WPE)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kCompactWPE, kCompactWPE)))
 void compact_mfma_kernel(CompactArgs a) {
   static_assert(D == 64 || D == 128, "D");
   constexpr int NT = D / 32;               // 32x32 tiles per side
@@ -176,7 +172,7 @@ void compact_mfma_kernel(CompactArgs a) {
   constexpr int DB = D / 8;                // 8-dim blocks per row
   constexpr int PAIRS = (256 / DB) < (kTok / 2) ? (256 / DB) : (kTok / 2);
   static_assert(PAIRS == kTok / 2, "one pass of token pairs per tile");
-  constexpr int NB = KVM_COMPACT_NB;       // raw tiles in flight per thread
+  constexpr int NB = kCompactNB;       // raw tiles in flight per thread
   const int c = blockIdx.x, g = blockIdx.y, bb = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t pair = (size_t)bb * a.H_kv + g;
@@ -291,14 +287,6 @@ void compact_mfma_kernel(CompactArgs a) {
       stage_tile<D, MEM>(a, pr, db, loader, p0 + (t + 1) * kTok + 2 * pr, p1, rk[sn][0], rk[sn][1], rv[sn][0],
                          rv[sn][1], rs[sn][0], rs[sn][1], sV[nxt], sH[nxt], sL[nxt], vacc0, vacc1, nloc);
       fetch(sn, t + 1 + NB);
-#ifdef KVM_COMPACT_INTERLEAVE
-      // spread the matrix-core instructions over the staging arithmetic
-#pragma unroll
-      for (int i = 0; i < NTI * NTJ * 2 * (MEM ? 2 : 1); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, KVM_COMPACT_INTERLEAVE, 0);
-      }
-#endif
       __syncthreads();
     }
   }

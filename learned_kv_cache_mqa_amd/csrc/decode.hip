@@ -671,10 +671,7 @@ __device__ __forceinline__ void tile_pv(TileRegs& T, const f32x4_t (&sc)[2], int
 // cap; slots at or past the length are masked once it is known); the blocks' shares differ
 // by at most one chunk for any length; and 128-slot chunks keep every 128-byte line of a V
 // row (cap a multiple of 64) within one block.
-#ifndef KVM_DECODE_WPE
-#define KVM_DECODE_WPE 2
-#endif
-constexpr int WPE = KVM_DECODE_WPE;
+constexpr int WPE = 2;   // waves per SIMD: two 4-wave blocks per compute unit
 template <int G, bool PROJ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int D = 128, NW = 4, TILE = 32, STEP = NW * TILE;

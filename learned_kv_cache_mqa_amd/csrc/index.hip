@@ -82,19 +82,12 @@ __device__ __forceinline__ void keyproj_epilogue(f32x16_t acc0, f32x16_t acc1, f
 // Key projection launch shape: 16 waves x 32 tokens per block share each staged weight
 // chunk, so the weights' L2 traffic per token is a sixteenth of the X stream's; 4 waves per
 // SIMD with two k-steps of X in flight per wave.
-#ifndef KVM_KEYPROJ_WPE
-#define KVM_KEYPROJ_WPE 4
-#endif
-#ifndef KVM_KEYPROJ_XS
-#define KVM_KEYPROJ_XS 2
-#endif
-#ifndef KVM_KEYPROJ_NW
-#define KVM_KEYPROJ_NW 16
-#endif
-constexpr int kKpNW = KVM_KEYPROJ_NW;       // waves per block, 32 tokens each
+constexpr int kKpWPE = 4;                   // waves per SIMD
+constexpr int kKpXS = 2;                    // k-steps of X in flight per wave
+constexpr int kKpNW = 16;                   // waves per block, 32 tokens each
 constexpr int kKpTB = kKpNW * 32;           // tokens per block
-__global__ __launch_bounds__(kKpNW * 64) __attribute__((amdgpu_waves_per_eu(KVM_KEYPROJ_WPE, KVM_KEYPROJ_WPE))) void keyproj_mfma_kernel(IndexArgs a) {
-  constexpr int XS = KVM_KEYPROJ_XS;   // k-steps of X in flight per wave
+__global__ __launch_bounds__(kKpNW * 64) __attribute__((amdgpu_waves_per_eu(kKpWPE, kKpWPE))) void keyproj_mfma_kernel(IndexArgs a) {
+  constexpr int XS = kKpXS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bb = blockIdx.y;
   const int tb0 = blockIdx.x * kKpTB, t0 = tb0 + wave * 32;
@@ -207,15 +200,9 @@ __global__ __launch_bounds__(kKpNW * 64) __attribute__((amdgpu_waves_per_eu(KVM_
 //    and the weights come from an L2 that the X stream keeps busy) and writes each into the
 //    idle half of the LDS double buffer one step ahead of its use.
 // Barriers: every wave, producer or not, passes one after the prologue and one per k-step.
-#ifndef KVM_KPS_NW
-#define KVM_KPS_NW 4   // compute waves per block
-#endif
-#ifndef KVM_KPS_XS
-#define KVM_KPS_XS 8   // k-steps of X in flight per compute wave
-#endif
-#ifndef KVM_KPS_WD
-#define KVM_KPS_WD 4   // weight chunks in flight in the producer
-#endif
+constexpr int kKpsNW = 4;   // compute waves per block
+constexpr int kKpsXS = 8;   // k-steps of X in flight per compute wave
+constexpr int kKpsWD = 4;   // weight chunks in flight in the producer
 template <int NW, int XS, int WD>
 __global__ __launch_bounds__((NW + 1) * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void keyproj_stream_kernel(IndexArgs a) {
   constexpr int TB = NW * 32;   // tokens per block
@@ -721,11 +708,11 @@ static kvm_status index_launch(IndexArgs a, float* gate_ws, bool bf, const float
   // weights): wide models fall back to the wide-grid kernel
   if (mfma && ((long long)a.b * ((a.L + kKpTB - 1) / kKpTB) >= kFillBlocks || a.D > (1 << 20)))
     hipLaunchKernelGGL(keyproj_mfma_kernel, dim3((a.L + kKpTB - 1) / kKpTB, a.b), dim3(kKpNW * 64), 0, s, a);
-  else if (mfma && (long long)a.b * ((a.L + KVM_KPS_NW * 32 - 1) / (KVM_KPS_NW * 32)) >= kFillBlocks)
-    hipLaunchKernelGGL((keyproj_stream_kernel<KVM_KPS_NW, KVM_KPS_XS, KVM_KPS_WD>), dim3((a.L + KVM_KPS_NW * 32 - 1) / (KVM_KPS_NW * 32), a.b),
-                       dim3((KVM_KPS_NW + 1) * 64), 0, s, a);
+  else if (mfma && (long long)a.b * ((a.L + kKpsNW * 32 - 1) / (kKpsNW * 32)) >= kFillBlocks)
+    hipLaunchKernelGGL((keyproj_stream_kernel<kKpsNW, kKpsXS, kKpsWD>), dim3((a.L + kKpsNW * 32 - 1) / (kKpsNW * 32), a.b),
+                       dim3((kKpsNW + 1) * 64), 0, s, a);
   else if (mfma)   // smaller still (batch 1): 2 compute waves per block, twice the blocks
-    hipLaunchKernelGGL((keyproj_stream_kernel<2, KVM_KPS_XS, KVM_KPS_WD>), dim3((a.L + 63) / 64, a.b), dim3(3 * 64), 0, s, a);
+    hipLaunchKernelGGL((keyproj_stream_kernel<2, kKpsXS, kKpsWD>), dim3((a.L + 63) / 64, a.b), dim3(3 * 64), 0, s, a);
   else if (bf)
     hipLaunchKernelGGL(keyproj_valu_kernel<uint16_t>, dim3((a.L + 15) / 16, a.b), dim3(256), 0, s, a);
   else
