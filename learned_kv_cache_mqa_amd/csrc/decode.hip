@@ -770,12 +770,17 @@ __global__ void len_add_kernel(int32_t* len, int b, int delta) {
 // attention blocks per compute unit (256 on this part).  A grid that overfills the round
 // leaves a second, partial round; one that does not divide evenly leaves some units with
 // twice the work of others -- both measured 15-30% slower than a full, even round.
+// Without a read-out each block should hold at least one 128-slot chunk.  With one, up to 8
+// splits even for short caches: the blocks also share the D read-out rows of M (or S), and
+// one block reading a whole 64 KB matrix in passes of 16 rows is the longest chain of a
+// short cache's step (measured, MomentKV batch 4, 36 layers: B = 128 13.4 -> 8.9 us per
+// layer-step, B = 256 12.3 -> 9.3 us; 16 splits were slower than 8).
 static int auto_split(const kvm_decode_desc* d) {
   if (d->n_split > 0) return d->n_split;
   constexpr int kBlockSlots = 2 * 256;
   const int pairs = d->b * d->H_kv;
   int s = std::max(1, kBlockSlots / pairs);
-  s = std::min(s, std::max(1, d->cap / 128));   // at least one 128-slot chunk per block
+  s = std::min(s, std::max(d->mode != KVM_READ_NONE ? 8 : 1, d->cap / 128));
   return std::min(s, 64);
 }
 
