@@ -77,6 +77,21 @@ struct Span {
   int n, app, j0, j1;
 };
 
+// The kernel arguments a kernel's first loads depend on, forced into scalar registers at one
+// point: their scalar loads then go out in one round.  Left to itself the compiler issues them
+// in two or three dependent rounds (a batch, a wait, the next batch), each a full
+// kernel-argument latency ahead of the first data load.
+__device__ __forceinline__ void args_early(const DecodeArgs& a) {
+  asm volatile("" ::"s"(a.q), "s"(a.k_new), "s"(a.v_new), "s"(a.append_slot), "s"(a.Kc), "s"(a.Vc), "s"(a.len),
+               "s"(a.rmat), "s"(a.b), "s"(a.H_q), "s"(a.H_kv), "s"(a.cap), "s"(a.n_split), "s"(a.mode));
+}
+__device__ __forceinline__ void args_merge(const DecodeArgs& a) {
+  asm volatile("" ::"s"(a.q), "s"(a.k_new), "s"(a.v_new), "s"(a.append_slot), "s"(a.len), "s"(a.bvec), "s"(a.w_g),
+               "s"(a.n_e), "s"(a.s_k), "s"(a.s_v), "s"(a.o), "s"(a.lse), "s"(a.part_a), "s"(a.part_lse), "s"(a.num),
+               "s"(a.q_mem), "s"(a.H_q), "s"(a.H_kv), "s"(a.cap), "s"(a.n_split), "s"(a.mode), "s"(a.scale),
+               "s"(a.eps));
+}
+
 // The sequence's cache length and append slot (read once, early: their latency overlaps
 // the loads that do not depend on them).
 struct SeqLen {
@@ -300,17 +315,25 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int rb = blockIdx.x, g = blockIdx.y, bb = blockIdx.z;
   const int h = threadIdx.x >> 5, l32 = threadIdx.x & 31, dd = rb * 32 + l32;
   if (h >= G) return;
+  args_merge(a);
   const size_t pair = (size_t)bb * a.H_kv + g;
   const SeqLen sl = seq_len(a, bb);
   const float* pl = a.part_lse + pair * a.n_split * G + h;
   const float* pa = a.part_a + pair * a.n_split * (size_t)(G * D) + (size_t)h * D + dd;
   const T* qh = reinterpret_cast<const T*>(a.q) + ((size_t)bb * a.H_q + (size_t)g * G + h) * D + l32 * E;
   const bool mem = a.mode == KVM_READ_MEMORY, mom = a.mode == KVM_READ_MOMENTS;
+  // the first 8 block states through buffers sized to n_split: states past it read zeros
+  // (lse replaced by -inf below), so these loads sit behind no branch
   float lv[8], av[8];
+  {
+    const int n8 = min(a.n_split, 8);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.part_lse + pair * a.n_split * G, n8 * G * 4);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.part_a + pair * a.n_split * (size_t)(G * D), n8 * G * D * 4);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    lv[e] = e < a.n_split ? pl[e * G] : -INFINITY;
-    av[e] = e < a.n_split ? pa[(size_t)e * G * D] : 0.f;
+    for (int e = 0; e < 8; ++e) {
+      lv[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (e * G + h) * 4, 0, 0));
+      av[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ra, ((e * G + h) * D + dd) * 4, 0, 0));
+    }
   }
   // optional inputs through buffers of size 0 when absent (their loads read zeros), so no
   // load sits behind a branch
@@ -342,6 +365,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const float sv = buffer_elem<float>(rs, dd * 4);
   const int ne = (int)__builtin_amdgcn_raw_buffer_load_b32(re, 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e >= a.n_split) lv[e] = -INFINITY;
   // online merge of the block states in chunk order, 8 at a time
   float mx = -INFINITY, z = 0.f, acc = 0.f;
   for (int c0 = 0; c0 < a.n_split; c0 += 8) {
@@ -684,6 +710,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   __shared__ float s_m[NW][G], s_l[NW][G];
   __shared__ float s_acc[NW][G][D];
 
+  args_early(a);
   const size_t pair = (size_t)bb * a.H_kv + g;
   // q and the read-out operands do not depend on the sequence length: their loads go out
   // while the length is still being read
