@@ -63,6 +63,11 @@ CASES = [
     ("f32", 1, 1, 1, 64, 80, [64], 0),
     ("f32", 1, 1, 1, 64, 80, [79], 4),
     ("f32", 2, 8, 2, 128, 96, [33, 60], 2),
+    # the 16K workload's 64 (sequence, KV head) pairs with ragged lengths; one split per pair
+    ("bf16", 8, 32, 8, 128, 704, [410, 666, 1, 703, 64, 500, 0, 333], 0),
+    ("bf16", 1, 64, 8, 128, 2176, [2100], 1),
+    ("bf16", 2, 8, 8, 128, 304, [0, 303], 1),
+    ("bf16", 3, 16, 8, 128, 64, [1, 63, 32], 1),
 ]
 
 
@@ -180,7 +185,28 @@ def _sweep_cases(n=40):
     return out
 
 
-@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"sweep{c[0]}-{c[1]}-d{c[2]}-G{c[3]}-{c[7]}-{c[10]}")
+def _pair_cases(n=24):
+    """Seeded bf16, d = 128 configurations at the matrix-core path's two extremes: one split
+    per (sequence, KV head) (n_split = 1), and the automatic split at 64-80 pairs (the 16K
+    workload's batch); every group size, append mode and read-out."""
+    r = np.random.default_rng(20261204)
+    out = []
+    for i in range(n):
+        G = int(r.choice([1, 2, 4, 8]))
+        auto = i % 2 == 0
+        H_kv = 8 if auto else int(r.choice([1, 2, 4, 8]))
+        b = int(r.integers(8, 11)) if auto else int(r.integers(1, 4))
+        cap = 8 * int(r.integers(1, 90)) if r.random() < 0.6 else 64 * int(r.integers(1, 36))
+        mode = ["none", "append", "slot"][int(r.integers(0, 3))]
+        lens = [int(r.integers(1, cap + 1)) for _ in range(b)]
+        slots = [int(r.integers(0, cap)) for _ in range(b)]
+        readout = ["none", "memory", "moments"][int(r.integers(0, 3))]
+        out.append((100 + i, "bf16", 128, G, H_kv, b, cap, mode, lens, slots, readout, 0 if auto else 1))
+    return out
+
+
+@pytest.mark.parametrize("case", _sweep_cases() + _pair_cases(),
+                         ids=lambda c: f"sweep{c[0]}-{c[1]}-d{c[2]}-G{c[3]}-{c[7]}-{c[10]}")
 def test_decode_random_sweep(case):
     import torch
     from oracle import momentkv as mk
@@ -253,6 +279,8 @@ PROJ_CASES = [
     ("bf16", 2, 32, 8, 128, 704, [410, 666], 0),     # matrix-core path
     ("bf16", 1, 16, 2, 64, 200, [150], 3),           # d 64, group of 8
     ("f32", 2, 8, 2, 128, 96, [33, 60], 2),          # FMA path
+    ("bf16", 8, 32, 8, 128, 704, [410, 666, 1, 703, 64, 500, 7, 333], 0),   # 64 pairs
+    ("bf16", 1, 64, 8, 128, 304, [300], 1),          # one split, group of 8
 ]
 
 

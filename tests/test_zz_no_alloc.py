@@ -43,8 +43,10 @@ def _run(c, lens, noalloc):
 
 def test_noalloc_decode_matches_workspace_decode():
     r = gen.rng(97, 1, 0, 0)
-    # the 16K workload's decode shape, then a smaller one (fewer sequences, shorter caches)
-    shapes = [(8, 32, 8, 128, 2176, [1894 - 7 * i for i in range(8)]), (2, 32, 8, 128, 704, [410, 333])]
+    # the 16K workload's decode shape, then a smaller one (fewer sequences, shorter caches),
+    # then a mid-sized one (more splits per pair than the first)
+    shapes = [(8, 32, 8, 128, 2176, [1894 - 7 * i for i in range(8)]), (2, 32, 8, 128, 704, [410, 333]),
+              (4, 32, 8, 128, 2176, [1894 - 7 * i for i in range(4)])]
     for n, (b, H_q, H_kv, d, cap, lens) in enumerate(shapes):
         c = _inputs(r, b, H_q, H_kv, d, cap)
         got = _run(c, lens, True)
