@@ -219,6 +219,168 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
 }
 
+// ------------------------------------------------------------------ rows held in registers
+// Rows of at most 1024 R positions: every thread loads its R scores once, as keys, and all
+// passes work from registers.  Element j of lane l in wave w is position w 64 R + 64 j + l,
+// so a wave's positions are contiguous (the layout the final ranking needs).  The two
+// histograms alternate (the next pass's buffer is cleared while the current one is
+// scanned), so a pass costs three block barriers, and the final ranking takes the counts of
+// keys above T and equal to T in one block-wide exchange: the equal keys taken before a wave
+// are min(equal keys before it, k).  Same keys, bins and order rule as topk_kernel, so the
+// result is the same, bit for bit, with a third of the barriers (measured per 16384-position
+// row: ~22 barrier-separated phases of 1-2 us each in topk_kernel).
+template <int R>
+__global__ __launch_bounds__(kTopkThreads) void topk_reg_kernel(const float* __restrict__ I, int32_t* __restrict__ idx,
+                                                              int32_t* __restrict__ slot_map, int L, int n_cand,
+                                                              int n_top, int keep) {
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* sm = slot_map + (size_t)row * L;
+  int32_t* ix = idx + (size_t)row * keep;
+  __shared__ int s_hist[2][4096];
+  __shared__ uint32_t s_mm[2 * kTopkWaves];
+  __shared__ int s_wt[2 * kTopkWaves];
+  __shared__ uint32_t s_sel[2];
+
+  // scores of the candidates (positions < n_cand); loads past them read zeros
+  const __amdgpu_buffer_rsrc_t rI = make_rsrc(I + (size_t)row * L, n_cand * 4);
+  const int p0 = wave * 64 * R + lane;
+  uint32_t key[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+    key[j] = order_key(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rI, (uint32_t)(p0 + 64 * j) * 4u, 0, 0)));
+  const bool all = n_top >= n_cand;
+  uint32_t T = 0;
+  int k = n_top;
+  if (n_top > 0 && !all) {
+    for (int i = tid; i < 2 * 4096; i += kTopkThreads) (&s_hist[0][0])[i] = 0;
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (p0 + 64 * j < n_cand) {
+        kmin = min(kmin, key[j]);
+        kmax = max(kmax, key[j]);
+      }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+    }
+    if (lane == 0) { s_mm[wave] = kmin; s_mm[kTopkWaves + wave] = kmax; }
+    __syncthreads();   // also orders the histogram clear before the first pass
+    kmin = s_mm[0];
+    kmax = s_mm[kTopkWaves];
+#pragma unroll
+    for (int w = 1; w < kTopkWaves; ++w) { kmin = min(kmin, s_mm[w]); kmax = max(kmax, s_mm[kTopkWaves + w]); }
+    // the interval [lo, lo + 2^width) holds every key still in play
+    uint32_t lo = kmin;
+    const uint32_t span = kmax - kmin;
+    int width = span ? 32 - __clz(span) : 0;
+    int buf = 0;
+    while (width > 0) {
+      const int dbits = width < 12 ? width : 12;
+      const int shift = width - dbits, nb = 1 << dbits;
+      int* h = s_hist[buf];
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const uint32_t rel = key[j] - lo;   // wraps below lo: out of range
+        if (p0 + 64 * j < n_cand && ((uint64_t)rel >> width) == 0) atomicAdd(&h[rel >> shift], 1);
+      }
+      __syncthreads();
+      // thread i owns the bins nb-1-4i .. nb-4-4i (descending); scan their counts
+      int c[4], sum = 0;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int bin = nb - 1 - 4 * tid - jj;
+        c[jj] = bin >= 0 ? h[bin] : 0;
+        sum += c[jj];
+      }
+      // the other buffer was last read before the previous pass's final barrier: clear it for
+      // the next pass
+      int* ho = s_hist[buf ^ 1];
+      for (int i = tid; i < 4096; i += kTopkThreads) ho[i] = 0;
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      if (lane == 63) s_wt[wave] = incl;
+      __syncthreads();
+      int excl = incl - sum;
+#pragma unroll
+      for (int w = 0; w < kTopkWaves; ++w) excl += w < wave ? s_wt[w] : 0;
+      if (excl < k && excl + sum >= k) {
+        int run = excl;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          if (run + c[jj] >= k) {
+            s_sel[0] = (uint32_t)(nb - 1 - 4 * tid - jj);
+            s_sel[1] = (uint32_t)(k - run);
+            break;
+          }
+          run += c[jj];
+        }
+      }
+      __syncthreads();
+      lo += s_sel[0] << shift;
+      k = (int)s_sel[1];
+      width = shift;
+      buf ^= 1;
+    }
+    T = lo;
+  }
+  // ranking: selected positions get slots in position order; keys equal to T are taken
+  // in position order while fewer than k of them are
+  const uint64_t below = lanes_below();
+  uint64_t gtm[R], eqm[R];
+  int gt_w = 0, eq_w = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int p = p0 + 64 * j;
+    bool sel = false, eq = false;
+    if (p < L) {
+      if (p >= n_cand || all) {
+        sel = true;
+      } else if (n_top > 0) {
+        sel = key[j] > T;
+        eq = key[j] == T;
+      }
+    }
+    gtm[j] = __ballot(sel);
+    eqm[j] = __ballot(eq);
+    gt_w += __popcll(gtm[j]);
+    eq_w += __popcll(eqm[j]);
+  }
+  if (lane == 0) { s_wt[wave] = gt_w; s_wt[kTopkWaves + wave] = eq_w; }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    gt_before += w < wave ? s_wt[w] : 0;
+    eq_before += w < wave ? s_wt[kTopkWaves + w] : 0;
+  }
+  int eq_rank = eq_before;
+  int slot0 = gt_before + min(eq_before, max(k, 0));
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const bool take = ((eqm[j] >> lane) & 1ull) && eq_rank + __popcll(eqm[j] & below) < k;
+    eq_rank += __popcll(eqm[j]);
+    const uint64_t selm = gtm[j] | __ballot(take);
+    const int p = p0 + 64 * j;
+    const int slot = slot0 + __popcll(selm & below);
+    if (p < L) {
+      if ((selm >> lane) & 1ull) {
+        sm[p] = slot;
+        if (slot < keep) ix[slot] = p;
+      } else {
+        sm[p] = -(p - slot + 1);
+      }
+    }
+    slot0 += __popcll(selm);
+  }
+}
+
 // ------------------------------------------------------------------ wide rows
 // Many blocks per row (a workspace is given): each row is cut into chunks of kWChunk
 // positions, one block per (chunk, row), and the select runs as a fixed sequence of
@@ -623,6 +785,16 @@ extern "C" kvm_status kvm_topk_select(const kvm_topk_desc* d, const float* I, in
   kvm_status st = require_gfx950();
   if (st != KVM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->L <= kTopkThreads * 4) {
+    hipLaunchKernelGGL(topk_reg_kernel<4>, dim3(d->rows), dim3(kTopkThreads), 0, s, I, idx, slot_map, d->L, n_cand,
+                       n_top, keep);
+    return check_hip(hipGetLastError(), "topk_reg_kernel launch");
+  }
+  if (d->L <= kTopkThreads * 16) {
+    hipLaunchKernelGGL(topk_reg_kernel<16>, dim3(d->rows), dim3(kTopkThreads), 0, s, I, idx, slot_map, d->L, n_cand,
+                       n_top, keep);
+    return check_hip(hipGetLastError(), "topk_reg_kernel launch");
+  }
   if (!ws || d->L < kWideMinL) {
     hipLaunchKernelGGL(topk_kernel, dim3(d->rows), dim3(kTopkThreads), 0, s, I, idx, slot_map, d->L, n_cand, n_top,
                        keep);
