@@ -435,29 +435,57 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(GatherArgs a) {
   const T* Vb = reinterpret_cast<const T*>(a.V) + bb * a.batch_stride + g * a.head_stride;
   T* Kcb = reinterpret_cast<T*>(a.Kc) + (pair * a.cap + s0) * D;
   T* Vcb = reinterpret_cast<T*>(a.Vc) + pair * a.cap * D + s0;
-  for (int i = tid; i < ns * C16; i += 256) {
-    const int sl = i / C16, cc = i % C16;
-    const int t = sPos[sl];
-    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+  // every load of the thread first, then the stores: in one loop each iteration's loads
+  // would wait for the previous iteration's stores (the compiler cannot rule out aliasing)
+  constexpr int IT = (64 * C16 + 255) / 256;   // 16-byte pieces per thread
+  uint4 kv[IT], vv[IT];
+#pragma unroll
+  for (int r = 0; r < IT; ++r) {
+    const int i = tid + r * 256;
+    kv[r] = vv[r] = make_uint4(0, 0, 0, 0);
+    const int t = i < ns * C16 ? sPos[i / C16] : -1;
     if (t >= 0) {
-      kv = *reinterpret_cast<const uint4*>(Kb + t * a.tok_stride + cc * E16);
-      vv = *reinterpret_cast<const uint4*>(Vb + t * a.tok_stride + cc * E16);
+      kv[r] = *reinterpret_cast<const uint4*>(Kb + t * a.tok_stride + (i % C16) * E16);
+      vv[r] = *reinterpret_cast<const uint4*>(Vb + t * a.tok_stride + (i % C16) * E16);
     }
-    *reinterpret_cast<uint4*>(Kcb + (size_t)sl * D + cc * E16) = kv;
+  }
+#pragma unroll
+  for (int r = 0; r < IT; ++r) {
+    const int i = tid + r * 256;
+    if (i >= ns * C16) continue;
+    const int sl = i / C16, cc = i % C16;
+    *reinterpret_cast<uint4*>(Kcb + (size_t)sl * D + cc * E16) = kv[r];
     if (a.v_row_major) {   // Vc [b, H_kv, cap, d]
-      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.Vc) + (pair * a.cap + s0 + sl) * D + cc * E16) = vv;
+      *reinterpret_cast<uint4*>(reinterpret_cast<T*>(a.Vc) + (pair * a.cap + s0 + sl) * D + cc * E16) = vv[r];
       continue;
     }
     T ve[E16];
-    __builtin_memcpy(ve, &vv, 16);
+    __builtin_memcpy(ve, &vv[r], 16);
 #pragma unroll
     for (int e = 0; e < E16; ++e) sVt[(cc * E16 + e) * SP + sl] = ve[e];
   }
   if (a.v_row_major) return;   // block-uniform
   __syncthreads();
-  for (int i = tid; i < D * 64; i += 256) {
-    const int dim = i / 64, sl = i % 64;
-    if (sl < ns) Vcb[(size_t)dim * a.cap + sl] = sVt[dim * SP + sl];
+  // dim-major rows out in 16-byte pieces of E16 consecutive slots, aligned when cap is a
+  // multiple of E16 (s0 is a multiple of 64); otherwise, and for a piece past the block's last
+  // slot, element by element
+  constexpr int PPR = 64 / E16;   // pieces per dim row
+  const bool vec = a.cap % E16 == 0;
+  for (int i = tid; i < D * PPR; i += 256) {
+    const int dim = i / PPR, sl = (i % PPR) * E16;
+    if (sl >= ns) continue;
+    T ve[E16];
+#pragma unroll
+    for (int e = 0; e < E16; ++e) ve[e] = sVt[dim * SP + sl + e];
+    if (vec && sl + E16 <= ns) {
+      uint4 w;
+      __builtin_memcpy(&w, ve, 16);
+      *reinterpret_cast<uint4*>(Vcb + (size_t)dim * a.cap + sl) = w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < E16; ++e)
+        if (sl + e < ns) Vcb[(size_t)dim * a.cap + sl + e] = ve[e];
+    }
   }
 }
 
