@@ -44,6 +44,14 @@ TOPK = [  # rows, L, B, R, inclusive, ties, specials
     (2, 36000, 16, 16, True, 0, False),   # recent window only
     (1, 40000, 4000, 64, False, 2, False),  # long runs of equal keys across chunk boundaries
     (2, 50000, 300, 0, True, 0, False),   # scores spread over many binades (three levels)
+    # the register-resident path's boundaries (rows of at most 4096 / 16384 positions) and the
+    # one-block path just past them
+    (2, 4097, 400, 16, True, 5, True),
+    (1, 16385, 1600, 32, True, 0, True),
+    (4, 4096, 4000, 0, True, 2, False),   # nearly everything kept, ties
+    (2, 16384, 16000, 100, False, 7, True),
+    (3, 16384, 1, 0, True, 0, False),     # k = 1
+    (2, 12000, 300, 0, True, 0, False),   # many binades in registers (three levels)
 ]
 
 
@@ -54,7 +62,7 @@ def test_topk_bit_exact(rows, L, B, R, inc, ties, specials, one_block):
     from learned_kv_cache_mqa_amd import api
     from tests.gpu_util import to_dev, to_np
     I = _scores(rows, L, seed=L + B, ties=ties, specials=specials)
-    if (L, B) == (50000, 300):
+    if (L, B) in ((50000, 300), (12000, 300)):
         # magnitudes from 1e-30 to 1e30, both signs: a key span that needs three 12-bit levels
         r = gen.rng(7, 2, 0, 0)
         I = (np.sign(r.standard_normal((rows, L))) * 10.0 ** r.uniform(-30, 30, (rows, L))).astype(np.float32)
@@ -67,6 +75,25 @@ def test_topk_bit_exact(rows, L, B, R, inc, ties, specials, one_block):
         ri, rs = im.topk_select(I[r].astype(np.float64), B, R, inc)
         assert gi[r].tolist() == ri.tolist(), f"row {r}"
         assert gs[r].tolist() == rs.tolist(), f"row {r}"
+
+
+@pytest.mark.parametrize("L", [100, 4096, 16384, 20000, 40000])
+@pytest.mark.parametrize("value", [1.0, -np.inf, np.nan])
+def test_topk_all_scores_equal(L, value):
+    """Every candidate key equal (a zero key span: no histogram pass): the kept ones are the
+    lowest positions, on every path (registers, one block, many blocks)."""
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from tests.gpu_util import to_dev, to_np
+    I = np.full((2, L), value, np.float32)
+    ws = torch.full((1 << 22,), 0x5a, dtype=torch.uint8, device="cuda")
+    for one_block in (False, True):
+        idx, sm = api.kvm_topk_select(to_dev(I), 50, 3, True, ws=None if one_block else ws, one_block=one_block)
+        torch.cuda.synchronize()
+        gi, gs = to_np(idx), to_np(sm)
+        for r in range(2):
+            ri, rs = im.topk_select(I[r].astype(np.float64), 50, 3, True)
+            assert gi[r].tolist() == ri.tolist() and gs[r].tolist() == rs.tolist(), (one_block, r)
 
 
 def _kv(dtype, b, L, H, d, seed):
