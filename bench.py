@@ -595,22 +595,24 @@ def cpu_baseline(cfg, decode_steps):
     from oracle import indexmem as im
     from synth import gen
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    one = cfg.with_(b=1, needles=0)
+    one = cfg.with_(b=1)   # sequence 0 of layer 0, with the workload's planted needles
     p = gen.make_prefill(one, layer=0)
     f = lambda x: gen.from_storage(x, one.dtype)
     X, Q, K, V = f(p["X"][0]), f(p["Qwin"][0]), f(p["K"][0]), f(p["V"][0])
     Wk, Wq, Wg, wg = f(p["W_kI"]), f(p["W_qI"]), f(p["W_g"]), f(p["w_g"])
     t0 = time.perf_counter()
-    pre = im.prefill(X, Q, K, V, Wk, p["gamma_k"], Wq, p["gamma_q"], Wg, cfg.B, cfg.R, cfg.lam,
+    lam = float(np.float32(cfg.lam))   # the value the library takes (fp32)
+    pre = im.prefill(X, Q, K, V, Wk, p["gamma_k"], Wq, p["gamma_q"], Wg, cfg.B, cfg.R, lam,
                      cap=cfg.keep + decode_steps)
     t_pre = time.perf_counter() - t0
     dec = gen.make_decode(one, layer=0, steps=decode_steps)
     t0 = time.perf_counter()
-    im.decode(f(dec["q"][:, 0]), f(dec["k_new"][:, 0]), f(dec["v_new"][:, 0]), pre["Kc"], pre["Vc"], cfg.keep,
-              pre["M"], pre["b"], wg)
+    o_ref, _, _, _ = im.decode(f(dec["q"][:, 0]), f(dec["k_new"][:, 0]), f(dec["v_new"][:, 0]), pre["Kc"],
+                               pre["Vc"], cfg.keep, pre["M"], pre["b"], wg)
     t_dec = (time.perf_counter() - t0) / decode_steps
     index_evict_ms = t_pre * cfg.layers * cfg.b * 1e3
     tok_s = 1.0 / (t_dec * cfg.layers)
+    parity = _sample_parity(one, p, pre, dec, o_ref)
     return dict(value=round(tok_s, 3), unit="tok/s", cores=threads, kind="oracle",
                 sample=f"1 layer x 1 sequence of the workload: prefill index+evict ({t_pre:.2f} s) and "
                        f"{decode_steps} decode steps ({t_dec * 1e3:.2f} ms each); decode tok/s = "
@@ -619,7 +621,76 @@ def cpu_baseline(cfg, decode_steps):
                 index_evict_ms_estimate=round(index_evict_ms, 1),
                 index_evict_estimate_from=f"one layer x one sequence measured ({t_pre * 1e3:.1f} ms) x "
                                           f"{cfg.layers} layers x {cfg.b} sequences",
-                single_thread_4k_layer=_oracle_4k_one_thread())
+                single_thread_4k_layer=_oracle_4k_one_thread(),
+                parity_sample=parity)
+
+
+def _sample_parity(one, p, pre, dec, o_ref):
+    """The GPU path (index, top-k, compaction with the memory fold, then the decode steps over
+    its own caches) on the oracle's sample, compared as the tests compare it: parity
+    statistics and needle recall for the record (the tests hold the bars)."""
+    import numpy as np
+    import torch
+    from learned_kv_cache_mqa_amd import api
+    from oracle import indexmem as im
+    dev = torch.device("cuda", 0)
+
+    def up(a):   # storage array (uint16 holds bf16 bits) -> device tensor
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    I = api.kvm_index_score(up(p["X"]), up(p["Qwin"]), up(p["W_kI"]), up(p["gamma_k"]), up(p["W_qI"]),
+                            up(p["gamma_q"]), up(p["W_g"]), eps=one.eps_rms)
+    idx, sm = api.kvm_topk_select(I, one.B, one.R, one.recent_inclusive)
+    keep = idx.shape[1]
+    T = dec["q"].shape[0]
+    cap = api.cache_cap(keep + T)
+    M = torch.zeros((1, one.H_kv, one.d, one.d), device=dev)
+    bv = torch.zeros((1, one.H_kv, one.d), device=dev)
+    Kc, Vc = api.kvm_compact_kv(up(p["K"]), up(p["V"]), sm, idx, keep, cap, M=M, bvec=bv,
+                                lam=float(np.float32(one.lam)))
+    lens = torch.full((1,), keep, dtype=torch.int32, device=dev)
+    outs = []
+    for t in range(T):
+        outs.append(api.kvm_decode_attn_mem(up(dec["q"][t]), Kc, Vc, lens, k_new=up(dec["k_new"][t]),
+                                            v_new=up(dec["v_new"][t]), M=M, bvec=bv, w_g=up(p["w_g"])))
+        api.kvm_len_add(lens, 1)
+    torch.cuda.synchronize()
+    gI, gidx = I.cpu().numpy()[0].astype(np.float64), idx.cpu().numpy()[0]
+    Iref = pre["I"]
+    # kept sets: positions where the GPU and the oracle differ, and those outside the 1e-5
+    # band around the oracle's threshold (the decision taken on its scores rounded to fp32)
+    I32 = Iref.astype(np.float32).astype(np.float64)
+    ref_idx, _ = im.topk_select(I32, one.B, one.R, one.recent_inclusive)
+    n_cand = one.L - min(one.R, one.L)
+    sel = [t for t in ref_idx.tolist() if t < n_cand]
+    tau = min(I32[t] for t in sel)
+    band = np.abs(I32 - tau) <= 1e-5 * abs(tau)
+    diff = set(gidx.tolist()) ^ set(ref_idx.tolist())
+    same = not diff
+    gK, gV = Kc.cpu().view(torch.int16).numpy()[0], Vc.cpu().view(torch.int16).numpy()[0]
+    K0, V0 = p["K"][0].view(np.int16), p["V"][0].view(np.int16)
+    caches_exact = (gK[:, :keep].tobytes() == np.ascontiguousarray(K0[gidx].transpose(1, 0, 2)).tobytes()
+                    and gV[:, :, :keep].tobytes() == np.ascontiguousarray(V0[gidx].transpose(1, 2, 0)).tobytes())
+    nw = lambda a, r: float(np.linalg.norm(a - r) / max(np.linalg.norm(r), 1e-300))
+    rec = {"workload": f"layer 0, sequence 0 of the workload ({one.L} tokens, {len(p['needles'])} planted needles)",
+           "I_max_rel_err": float(np.max(np.abs(gI - Iref) / np.maximum(np.abs(Iref), 1e-3))),
+           "kept_set_diff": len(diff), "kept_set_diff_outside_band": sum(1 for t in diff if not band[t]),
+           "band_positions": int(band.sum()), "caches_bit_exact": bool(caches_exact)}
+    if same:   # equal kept sets: the memory and the decode see the oracle's own state
+        rec["M_normwise_err"] = nw(M.cpu().numpy()[0].astype(np.float64), pre["M"])
+        rec["b_normwise_err"] = nw(bv.cpu().numpy()[0].astype(np.float64), pre["b"])
+        go = torch.stack(outs).cpu().numpy()[:, 0].astype(np.float64)
+        rec["decode_steps"] = T
+        rec["decode_o_max_abs_err"] = float(np.max(np.abs(go - o_ref)))
+        rec["decode_o_normwise_err"] = nw(go, o_ref)
+    needles = np.asarray(p["needles"])
+    if len(needles):
+        rec["needle_recall_gpu"] = float(np.isin(needles, gidx).mean())
+        rec["needle_recall_oracle"] = float(np.isin(needles, pre["idx"]).mean())
+    return rec
 
 
 def _cpu_model():
