@@ -461,6 +461,62 @@ def measured_peaks(torch, dev):
             "how": "1 GiB device copy (2 x bytes / time) and an 8192^3 bf16 torch.matmul, best of 5 each"}
 
 
+def time_prefill_pieces(torch, api, cfg, li, I, idx, sm, Kc, Vc, M, bvec, keep, cap, lam, ws_i, ws_c, reps=10):
+    """One layer of the stack's index+evict split into its three calls, each replayed `reps`
+    times from a HIP graph: indexer keys + queries + scores (A1-A3), top-k (A4), compaction +
+    memory build (A5-A6), each with the roofline that bounds it (algorithmic work only)."""
+    stream = torch.cuda.Stream()
+    calls = {
+        "A1_A3_index_score": lambda: api.kvm_index_score(li["X"], li["Q"], li["W_kI"], li["gk"], li["W_qI"], li["gq"],
+                                                         li["W_g"], I=I, eps=cfg.eps_rms, ws=ws_i, stream=stream),
+        "A4_topk": lambda: api.kvm_topk_select(I, cfg.B, cfg.R, True, idx=idx, slot_map=sm, stream=stream),
+        "A5_A6_compact_build": lambda: api.kvm_compact_kv(li["K"], li["V"], sm, idx, keep, cap, Kc=Kc, Vc=Vc, M=M,
+                                                          bvec=bvec, lam=lam, ws=ws_c, stream=stream),
+    }
+    us = {}
+    for name, fn in calls.items():
+        with torch.cuda.stream(stream):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for _ in range(reps):
+                    fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            g.replay()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us[name] = e0.elapsed_time(e1) * 1e3 / reps
+    tok = cfg.b * cfg.L
+    x_bytes = tok * cfg.D * 2
+    kv_bytes = tok * cfg.H_kv * cfg.d * 2 * 2
+    kept_bytes = cfg.b * keep * cfg.H_kv * cfg.d * 2 * 2
+    score_flops = 2 * cfg.W * cfg.H_I * cfg.d_I * tok
+    build_flops = (tok - cfg.b * keep) * 2 * cfg.H_kv * cfg.d * (cfg.d + 1)
+    build_bytes = kv_bytes + kept_bytes
+    ai = build_flops / build_bytes
+    attain = min(MFMA_BF16_PEAK_TFS, ai * HBM_PEAK_GBS / 1e3)   # TFLOP/s the build can reach
+    t1, t2, t3 = us["A1_A3_index_score"], us["A4_topk"], us["A5_A6_compact_build"]
+    return {
+        "workload": f"one layer of the stack (batch {cfg.b}, {cfg.L} tokens), each call replayed {reps} times from a "
+                    f"HIP graph",
+        "A1_A3_index_score": {"us": round(t1, 2), "bound": "hbm", "bytes": x_bytes,
+                              "hbm_frac": round(x_bytes / (t1 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                              "score_flops": score_flops},
+        "A4_topk": {"us": round(t2, 2), "bound": "lds/alu latency (4 B read per token)"},
+        "A5_A6_compact_build": {"us": round(t3, 2), "bound": "hbm", "bytes": build_bytes,
+                                "hbm_frac": round(build_bytes / (t3 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "flops": build_flops, "arith_intensity": round(ai, 2),
+                                "attainable_tflops": round(attain, 1),
+                                "frac_of_attainable": round(build_flops / (t3 * 1e-6) / 1e12 / attain, 4)},
+    }
+
+
 def time_long_prefill(torch, api, dev):
     """The 131072-token workload's one-shot index + evict (batch 1): indexer scores over the
     whole prefill, the top 1024 plus a recent window of 64, compaction + memory build, and
@@ -864,6 +920,8 @@ def main():
         "decode_ms_per_step": round(dec_mean / T, 4),
         "roofline": roofline,
     }
+    out["index_evict_pieces"] = time_prefill_pieces(torch, api, cfg, L_in[0], I, idx, sm, Kc[0], Vc[0], Ms[0], bs[0],
+                                                   keep, cap, lam, ws_i, ws_c)
     peaks = measured_peaks(torch, dev)
     roofline["measured_peak"] = peaks["hbm_copy_GBps"]
     roofline["frac_of_measured"] = round(achieved / peaks["hbm_copy_GBps"], 4)
