@@ -203,7 +203,9 @@ __global__ __launch_bounds__(256) void alpha_merge_kernel(AlphaArgs a) {
 // ------------------------------------------------------------------ residual score
 // grid (ceil(L / KEYS), pairs), D / 32 waves (KEYS = 256, or 1024 where the grid keeps a
 // block per CU: each block splits its S once, so larger blocks repeat that less; 32K tokens
-// x batch 4: 0.286 -> 0.251 ms).
+// x batch 4: 0.286 -> 0.251 ms).  The K and V tiles are shared by the block's waves through
+// LDS (each byte fetched once per block, in whole cache lines): with every wave loading the
+// whole K tile itself the round took 0.25 ms, with the shared tiles 0.11 ms.
 // residual: C[i][key] = sum_c S'[i][c] k[key][c] with S' = S~ / (n_e sqrt d) split into
 // three bf16 terms (hi + mid + lo, ~24 bits) as the A operand and the exact bf16 keys as
 // the B operand; r = v - v_bar - C; ||r||^2 sums the lane's rows, the two half-waves and
@@ -230,8 +232,13 @@ __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
   constexpr int NW = D / 32;
   const int c = blockIdx.x, pair = blockIdx.y;
   const int bb = pair / a.H_kv, g = pair % a.H_kv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
+  // LDS K/V tiles: 32 rows of P 16-byte pieces; piece q of row r sits at position q ^ swz(r)
+  constexpr int P = D / 8;
+  const auto swz = [](int r) { return P == 16 ? (r & 15) : ((r >> 1) & 7); };
+  struct SharedTile { uint32_t w[16 * D]; };
+  __shared__ __attribute__((aligned(16))) SharedTile s_k0, s_k1, s_k2, s_v0, s_v1, s_v2;
   __shared__ float s_ss[NW][kScoreKeys];
 
   const int ne = a.n_e[pair];
@@ -280,34 +287,54 @@ __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
   const auto rV = make_rsrc(a.V + bb * a.batch_stride + g * a.head_stride, span);
   const int k0 = c * kScoreKeys;
   const int ntile = min(kScoreKeys, a.L - k0 + 31) / 32;
-  for (int t = 0; t < ntile; ++t) {
-    const int key = k0 + t * 32 + col;
-    const int kbase = key * (int)a.tok_stride;
-    uint4 kt[KS];
-    uint2 vt[4];
+  // Tile t (32 keys) of K and of V moves into LDS slot t % 3 by direct buffer-to-LDS loads:
+  // each of the 2 NW loads per tensor moves 1 KB, lane i writing the 16-byte piece i.  Piece
+  // q of row r holds dims 8 (q ^ swz(r)) .. +8 of key r, so the MFMA operand reads (16 rows
+  // of one 16-byte column per phase) meet no bank conflicts.  A wave waits for its own loads
+  // of a tile, then the block barrier makes every wave's pieces visible; tiles t + 1 and
+  // t + 2 stay in flight meanwhile.
+  const auto kpiece = [&](int t, int i) {
+    const int s = i * 64 + lane;                  // slot of this lane's piece
+    const int r = s / P, q = s % P;
+    const int key = k0 + t * 32 + r;
+    return (key * (int)a.tok_stride + 8 * (q ^ swz(r))) * tb;
+  };
+  auto issue = [&](int st, int t) {
+    SharedTile* sk = st == 0 ? &s_k0 : st == 1 ? &s_k1 : &s_k2;
+    SharedTile* svv = st == 0 ? &s_v0 : st == 1 ? &s_v1 : &s_v2;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kt[ks] = load16(rK, (kbase + half * 8 + ks * 16) * tb);
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rV, (kbase + wave * 32 + 4 * half + 8 * q4) * tb, 0, 0);
-      vt[q4] = make_uint2(v[0], v[1]);
+    for (int j = 0; j < 2; ++j) {
+      const int i = 2 * wave + j;
+      const int off = kpiece(t, i);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (__attribute__((address_space(3))) void*)(&sk->w[i * 256]), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (__attribute__((address_space(3))) void*)(&svv->w[i * 256]), 16, off, 0, 0, 0);
     }
+  };
+  auto compute = [&](int st, int t) {
+    const SharedTile* sk = st == 0 ? &s_k0 : st == 1 ? &s_k1 : &s_k2;
+    const SharedTile* svv = st == 0 ? &s_v0 : st == 1 ? &s_v1 : &s_v2;
+    uint2 vv[4];
     f32x16_t acc;
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      // B operand: key col, dims ks*16 + half*8 .. +8
+      const uint4 kvv = *reinterpret_cast<const uint4*>(&sk->w[(col * P + ((2 * ks + half) ^ swz(col))) * 4]);
       bf16x8_t B;
-      __builtin_memcpy(&B, &kt[ks], 16);
+      __builtin_memcpy(&B, &kvv, 16);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh[ks], B, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sm[ks], B, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl[ks], B, acc, 0, 0, 0);
     }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)    // dims wave*32 + 8 q4 + 4 half .. +4 of this key's v
+      vv[q4] = *reinterpret_cast<const uint2*>(&svv->w[(col * P + ((wave * 4 + q4) ^ swz(col))) * 4 + half * 2]);
     float ss = 0.f;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      // rows 8 q4 + 4 half + 0..3: four consecutive dims of this key's v
-      const float v4[4] = {bf16_lo(vt[q4].x), bf16_hi(vt[q4].x), bf16_lo(vt[q4].y), bf16_hi(vt[q4].y)};
+      // rows 8 q4 + 4 half + 0..3 of the C tile
+      const float v4[4] = {bf16_lo(vv[q4].x), bf16_hi(vv[q4].x), bf16_lo(vv[q4].y), bf16_hi(vv[q4].y)};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float r = v4[e] - vbar[q4 * 4 + e] - acc[q4 * 4 + e];
@@ -315,8 +342,26 @@ __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
       }
     }
     ss += shfl_xor32(ss);
-    if (half == 0) s_ss[wave][t * 32 + col] = ss;
+    s_ss[wave][t * 32 + col] = ss;   // both half-waves hold the same sum
+  };
+  // step t: this wave's loads of tile t are done once at most those of tile t + 1 (4) are
+  // out; the barrier then also tells that every wave has finished with tile t - 1, whose slot
+  // tile t + 2 takes (past the last tile the last one is loaded again, into a free slot)
+  auto step = [&](int st, int t) {
+    asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+    issue((st + 2) % 3, min(t + 2, ntile - 1));
+    compute(st, t);
+  };
+  issue(0, 0);
+  issue(1, min(1, ntile - 1));
+  int t = 0;
+  for (; t + 3 <= ntile; t += 3) {
+    step(0, t);
+    step(1, t + 1);
+    step(2, t + 2);
   }
+  if (t < ntile) step(0, t);
+  if (t + 1 < ntile) step(1, t + 1);
   __syncthreads();
   for (int i = tid; i < ntile * 32; i += NW * 64) {
     const int j = k0 + i;
@@ -470,7 +515,7 @@ extern "C" kvm_status kvm_moment_score(const kvm_moment_desc* d, const void* K, 
   {
     long long ts, hs, bs;
     strides(d, ts, hs, bs);
-    KVM_REQUIRE(((long long)(d->L + 1024) * ts + d->d) * 2 < 0x7fffffffLL, KVM_ERR_RANGE,
+    KVM_REQUIRE(((long long)(d->L + 2048) * ts + d->d) * 2 < 0x7fffffffLL, KVM_ERR_RANGE,
                 "one (sequence, KV head) of K/V spans more than 2 GiB (L %d)", d->L);
   }
   st = require_gfx950();
