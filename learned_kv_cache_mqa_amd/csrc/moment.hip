@@ -34,18 +34,19 @@ struct AlphaArgs {
 // passes 0.329 -> 0.281 ms).
 static int alpha_chunk(int L, int pairs) { return (long long)((L + 2047) / 2048) * pairs >= 512 ? 2048 : 512; }
 constexpr int kAlphaQPW = 2;       // 32-row query tiles per wave (W G <= 256)
-constexpr int kKPitch = 8;         // LDS row pad (elements) of a key tile
 
 template <int D, int PASS, int kAlphaChunk>
-__global__ __launch_bounds__(256) void moment_alpha_kernel(AlphaArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void moment_alpha_kernel(AlphaArgs a) {
   constexpr int KS = D / 16;
-  constexpr int RP = D + kKPitch;             // LDS pitch (elements)
-  constexpr int PER = 32 * D / 8 / 256;       // 16-byte pieces of a key tile per thread
   const int c = blockIdx.x, pair = blockIdx.y;
   const int bb = pair / a.H_kv, g = pair % a.H_kv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
-  __shared__ uint16_t sK[2][32 * RP];
+  constexpr int P = D / 8;                    // 16-byte pieces per key row
+  constexpr int NI = 32 * P / 64 / 4;         // 1 KB loads per wave per key tile
+  const auto swz = [](int r) { return P == 16 ? (r & 15) : ((r >> 1) & 7); };
+  struct KeyTile { uint32_t w[16 * D]; };
+  __shared__ __attribute__((aligned(16))) KeyTile sK0, sK1, sK2;
   __shared__ float s_alpha[4][kAlphaChunk];
 
   // query operands of this wave's tiles: rows r = s G + hh of the group (q of position L-W+s)
@@ -78,39 +79,38 @@ __global__ __launch_bounds__(256) void moment_alpha_kernel(AlphaArgs a) {
 #pragma unroll
   for (int x = 0; x < kAlphaQPW; ++x) { m[x] = -INFINITY; l[x] = 0.f; }
 
-  const uint16_t* Kb = a.K + bb * a.batch_stride + g * a.head_stride;
   const int k0 = c * kAlphaChunk;
   const int ntile = min(kAlphaChunk, a.L - k0 + 31) / 32;
   const int p0 = a.L - a.W;   // position of window query 0
-  // key tile t -> LDS buffer (t & 1); rows past L are zero
-  uint4 kr[PER];
-  auto kload = [&](int t) {
+  // Key tile t (32 rows) moves into LDS slot t % 3 by direct buffer-to-LDS loads, NI per
+  // wave, each moving 1 KB (lane i writes the 16-byte piece i).  Piece q of row r holds dims
+  // 8 (q ^ swz(r)) .. +8 of key r, so the operand reads (16 rows of one 16-byte column per
+  // phase) meet no bank conflicts; rows past L read zeros.  A wave waits for its own loads
+  // of tile t, then the block barrier makes every wave's pieces visible, while tiles t + 1
+  // and t + 2 stay in flight: with one tile in flight per block (8 KB) the pass ran at the
+  // rate its loads in flight allow (~2 TB/s).
+  const int span = (int)(((long long)(a.L - 1) * a.tok_stride + D) * 2);
+  const auto rK = make_rsrc(a.K + bb * a.batch_stride + g * a.head_stride, span);
+  auto issue = [&](int st, int t) {
+    KeyTile* sk = st == 0 ? &sK0 : st == 1 ? &sK1 : &sK2;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int piece = tid + i * 256, row = piece / (D / 8), cc = piece % (D / 8);
-      const int j = k0 + t * 32 + row;
-      kr[i] = j < a.L ? *reinterpret_cast<const uint4*>(Kb + (size_t)j * a.tok_stride + cc * 8) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < NI; ++j) {
+      const int i = NI * wave + j;
+      const int sl = i * 64 + lane, r = sl / P, q = sl % P;
+      const int off = ((k0 + t * 32 + r) * (int)a.tok_stride + 8 * (q ^ swz(r))) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (__attribute__((address_space(3))) void*)(&sk->w[i * 256]), 16, off, 0, 0, 0);
     }
   };
-  auto kstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int piece = tid + i * 256, row = piece / (D / 8), cc = piece % (D / 8);
-      *reinterpret_cast<uint4*>(&sK[buf][row * RP + cc * 8]) = kr[i];
-    }
-  };
-  kload(0);
-  kstore(0);
-  __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
-    if (t + 1 < ntile) kload(t + 1);
-    const int buf = t & 1;
+  auto compute = [&](int st, int t) {
+    const KeyTile* sk = st == 0 ? &sK0 : st == 1 ? &sK1 : &sK2;
     const int kb = k0 + t * 32;
+    // a tile whose keys every window query sees (and all below L) needs no causal mask
+    const bool interior = kb + 31 <= p0;
     // key operand: key row `col`, k-slice half*8 .. +8 of each k-step
     bf16x8_t kop[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&sK[buf][col * RP + ks * 16 + half * 8]);
+      const uint4 v = *reinterpret_cast<const uint4*>(&sk->w[(col * P + ((2 * ks + half) ^ swz(col))) * 4]);
       __builtin_memcpy(&kop[ks], &v, 16);
     }
     float asum = 0.f;
@@ -129,38 +129,75 @@ __global__ __launch_bounds__(256) void moment_alpha_kernel(AlphaArgs a) {
         const int r = rbase + col;
         const int lim = r < a.WG ? min(a.L - 1, p0 + r / a.G) : -1;   // last visible key
         float z[16], mt = -INFINITY;
+        if (interior) {   // (rows past W G only fill state that is never written)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = kb + 8 * (j / 4) + 4 * half + (j % 4);
-          z[j] = key <= lim ? acc[j] * a.scale_log2 : -INFINITY;
-          mt = fmaxf(mt, z[j]);
+          for (int j = 0; j < 16; ++j) {
+            z[j] = acc[j] * a.scale_log2;
+            mt = fmaxf(mt, z[j]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = kb + 8 * (j / 4) + 4 * half + (j % 4);
+            z[j] = key <= lim ? acc[j] * a.scale_log2 : -INFINITY;
+            mt = fmaxf(mt, z[j]);
+          }
         }
+        // no branch on an empty column: with the maximum still -inf every term is 0 and the
+        // state stays (-inf, 0)
         const float mn = fmaxf(m[x], mt);
-        if (mn != -INFINITY) {
-          float sacc = l[x] * __builtin_amdgcn_exp2f(m[x] - mn);
+        const float msafe = mn == -INFINITY ? 0.f : mn;
+        float sacc = l[x] * __builtin_amdgcn_exp2f(m[x] - msafe);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) sacc += __builtin_amdgcn_exp2f(z[j] - mn);
-          l[x] = sacc;
-          m[x] = mn;
-        }
+        for (int j = 0; j < 16; ++j) sacc += __builtin_amdgcn_exp2f(z[j] - msafe);
+        l[x] = sacc;
+        m[x] = mn;
       } else {
         // rows = queries, this lane's column = key kb + col
         const int key = kb + col;
+        if (interior) {   // rows past W G: lq = inf, so their terms are +0
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int r = rbase + 8 * (j / 4) + 4 * half + (j % 4);
-          const bool vis = r < a.WG && key < a.L && key <= p0 + r / a.G;
-          asum += vis ? __builtin_amdgcn_exp2f(acc[j] * a.scale_log2 - lq[x][j]) : 0.f;
+          for (int j = 0; j < 16; ++j) asum += __builtin_amdgcn_exp2f(acc[j] * a.scale_log2 - lq[x][j]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int r = rbase + 8 * (j / 4) + 4 * half + (j % 4);
+            const bool vis = r < a.WG && key < a.L && key <= p0 + r / a.G;
+            asum += vis ? __builtin_amdgcn_exp2f(acc[j] * a.scale_log2 - lq[x][j]) : 0.f;
+          }
         }
       }
     }
     if (PASS == 2) {
       asum += shfl_xor32(asum);
-      if (half == 0) s_alpha[wave][t * 32 + col] = asum;
+      s_alpha[wave][t * 32 + col] = asum;   // both half-waves hold the same sum
+    } else {
+      // the tile's softmax state is final here: left free, the compiler defers the epilogues
+      // of three tiles past the next barriers and keeps their accumulators live meanwhile
+#pragma unroll
+      for (int x = 0; x < kAlphaQPW; ++x) asm volatile("" : "+v"(m[x]), "+v"(l[x]));
     }
-    if (t + 1 < ntile) kstore(buf ^ 1);
-    __syncthreads();
+  };
+  // step t: this wave's loads of tile t are done once at most those of tile t + 1 (NI) are
+  // out; the barrier then also tells that every wave has finished with tile t - 1, whose slot
+  // tile t + 2 takes (past the last tile the last one is loaded again, into a free slot)
+  auto step = [&](int st, int t) {
+    if constexpr (NI == 2) asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
+    issue((st + 2) % 3, min(t + 2, ntile - 1));
+    compute(st, t);
+  };
+  issue(0, 0);
+  issue(1, min(1, ntile - 1));
+  int t = 0;
+  for (; t + 3 <= ntile; t += 3) {
+    step(0, t);
+    step(1, t + 1);
+    step(2, t + 2);
   }
+  if (t < ntile) step(0, t);
+  if (t + 1 < ntile) step(1, t + 1);
+  __syncthreads();
   if (PASS == 1) {
     // combine the two half-waves (same query column, different key rows)
 #pragma unroll
@@ -466,6 +503,12 @@ extern "C" kvm_status kvm_moment_alpha(const kvm_moment_desc* d, const void* Qwi
   KVM_REQUIRE(d->W * G <= 4 * kAlphaQPW * 32, KVM_ERR_SHAPE, "W * G = %d exceeds %d", d->W * G, 4 * kAlphaQPW * 32);
   KVM_REQUIRE(d->scale > 0.f, KVM_ERR_RANGE, "scale %g must be positive", d->scale);
   KVM_PTR_ALIGNED(Qwin); KVM_PTR_ALIGNED(K); KVM_PTR_ALIGNED(alpha);
+  {
+    long long ts, hs, bs;
+    strides(d, ts, hs, bs);
+    KVM_REQUIRE(((long long)(d->L + 2048) * ts + d->d) * 2 < 0x7fffffffLL, KVM_ERR_RANGE,
+                "one (sequence, KV head) of K spans more than 2 GiB (L %d)", d->L);
+  }
   const MomentWs w = moment_ws(d);
   KVM_REQUIRE(ws != nullptr && ws_bytes >= w.total, KVM_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.total);
   KVM_ALIGNED(ws);
