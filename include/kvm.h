@@ -384,9 +384,9 @@ kvm_status kvm_moment_readout(const kvm_mread_desc* desc, const void* q, const f
  * q [b, H_q, d], k_new, v_new [b, H_kv, d] bf16; Kc [b, H_kv, cap, d], Vc [b, H_kv, d, cap]
  * bf16 (read-modify-write); slot_pos [b, H_kv, P] i32, next_pos [b] i32, n_e [b, H_kv] i32,
  * s_k, s_v [b, H_kv, d] f32, S [b, H_kv, d, d] f32 (all read-modify-write);
- * evict_slot [b, H_kv] i32 (output).  Requires P > R, cap >= P, d in {64, 128},
- * G in {1, 2, 4, 8}.  Arithmetic: fp32; S~ / (n_e sqrt d) enters the matrix cores as three bf16
- * terms against the exact bf16 keys.
+ * evict_slot [b, H_kv] i32 (output).  Requires P > R, cap >= P with cap a multiple of 8 (as
+ * kvm_decode_attn_mem does), d in {64, 128}, G in {1, 2, 4, 8}.  Arithmetic: fp32;
+ * S~ / (n_e sqrt d) enters the matrix cores as three bf16 terms against the exact bf16 keys.
  * ------------------------------------------------------------------------------------ */
 typedef struct {
   int32_t b, H_q, H_kv, d;

@@ -131,6 +131,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
+// LDS tiles whose rows are P 16-byte pieces (P = 16: 128 bf16; P = 8: 64 bf16): piece q of
+// row r is stored at position q ^ piece_swz<P>(r).  Sixteen consecutive rows reading the same
+// piece then hit sixteen different 16-byte bank groups, so 16-byte operand reads down a
+// column meet no bank conflicts.
+template <int P>
+__device__ __forceinline__ int piece_swz(int r) {
+  static_assert(P == 8 || P == 16, "pieces per row");
+  return P == 16 ? (r & 15) : ((r >> 1) & 7);
+}
+
 // x = h + m + l in bf16 (round to nearest even at each step; ~24 bits of x), 8 values with
 // the packed hardware conversion
 __device__ __forceinline__ void split3_bf16x8(const float (&x)[8], bf16x8_t& h, bf16x8_t& m, bf16x8_t& l) {

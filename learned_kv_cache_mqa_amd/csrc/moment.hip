@@ -44,7 +44,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   const int col = lane & 31, half = lane >> 5;
   constexpr int P = D / 8;                    // 16-byte pieces per key row
   constexpr int NI = 32 * P / 64 / 4;         // 1 KB loads per wave per key tile
-  const auto swz = [](int r) { return P == 16 ? (r & 15) : ((r >> 1) & 7); };
   struct KeyTile { uint32_t w[16 * D]; };
   __shared__ __attribute__((aligned(16))) KeyTile sK0, sK1, sK2;
   __shared__ float s_alpha[4][kAlphaChunk];
@@ -84,7 +83,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
   const int p0 = a.L - a.W;   // position of window query 0
   // Key tile t (32 rows) moves into LDS slot t % 3 by direct buffer-to-LDS loads, NI per
   // wave, each moving 1 KB (lane i writes the 16-byte piece i).  Piece q of row r holds dims
-  // 8 (q ^ swz(r)) .. +8 of key r, so the operand reads (16 rows of one 16-byte column per
+  // 8 (q ^ piece_swz<P>(r)) .. +8 of key r, so the operand reads (16 rows of one 16-byte column per
   // phase) meet no bank conflicts; rows past L read zeros.  A wave waits for its own loads
   // of tile t, then the block barrier makes every wave's pieces visible, while tiles t + 1
   // and t + 2 stay in flight: with one tile in flight per block (8 KB) the pass ran at the
@@ -97,7 +96,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     for (int j = 0; j < NI; ++j) {
       const int i = NI * wave + j;
       const int sl = i * 64 + lane, r = sl / P, q = sl % P;
-      const int off = ((k0 + t * 32 + r) * (int)a.tok_stride + 8 * (q ^ swz(r))) * 2;
+      const int off = ((k0 + t * 32 + r) * (int)a.tok_stride + 8 * (q ^ piece_swz<P>(r))) * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (__attribute__((address_space(3))) void*)(&sk->w[i * 256]), 16, off, 0, 0, 0);
     }
   };
@@ -110,7 +109,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     bf16x8_t kop[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&sk->w[(col * P + ((2 * ks + half) ^ swz(col))) * 4]);
+      const uint4 v = *reinterpret_cast<const uint4*>(&sk->w[(col * P + ((2 * ks + half) ^ piece_swz<P>(col))) * 4]);
       __builtin_memcpy(&kop[ks], &v, 16);
     }
     float asum = 0.f;
@@ -271,9 +270,8 @@ __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
   const int bb = pair / a.H_kv, g = pair % a.H_kv;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
-  // LDS K/V tiles: 32 rows of P 16-byte pieces; piece q of row r sits at position q ^ swz(r)
+  // LDS K/V tiles: 32 rows of P 16-byte pieces, swizzled by piece_swz
   constexpr int P = D / 8;
-  const auto swz = [](int r) { return P == 16 ? (r & 15) : ((r >> 1) & 7); };
   struct SharedTile { uint32_t w[16 * D]; };
   __shared__ __attribute__((aligned(16))) SharedTile s_k0, s_k1, s_k2, s_v0, s_v1, s_v2;
   __shared__ float s_ss[NW][kScoreKeys];
@@ -326,7 +324,7 @@ __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
   const int ntile = min(kScoreKeys, a.L - k0 + 31) / 32;
   // Tile t (32 keys) of K and of V moves into LDS slot t % 3 by direct buffer-to-LDS loads:
   // each of the 2 NW loads per tensor moves 1 KB, lane i writing the 16-byte piece i.  Piece
-  // q of row r holds dims 8 (q ^ swz(r)) .. +8 of key r, so the MFMA operand reads (16 rows
+  // q of row r holds dims 8 (q ^ piece_swz<P>(r)) .. +8 of key r, so the MFMA operand reads (16 rows
   // of one 16-byte column per phase) meet no bank conflicts.  A wave waits for its own loads
   // of a tile, then the block barrier makes every wave's pieces visible; tiles t + 1 and
   // t + 2 stay in flight meanwhile.
@@ -334,7 +332,7 @@ __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
     const int s = i * 64 + lane;                  // slot of this lane's piece
     const int r = s / P, q = s % P;
     const int key = k0 + t * 32 + r;
-    return (key * (int)a.tok_stride + 8 * (q ^ swz(r))) * tb;
+    return (key * (int)a.tok_stride + 8 * (q ^ piece_swz<P>(r))) * tb;
   };
   auto issue = [&](int st, int t) {
     SharedTile* sk = st == 0 ? &s_k0 : st == 1 ? &s_k1 : &s_k2;
@@ -357,7 +355,7 @@ __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       // B operand: key col, dims ks*16 + half*8 .. +8
-      const uint4 kvv = *reinterpret_cast<const uint4*>(&sk->w[(col * P + ((2 * ks + half) ^ swz(col))) * 4]);
+      const uint4 kvv = *reinterpret_cast<const uint4*>(&sk->w[(col * P + ((2 * ks + half) ^ piece_swz<P>(col))) * 4]);
       bf16x8_t B;
       __builtin_memcpy(&B, &kvv, 16);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh[ks], B, acc, 0, 0, 0);
@@ -366,7 +364,7 @@ __global__ __launch_bounds__(D * 2) void moment_score_kernel(ScoreArgs a) {
     }
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)    // dims wave*32 + 8 q4 + 4 half .. +4 of this key's v
-      vv[q4] = *reinterpret_cast<const uint2*>(&svv->w[(col * P + ((wave * 4 + q4) ^ swz(col))) * 4 + half * 2]);
+      vv[q4] = *reinterpret_cast<const uint2*>(&svv->w[(col * P + ((wave * 4 + q4) ^ piece_swz<P>(col))) * 4 + half * 2]);
     float ss = 0.f;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {

@@ -53,11 +53,18 @@ __global__ __launch_bounds__(D * 2) void mstream_score_kernel(MsArgs a) {
   constexpr int kMsKeys = KEYS;
   constexpr int KS = D / 16;
   constexpr int NW = D / 32;
+  constexpr int NT = kMsKeys / 32;
+  constexpr int P = D / 8;              // 16-byte pieces per key row
+  constexpr int NLD = kMsKeys / 16;     // 1 KB loads per wave for each of K and V
+  static_assert(NLD * NW * 1024 == kMsKeys * D * 2, "the waves' loads cover the block");
   const int c = blockIdx.x, g = blockIdx.y, bb = blockIdx.z;
   const size_t pair = (size_t)bb * a.H_kv + g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
-  __shared__ float s_ss[NW][kMsKeys];
+  // the block's K rows [KEYS][P pieces] (swizzled by piece_swz) and V columns [D][KEYS]
+  // (dim-major, as in the cache); after the products the K region holds the per-wave sums
+  __shared__ __attribute__((aligned(16))) uint32_t s_kb[kMsKeys * D / 2];
+  __shared__ __attribute__((aligned(16))) uint32_t s_vb[kMsKeys * D / 2];
   // the step's position advances once per sequence, here; the commit reads next_pos - 1
   if (c == 0 && g == 0 && tid == 0) a.next_pos[bb] += 1;
 
@@ -65,10 +72,17 @@ __global__ __launch_bounds__(D * 2) void mstream_score_kernel(MsArgs a) {
   const float inv_n = (ne > 0 ? 1.f : 0.f) / (float)max(ne, 1);   // no branch on the count
   const float* sk = a.s_k + pair * D;
   const float* sv = a.s_v + pair * D;
+  // K and V come into LDS by direct buffer-to-LDS loads, 1 KB each, issued right after the
+  // S rows so that they travel while S is split.  K slots past the pool read zeros; V
+  // slots past it read whatever the rows hold (cap is a multiple of 8, so every row's
+  // slots start on a 16-byte boundary) and only reach results that are never written.
+  const int k0 = c * kMsKeys;
+  const auto rK = make_rsrc(a.Kc + pair * a.cap * D, a.P * D * 2);
+  const auto rV = make_rsrc(a.Vc + pair * D * a.cap, D * a.cap * 2);
   // A operands: row i = 32 wave + col of S' (zero while nothing is evicted).  Every load is
   // unconditional; the count only selects the result, so no load waits behind a branch.
   const int i_row = wave * 32 + col;
-  bf16x8_t sh[KS], sm[KS], sl[KS];
+  bf16x8_t sh[KS], sm[KS], sl3[KS];
   {
     const float* Sr = a.S + (pair * D + i_row) * D;
     const float svi = sv[i_row];
@@ -82,6 +96,22 @@ __global__ __launch_bounds__(D * 2) void mstream_score_kernel(MsArgs a) {
         k4[ks][u] = *reinterpret_cast<const float4*>(sk + ks * 16 + half * 8 + 4 * u);
       }
     }
+    // the block's K and V, issued behind the S rows (the offsets are computed apart from the
+    // load builtin's arguments: with a device call inside them the host pass drops the
+    // kernel's launch stubs)
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int i = NLD * wave + j;
+      const int sl = i * 64 + lane, r = sl / P, q = sl % P;
+      const int koff = ((k0 + r) * D + 8 * (q ^ piece_swz<P>(r))) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (__attribute__((address_space(3))) void*)(&s_kb[i * 256]), 16, koff,
+                                               0, 0, 0);
+      const int bv = i * 1024 + lane * 16;   // byte of the V block
+      const int dim = bv / (kMsKeys * 2), sb = bv % (kMsKeys * 2);
+      const int voff = (dim * a.cap + k0) * 2 + sb;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (__attribute__((address_space(3))) void*)(&s_vb[i * 256]), 16, voff,
+                                               0, 0, 0);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       float x[8];
@@ -91,7 +121,7 @@ __global__ __launch_bounds__(D * 2) void mstream_score_kernel(MsArgs a) {
         const float kv = e < 4 ? (&k4[ks][0].x)[e] : (&k4[ks][1].x)[e - 4];
         x[e] = ne > 0 ? (sr - svi * kv * inv_n) * f : 0.f;
       }
-      split3_bf16x8(x, sh[ks], sm[ks], sl[ks]);
+      split3_bf16x8(x, sh[ks], sm[ks], sl3[ks]);
     }
   }
   // the group's queries as rows (rows >= G read zeros)
@@ -109,46 +139,37 @@ __global__ __launch_bounds__(D * 2) void mstream_score_kernel(MsArgs a) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) vbar[j] = sv[wave * 32 + 8 * (j / 4) + 4 * half + (j % 4)] * inv_n;
 
-  // tile loads through buffer resources: slots past the pool read zeros (K) or take an
-  // offset past the end (V), so no load is conditional
-  const auto rK = make_rsrc(a.Kc + pair * a.cap * D, a.P * D * 2);
-  const auto rV = make_rsrc(a.Vc + pair * D * a.cap, D * a.cap * 2);
-  const int k0 = c * kMsKeys;
-  constexpr int NT = kMsKeys / 32;
+  // every wave's loads have landed: the block's K and V are in LDS
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const uint16_t* svh = reinterpret_cast<const uint16_t*>(s_vb);
+  float ssr[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int slot = k0 + t * 32 + col;
     const bool ok = slot < a.P;
-    uint4 kt[KS];
-    float vt[16];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kt[ks] = load16(rK, (slot * D + ks * 16 + half * 8) * 2);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int dim = wave * 32 + 8 * (j / 4) + 4 * half + (j % 4);
-      const int off = ok ? (dim * a.cap + slot) * 2 : 0x7ffffff0;
-      vt[j] = bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rV, off, 0, 0));
-    }
     f32x16_t acc, accq;
 #pragma unroll
     for (int j = 0; j < 16; ++j) { acc[j] = 0.f; accq[j] = 0.f; }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      // B operand: slot t*32 + col, dims ks*16 + half*8 .. +8
+      const uint4 kv = *reinterpret_cast<const uint4*>(&s_kb[((t * 32 + col) * P + ((2 * ks + half) ^ piece_swz<P>(col))) * 4]);
       bf16x8_t B;
-      __builtin_memcpy(&B, &kt[ks], 16);
+      __builtin_memcpy(&B, &kv, 16);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh[ks], B, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sm[ks], B, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl[ks], B, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl3[ks], B, acc, 0, 0, 0);
       if (wave == 0) accq = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], B, accq, 0, 0, 0);
     }
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const float r = vt[j] - vbar[j] - acc[j];
+      const int dim = wave * 32 + 8 * (j / 4) + 4 * half + (j % 4);
+      const float r = bf16_to_f32(svh[dim * kMsKeys + t * 32 + col]) - vbar[j] - acc[j];
       ss = fmaf(r, r, ss);
     }
-    ss += shfl_xor32(ss);
-    if (half == 0) s_ss[wave][t * 32 + col] = ss;
+    ssr[t] = ss + shfl_xor32(ss);
     if (wave == 0 && ok) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -157,13 +178,17 @@ __global__ __launch_bounds__(D * 2) void mstream_score_kernel(MsArgs a) {
       }
     }
   }
+  __syncthreads();   // every wave is done with the K rows: their LDS takes the sums
+  float* s_ss = reinterpret_cast<float*>(s_kb);   // [NW][KEYS]
+#pragma unroll
+  for (int t = 0; t < NT; ++t) s_ss[wave * kMsKeys + t * 32 + col] = ssr[t];   // both halves: same sum
   __syncthreads();
   for (int i = tid; i < kMsKeys; i += NW * 64) {
     const int j = k0 + i;
     if (j < a.P) {
       float ss = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) ss += s_ss[w][i];
+      for (int w = 0; w < NW; ++w) ss += s_ss[w * kMsKeys + i];
       a.rn[pair * a.P + j] = sqrtf(ss);
     }
   }
@@ -365,6 +390,7 @@ extern "C" kvm_status kvm_moment_stream_evict(const kvm_mstream_desc* d, const v
   KVM_REQUIRE(d->dtype == KVM_BF16, KVM_ERR_DTYPE, "MomentKV scoring takes bf16 q, K, V (dtype %d)", d->dtype);
   KVM_REQUIRE(d->R >= 0 && d->P > d->R, KVM_ERR_RANGE, "pool %d must exceed the recent window %d", d->P, d->R);
   KVM_REQUIRE(d->cap >= d->P, KVM_ERR_RANGE, "cap %d below pool %d", d->cap, d->P);
+  KVM_REQUIRE(d->cap % 8 == 0, KVM_ERR_SHAPE, "cap %d is not a multiple of 8", d->cap);
   KVM_REQUIRE((long long)d->cap * d->d * 2 < 0x7ffffff0LL, KVM_ERR_RANGE, "cap %d too large", d->cap);
   KVM_PTR_ALIGNED(q); KVM_PTR_ALIGNED(k_new); KVM_PTR_ALIGNED(v_new); KVM_PTR_ALIGNED(Kc); KVM_PTR_ALIGNED(Vc);
   KVM_PTR_ALIGNED(slot_pos); KVM_PTR_ALIGNED(next_pos); KVM_PTR_ALIGNED(n_e); KVM_PTR_ALIGNED(s_k);

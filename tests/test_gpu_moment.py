@@ -74,6 +74,8 @@ def _dev_moments(moms):
 
 @pytest.mark.parametrize("L,d,n,hm", [(1000, 128, 300, False), (513, 64, 50, True), (300, 128, 0, False),
                                       (4097, 128, 4000, True),
+                                      # a last block of 3 tiles: the tile ring's loop without a tail
+                                      (864, 128, 100, False), (352, 64, 20, True),
                                       # >= 256 blocks of 1024 keys: the wide-block variant
                                       (32769, 128, 5000, False), (32000, 64, 100, True)])
 def test_residual_score_matches_oracle(L, d, n, hm):
