@@ -285,11 +285,21 @@ __global__ __launch_bounds__(256) void kmeans_prep_kernel(KmArgs a) {
 
 // grid (ceil(N / 128), H), 256 threads: wave w scores queries 128 x + 32 w .. + 31 against
 // 32-centroid tiles, S^T = C' X^T (centroids as rows), so each lane holds 16 centroids of
-// one query; the lower score wins, ties keep the lower index.
+// one query; the lower score wins, ties keep the lower index.  The centroid tiles (three
+// planes of 32 rows) come by direct buffer-to-LDS loads into a three-slot ring shared by the
+// block's waves (rows of P 16-byte pieces, swizzled by piece_swz); a wave waits for its own
+// loads of tile t before the block barrier while tiles t + 1 and t + 2 stay in flight.  (With
+// every wave loading each tile itself, 16 bytes per lane over 32 rows and one tile at a
+// time, an assignment pass over 4096 queries x 32 heads took ~98 us.)
 template <int D>
 __global__ __launch_bounds__(256) void kmeans_assign_kernel(KmArgs a) {
   constexpr int KS = D / 16;
-  const int hh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int P = D / 8;                    // 16-byte pieces per centroid row
+  constexpr int NI = 3 * 32 * P / 64 / 4;     // 1 KB loads per wave per tile
+  struct CTile { uint32_t w[3 * 32 * D / 2]; };   // [plane][32 rows][P pieces]
+  __shared__ __attribute__((aligned(16))) CTile sC0, sC1, sC2;
+  __shared__ float s_n2[256];
+  const int hh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int q0 = blockIdx.x * 128 + wave * 32;
   bf16x8_t xb[KS];
@@ -301,20 +311,34 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(KmArgs a) {
       __builtin_memcpy(&xb[ks], &v, 16);
     }
   }
-  const uint16_t* cs = a.Cs + (size_t)hh * 3 * a.Kp * D;
-  const float* n2 = a.cn2 + (size_t)hh * a.Kp;
+  for (int i = tid; i < a.Kp; i += 256) s_n2[i] = a.cn2[(size_t)hh * a.Kp + i];
+  const auto rC = make_rsrc(a.Cs + (size_t)hh * 3 * a.Kp * D, 3 * a.Kp * D * 2);
+  const int ntile = a.Kp / 32;
+  auto issue = [&](int st, int t) {
+    CTile* sc = st == 0 ? &sC0 : st == 1 ? &sC1 : &sC2;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const int i = NI * wave + j;
+      const int sl = i * 64 + lane, pl = sl / (32 * P), r = (sl / P) % 32, q = sl % P;
+      const int off = ((pl * a.Kp + t * 32 + r) * D + 8 * (q ^ piece_swz<P>(r))) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rC, (__attribute__((address_space(3))) void*)(&sc->w[i * 256]), 16, off, 0, 0, 0);
+    }
+  };
   float best = INFINITY;
   int bi = 0;
-  for (int k0 = 0; k0 < a.Kp; k0 += 32) {
+  auto compute = [&](int st, int t) {
+    const CTile* sc = st == 0 ? &sC0 : st == 1 ? &sC1 : &sC2;
+    const int k0 = t * 32;
     f32x16_t acc;
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const size_t off = (size_t)(k0 + col) * D + ks * 16 + half * 8;
-      const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(cs + off);
-      const bf16x8_t am = *reinterpret_cast<const bf16x8_t*>(cs + (size_t)a.Kp * D + off);
-      const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(cs + (size_t)2 * a.Kp * D + off);
+      // A operands: centroid row k0 + col, dims ks*16 + half*8 .. +8 of each plane
+      const int pw = (col * P + ((2 * ks + half) ^ piece_swz<P>(col))) * 4;
+      const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sc->w[pw]);
+      const bf16x8_t am = *reinterpret_cast<const bf16x8_t*>(&sc->w[pw + 32 * P * 4]);
+      const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sc->w[pw + 64 * P * 4]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[ks], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, xb[ks], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[ks], acc, 0, 0, 0);
@@ -322,10 +346,33 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(KmArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {   // centroid of row j: k0 + 8 (j / 4) + 4 half + j % 4 (increasing)
       const int k = k0 + 8 * (j / 4) + 4 * half + (j & 3);
-      const float sc = fmaf(-2.f, acc[j], n2[k]);
-      if (sc < best) { best = sc; bi = k; }
+      const float sc2 = fmaf(-2.f, acc[j], s_n2[k]);
+      if (sc2 < best) { best = sc2; bi = k; }
     }
+    // the tile's result is final here (left free, the compiler defers the comparisons of
+    // several tiles past the next barriers and keeps their accumulators live)
+    asm volatile("" : "+v"(best), "+v"(bi));
+  };
+  // step t: this wave's loads of tile t are done once at most those of tile t + 1 (NI) are
+  // out; the barrier then also tells that every wave has finished with tile t - 1, whose slot
+  // tile t + 2 takes (past the last tile the last one is loaded again, into a free slot)
+  auto step = [&](int st, int t) {
+    if constexpr (NI == 6) asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(3)\n\ts_barrier" ::: "memory");
+    issue((st + 2) % 3, min(t + 2, ntile - 1));
+    compute(st, t);
+  };
+  issue(0, 0);
+  issue(1, min(1, ntile - 1));
+  __syncthreads();   // the norms in LDS (and the first tiles landed)
+  int t = 0;
+  for (; t + 3 <= ntile; t += 3) {
+    step(0, t);
+    step(1, t + 1);
+    step(2, t + 2);
   }
+  if (t < ntile) step(0, t);
+  if (t + 1 < ntile) step(1, t + 1);
   const float ob = shfl_xor32(best);
   const int oi = __shfl_xor(bi, 32);
   if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
