@@ -469,17 +469,26 @@ __global__ __launch_bounds__(256) void kmeans_reduce_kernel(KmArgs a, int nchunk
   constexpr int RW = D + kRowExtra;
   __shared__ float sC[32][D + 4];
   const int k0 = blockIdx.x * 32, hh = blockIdx.y;
-  for (int i = threadIdx.x; i < 32 * D; i += 256) {
-    const int kk = i / D, c = i % D, k = k0 + kk;
-    float s = 0.f, n = 0.f;
+  // thread: four consecutive dims of a centroid (16-byte loads of each chunk's partial row),
+  // each summed over the chunks in chunk order
+  static_assert(RW % 4 == 0, "16-byte aligned partial rows");
+  for (int i = threadIdx.x; i < 32 * D / 4; i += 256) {
+    const int kk = i / (D / 4), c = (i % (D / 4)) * 4, k = k0 + kk;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    float n = 0.f;
     for (int chn = 0; chn < nchunk; ++chn) {
       const float* p = a.part + (((size_t)hh * nchunk + chn) * a.Kp + k) * RW;
-      s += p[c];
+      const float4 v = *reinterpret_cast<const float4*>(p + c);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
       n += p[D];
     }
-    float v = 0.f;
-    if (k < a.K) v = n > 0.f ? s / n : a.C[((size_t)hh * a.K + k) * D + c];
-    sC[kk][c] = v;
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = 0.f;
+      if (k < a.K) v = n > 0.f ? sv[e] / n : a.C[((size_t)hh * a.K + k) * D + c + e];
+      sC[kk][c + e] = v;
+    }
   }
   __syncthreads();
   write_centroid_tile<D>(a, hh, k0, sC, true);
