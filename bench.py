@@ -848,12 +848,17 @@ def main():
             api.kvm_len_add(lens, 1)
 
     graphs = []
+    pgraph = None
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
     if not args.no_graph:
-        # capture the decode loop in chunks; the kernels never allocate or memset
+        # capture the prefill (every layer's index, selection and compaction) and the decode
+        # loop in chunks; the kernels never allocate or memset
         with torch.cuda.stream(stream):
             prefill()      # fill caches once so capture-time launches see valid data
+            pgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(pgraph, stream=stream):
+                prefill()
             for c0 in range(0, T, args.graph_chunk):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
@@ -862,12 +867,15 @@ def main():
         torch.cuda.synchronize()
         lens.fill_(keep)
         torch.cuda.synchronize()
-        log(f"captured {len(graphs)} decode graphs of {args.graph_chunk} steps x {layers} layers")
+        log(f"captured the prefill ({layers} layers) and {len(graphs)} decode graphs of {args.graph_chunk} steps")
 
     def step(ev):
         with torch.cuda.stream(stream):
             ev[0].record(stream)
-            prefill()
+            if pgraph is not None:
+                pgraph.replay()
+            else:
+                prefill()
             ev[1].record(stream)
             if graphs:
                 for g in graphs:
