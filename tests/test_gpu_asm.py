@@ -95,6 +95,11 @@ KMEANS_CASES = [
     (600, 4, 128, 16, 5, 16),
     (1100, 2, 64, 24, 3, 20),     # more than two 512-row chunks, 4 centroids drawing nobody
     (70, 3, 128, 8, 0, 8),        # assignment only
+    # several 32-centroid tiles through the assignment's three-slot ring: 3 tiles (the loop
+    # without a tail), 4 (one tail step), 2 (two tail steps)
+    (900, 2, 128, 96, 2, 96),
+    (700, 2, 64, 100, 2, 100),
+    (500, 3, 128, 40, 2, 40),
 ]
 
 
