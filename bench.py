@@ -411,7 +411,8 @@ def time_rows(torch, api, KL, dev):
 
 
 def source_sha16():
-    """Hash of the library sources, the header and this script (the GPU machine has no git)."""
+    """Hash of the library sources, the header and this script (a machine that runs the
+    benchmark need not have the git history)."""
     import glob
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
